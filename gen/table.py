@@ -1,0 +1,98 @@
+"""FP8 table generator: a GPU filler for HBM and a CPU row rebuilder.
+
+Both implement the same counter-based recipe (Philox4x64-10, see
+csrc/tablegen_host.c), so the CPU side can rebuild any row the GPU wrote.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import inputs
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+HOST_LIB = os.path.join(_HERE, "libplegen_host.so")
+HIP_LIB = os.path.join(_HERE, "libplegen_hip.so")
+
+_host = None
+_hip = None
+_thr = None
+
+
+def thresholds() -> np.ndarray:
+    global _thr
+    if _thr is None:
+        _thr = inputs.e4m3_magnitude_thresholds()
+    return _thr
+
+
+def _host_lib():
+    global _host
+    if _host is None:
+        if not os.path.exists(HOST_LIB):
+            raise RuntimeError(f"{HOST_LIB} is not built; run __graft_entry__.build()")
+        lib = ctypes.CDLL(HOST_LIB)
+        lib.gen_table_rows.argtypes = [ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int64,
+                                       ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint32,
+                                       ctypes.c_void_p, ctypes.c_void_p]
+        lib.gen_table_rows.restype = None
+        lib.gen_philox4x64_10.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        lib.gen_philox4x64_10.restype = None
+        _host = lib
+    return _host
+
+
+def philox4x64_10(ctr, key) -> np.ndarray:
+    c = np.ascontiguousarray(np.asarray(ctr, dtype=np.uint64))
+    k = np.ascontiguousarray(np.asarray(key, dtype=np.uint64))
+    o = np.zeros(4, dtype=np.uint64)
+    _host_lib().gen_philox4x64_10(c.ctypes.data, k.ctypes.data, o.ctypes.data)
+    return o
+
+
+def rows_cpu(ids, seed: int = inputs.TABLE_SEED):
+    """Rebuild table rows `ids` on the CPU: (codes uint8[n][2560], scales float32[n])."""
+    ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int64).reshape(-1))
+    n = len(ids)
+    rows = np.empty((n, inputs.D), dtype=np.uint8)
+    scales = np.empty(n, dtype=np.float32)
+    thr = np.ascontiguousarray(thresholds())
+    if n:
+        _host_lib().gen_table_rows(seed, ids.ctypes.data, n, thr.ctypes.data,
+                                   inputs.SCALE_M_LO, inputs.SCALE_M_SPAN,
+                                   rows.ctypes.data, scales.ctypes.data)
+    return rows, scales
+
+
+def _hip_lib():
+    global _hip
+    if _hip is None:
+        import torch  # noqa: F401  (torch's HIP runtime must be the one loaded)
+        if not os.path.exists(HIP_LIB):
+            raise RuntimeError(f"{HIP_LIB} is not built; run __graft_entry__.build()")
+        lib = ctypes.CDLL(HIP_LIB)
+        lib.gen_fill_table.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                       ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint32,
+                                       ctypes.c_uint32, ctypes.c_void_p]
+        lib.gen_fill_table.restype = ctypes.c_int
+        _hip = lib
+    return _hip
+
+
+def table_gpu(R: int, seed: int = inputs.TABLE_SEED, device="cuda"):
+    """Allocate and fill (codes uint8[R][2560], scales float32[R]) on the GPU."""
+    import torch
+    table = torch.empty((R, inputs.D), dtype=torch.uint8, device=device)
+    scales = torch.empty((R,), dtype=torch.float32, device=device)
+    thr = torch.from_numpy(thresholds().astype(np.int64)).to(torch.int32).to(device)
+    stream = torch.cuda.current_stream(table.device).cuda_stream
+    rc = _hip_lib().gen_fill_table(table.data_ptr(), scales.data_ptr(), R, seed, thr.data_ptr(),
+                                   inputs.SCALE_M_LO, inputs.SCALE_M_SPAN, stream)
+    if rc != 0:
+        raise RuntimeError(f"gen_fill_table failed: {rc}")
+    torch.cuda.current_stream(table.device).synchronize()
+    del thr
+    return table, scales
