@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Throughput of the PLE n-gram embedding path on one MI355X.
+
+A step is one ple_forward over one batch of the workload (n-gram IDs ->
+gather/dequant from the 51.2 GB FP8 table in HBM -> projection -> gate /
+short conv / residual add). The default workload is the 32,768-token Zipf
+prefill, the one the gather roofline target is stated for; --workload picks
+another (tiny, decode, ragged, long). Inputs are resident in HBM before the
+timed region; the timed region is K back-to-back steps between two device
+synchronizations.
+
+Printed: one JSON line with the step throughput (tokens/s), the roofline of
+the dominant kernel measured with HIP events inside the same run, per-stage
+durations, and the CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "PLE fused tokens/s (hash+gather+dequant+proj+fuse); gather HBM GB/s vs peak"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+D = 2560
+
+# Algorithmic bytes / flop per unit (one token, or one valid lookup).
+#  gather: per valid lookup 2560 B of codes + 4 B scale; per token 8 B of row
+#          ids read and 5120 B of bf16 x written
+#  proj:   2 * 2560 * 2560 flop per token
+#  fuse:   per token h 5120 B + e 5120 B + out 5120 B + 320 B gate partials
+#  hash:   per token 4 B token read (+ history), 8 B ids written
+GATHER_BYTES_PER_LOOKUP = 2560 + 4
+GATHER_BYTES_PER_TOKEN = 8 + 2 * D
+PROJ_FLOP_PER_TOKEN = 2 * D * D
+FUSE_BYTES_PER_TOKEN = 3 * 2 * D + 20 * 16
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+            out.append(e.value)
+        return out
+
+    def record(self, ev, stream):
+        assert self.hip.hipEventRecord(ev, stream) == 0
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        assert self.hip.hipEventSynchronize(b) == 0
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return float(ms.value)
+
+
+def describe(name, wl):
+    T = len(wl.chunks[0][0])
+    if name == "prefill":
+        return f"prefill: 1 sequence x 32768 Zipf(1.1) tokens, {wl.R:,}-row x 2560 FP8 E4M3 table (51.2 GB) in HBM"
+    if name == "ragged":
+        return f"ragged prefill: 64 sequences x 256 uniform tokens, {wl.R:,}-row FP8 table in HBM"
+    if name == "decode":
+        return f"decode: 8 sequences x 1 token per step after 4096-token histories, {wl.R:,}-row FP8 table in HBM"
+    if name == "long":
+        return f"long context: 262144 tokens as 16 x 16384-token chunks with carried state, {wl.R:,}-row FP8 table"
+    return f"tiny: 1 x {T} uniform tokens, {wl.R:,}-row FP8 table"
+
+
+def cpu_baseline(wl, name, W, cw, h0, budget_s=12.0):
+    """The CPU oracle (as it stands) on the first N tokens of the workload's
+    first chunk, N sized so that the run takes about `budget_s` seconds."""
+    import numpy as np
+
+    import oracle
+    from gen import table
+
+    toks, cu = wl.chunks[0]
+    S = len(cu) - 1
+
+    def run(n):
+        # the first n tokens, cut at the same sequence boundaries
+        cut = np.minimum(cu, n).astype(np.int32)
+        t0 = time.perf_counter()
+        oracle.forward(toks[:n], cut, h0[:n], W, cw, wl.R, table.rows_cpu,
+                       np.zeros((S, 2), np.int32), np.zeros(S, np.int32), np.zeros((S, 3, D)))
+        return time.perf_counter() - t0
+
+    T = len(toks)
+    probe = min(64, T)
+    tp = run(probe)
+    n = int(min(T, max(probe, round(probe * budget_s / max(tp, 1e-6) / 64) * 64)))
+    dt = run(n)
+    return {"value": round(n / dt, 2), "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"first {n} of {T} tokens of the {name} workload's first chunk, one call "
+                      f"({dt:.1f} s); table rows rebuilt on demand by the CPU generator"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill", choices=["tiny", "decode", "prefill", "ragged", "long"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        sys.exit("bench.py measures one GPU: this build runs the path on a single MI355X "
+                 "(multi-GPU sharding is design-only), so --gpus must be 1")
+
+    import numpy as np
+    import torch
+
+    import sparse_memory_gather_amd as ple
+    from gen import inputs, table
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ple.load_library()
+    name = args.workload
+    wl = inputs.make_workload(name, decode_steps=max(1, args.steps + args.warmup))
+    W, cw = inputs.weights()
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    print(f"[bench] {name}: generating the {wl.R:,}-row table", file=sys.stderr, flush=True)
+    tab, sc = table.table_gpu(wl.R, device=dev)
+    Wd, cwd = bf16(W), bf16(cw)
+    ws = ple.Workspace(dev)
+
+    # batches, all resident on the device before timing
+    batches = []
+    if name == "long":
+        for i, (t, c) in enumerate(wl.chunks):
+            batches.append((torch.from_numpy(t).to(dev), torch.from_numpy(c).to(dev), bf16(wl.hidden(i))))
+    elif name == "decode":
+        for i, (t, c) in enumerate(wl.chunks):
+            batches.append((torch.from_numpy(t).to(dev), torch.from_numpy(c).to(dev), bf16(wl.hidden(i))))
+    else:
+        t, c = wl.chunks[0]
+        batches.append((torch.from_numpy(t).to(dev), torch.from_numpy(c).to(dev), bf16(wl.hidden(0))))
+    h0 = wl.hidden(0) if name != "long" else None
+    state = ple.State(wl.S, dev)
+    if name == "decode":
+        hist = wl.history[0]
+        hh = bf16(wl.history_hidden(hist.size))
+        cu_h = torch.arange(0, hist.size + 1, hist.shape[1], dtype=torch.int32, device=dev)
+        ple.ple_forward(torch.from_numpy(hist.reshape(-1)).to(dev), cu_h, tab, sc, Wd, cwd, hh, state,
+                        workspace=ws)
+        del hh
+    outs = [torch.empty_like(b[2]) for b in batches] if name in ("long", "decode") else \
+        [torch.empty_like(batches[0][2])]
+    for b in batches:
+        ws.get(b[0].numel(), b[1].numel() - 1)
+
+    if name == "long":
+        def step(k, events=None):
+            for (t, c, h), o in zip(batches, outs):
+                ple.ple_forward(t, c, tab, sc, Wd, cwd, h, state, out=o, workspace=ws, events=events)
+        tokens_per_step = sum(b[0].numel() for b in batches)
+    elif name == "decode":
+        def step(k, events=None):
+            t, c, h = batches[k % len(batches)]
+            ple.ple_forward(t, c, tab, sc, Wd, cwd, h, state, out=outs[k % len(outs)], workspace=ws,
+                            events=events)
+        tokens_per_step = batches[0][0].numel()
+    else:
+        def step(k, events=None):
+            t, c, h = batches[0]
+            ple.ple_forward(t, c, tab, sc, Wd, cwd, h, state, out=outs[0], workspace=ws, events=events)
+        tokens_per_step = batches[0][0].numel()
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(args.warmup + k)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1e3 * wall / args.steps
+    value = tokens_per_step * args.steps / wall
+
+    # per-kernel durations inside the real forward: events around each kernel
+    hev = HipEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+    n_calls = len(batches) if name == "long" else 1
+    reps = args.steps
+    ev = [hev.create(5) for _ in range(reps * n_calls)]
+    torch.cuda.synchronize()
+    for k in range(reps):
+        if name == "long":
+            for j, ((t, c, h), o) in enumerate(zip(batches, outs)):
+                ple.ple_forward(t, c, tab, sc, Wd, cwd, h, state, out=o, workspace=ws,
+                                events=ev[k * n_calls + j])
+        else:
+            step(k, events=ev[k])
+    torch.cuda.synchronize()
+    stage = np.zeros(4)
+    for e in ev:
+        for i in range(4):
+            stage[i] += hev.elapsed_ms(e[i], e[i + 1])
+    stage_us = 1e3 * stage / len(ev)  # average per launch
+    tokens_per_call = tokens_per_step / n_calls
+
+    # valid lookups per call (for the gather's algorithmic bytes)
+    rid = ple.ple_hash(batches[0][0], batches[0][1], torch.zeros((wl.S, 2), dtype=torch.int32, device=dev),
+                       torch.full((wl.S,), 2 if name == "decode" else 0, dtype=torch.int32, device=dev), wl.R)
+    lookups = int((rid >= 0).sum().item()) if name != "decode" else 2 * batches[0][0].numel()
+    gather_bytes = lookups * GATHER_BYTES_PER_LOOKUP + tokens_per_call * GATHER_BYTES_PER_TOKEN
+    gather_gbs = gather_bytes / (stage_us[1] * 1e-6) / 1e9
+    proj_flop = tokens_per_call * PROJ_FLOP_PER_TOKEN
+    proj_tflops = proj_flop / (stage_us[2] * 1e-6) / 1e12
+    fuse_bytes = tokens_per_call * FUSE_BYTES_PER_TOKEN
+    fuse_gbs = fuse_bytes / (stage_us[3] * 1e-6) / 1e9
+
+    dominant = int(np.argmax(stage_us))
+    if dominant == 2:
+        roofline = {"kernel": "ple_proj (proj_kernel, forward variant)", "bound": "mfma",
+                    "achieved": round(proj_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(proj_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "per_launch": {"flop": proj_flop, "avg_us": round(float(stage_us[2]), 2)}}
+    elif dominant == 1:
+        roofline = {"kernel": "ple_gather_dequant (gather_kernel)", "bound": "hbm",
+                    "achieved": round(gather_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(gather_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                    "per_launch": {"bytes": gather_bytes, "avg_us": round(float(stage_us[1]), 2)}}
+    else:
+        k = ["ple_hash (hash_kernel)", "", "", "ple_gate_conv_fuse (fuse_kernel)"][dominant]
+        nb = fuse_bytes if dominant == 3 else tokens_per_call * 12
+        gbs = nb / (stage_us[dominant] * 1e-6) / 1e9
+        roofline = {"kernel": k, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                    "per_launch": {"bytes": nb, "avg_us": round(float(stage_us[dominant]), 2)}}
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": describe(name, wl), "name": name, "tokens_per_step": tokens_per_step,
+                   "sequences": wl.S, "table_rows": wl.R, "table_bytes": wl.R * D},
+        "roofline": roofline,
+        "stages_us": {"hash": round(float(stage_us[0]), 2), "gather": round(float(stage_us[1]), 2),
+                      "proj": round(float(stage_us[2]), 2), "fuse": round(float(stage_us[3]), 2)},
+        "gather": {"bound": "hbm", "achieved": round(gather_gbs, 1), "peak": HBM_PEAK_GBS,
+                   "unit": "GB/s", "frac": round(gather_gbs / HBM_PEAK_GBS, 4),
+                   "bytes_per_launch": gather_bytes, "lookups_per_launch": lookups},
+        "proj": {"bound": "mfma", "achieved": round(proj_tflops, 2), "peak": BF16_PEAK_TFLOPS,
+                 "unit": "TFLOP/s", "frac": round(proj_tflops / BF16_PEAK_TFLOPS, 4)},
+        "fuse": {"bound": "hbm", "achieved": round(fuse_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                 "frac": round(fuse_gbs / HBM_PEAK_GBS, 4)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline and h0 is not None:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(wl, name, W, cw, h0, args.cpu_budget)
+    elif not args.no_cpu_baseline:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        h0 = wl.hidden(0)
+        result["cpu_baseline"] = cpu_baseline(wl, name, W, cw, h0, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -47,6 +47,7 @@ def _load():
             raise RuntimeError(f"{LIB} is not built; run __graft_entry__.build()")
         lib = ctypes.CDLL(LIB)
         sig = {
+            "oracle_num_threads": ([], ctypes.c_int),
             "oracle_mix64": ([ctypes.c_uint64], ctypes.c_uint64),
             "oracle_key2": ([ctypes.c_uint32, ctypes.c_uint32], ctypes.c_uint64),
             "oracle_key3": ([ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32], ctypes.c_uint64),
@@ -76,6 +77,10 @@ def _ptr(a):
 
 
 # --- scalar helpers -------------------------------------------------------
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
 
 def mix64(z: int) -> int:
     return int(_load().oracle_mix64(z & (2 ** 64 - 1)))

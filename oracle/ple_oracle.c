@@ -32,9 +32,21 @@
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define D 2560
 #define KTAPS 4
+
+/* Threads the projection loop runs on (OpenMP), for reporting. */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* ------------------------------------------------------------------------ */
 /* n-gram IDs                                                                */

@@ -1,0 +1,265 @@
+"""Python binding of libple, the MI355X PLE n-gram embedding lookup.
+
+Argument marshalling only: every step of the path runs in the HIP kernels
+behind the C ABI declared in include/ple.h. Torch provides device memory
+and the current stream. There is no CPU fallback: if libple.so is missing,
+or torch has no GPU, the calls raise.
+
+The operation (Qwen3.8-Flash-Next pages; mengman.github.io "Qwen3.8-Flash-
+Next 端侧部署 01", n-gram embedding section): per token, hash the recent
+token IDs into bigram/trigram row IDs, gather and dequantize the FP8 rows,
+project, gate, short-convolve with carried state and add to the hidden
+state. Exact formulas are in include/ple.h.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+D = 2560
+CONV_TAPS = 4
+MAX_VOCAB = 1 << 20
+DEFAULT_VOCAB = 248_320
+DEFAULT_EPS = 1e-6
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libple.so")
+
+PLE_OK = 0
+STATUS_NAMES = {0: "PLE_OK", -1: "PLE_ERR_NULL", -2: "PLE_ERR_SHAPE", -3: "PLE_ERR_RANGE",
+                -4: "PLE_ERR_ALIGN", -5: "PLE_ERR_ALIAS", -6: "PLE_ERR_WORKSPACE", -7: "PLE_ERR_HIP"}
+DEVERR_TOKEN_RANGE = 1
+DEVERR_CU_SEQLENS = 2
+DEVERR_HIST_LEN = 4
+DEVERR_ROW_RANGE = 8
+
+
+class PLEError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_P = ctypes.c_void_p
+
+
+class ForwardArgs(ctypes.Structure):
+    """Mirror of ple_forward_args (include/ple.h), same field order."""
+    _fields_ = [
+        ("tokens", _P), ("T", ctypes.c_int64), ("cu_seqlens", _P), ("S", ctypes.c_int32),
+        ("vocab_size", ctypes.c_int32), ("table", _P), ("scales", _P), ("R", ctypes.c_int64),
+        ("W", _P), ("conv_w", _P), ("h", _P), ("out", _P), ("hist_ids", _P), ("hist_len", _P),
+        ("conv_state", _P), ("workspace", _P), ("workspace_bytes", ctypes.c_size_t),
+        ("dev_err", _P), ("eps", ctypes.c_float), ("row_ids_out", _P), ("x_out", _P),
+        ("e_out", _P), ("gate_out", _P), ("y_out", _P),
+    ]
+
+
+_lib = None
+
+EXPORTS = ("ple_hash", "ple_lookup", "ple_proj", "ple_forward", "ple_forward_profiled",
+           "ple_forward_workspace_size", "ple_status_string", "ple_last_error")
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libple.so (torch is imported first so that its HIP runtime is the
+    one the library binds to)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libple is not built ({path} missing); run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    I32, I64 = ctypes.c_int32, ctypes.c_int64
+    lib.ple_hash.argtypes = [_P, I64, _P, I32, _P, _P, I32, I64, _P, _P, _P]
+    lib.ple_hash.restype = ctypes.c_int
+    lib.ple_lookup.argtypes = [_P, I64, _P, _P, I64, _P, _P, _P, _P]
+    lib.ple_lookup.restype = ctypes.c_int
+    lib.ple_proj.argtypes = [_P, I64, _P, _P, _P]
+    lib.ple_proj.restype = ctypes.c_int
+    lib.ple_forward.argtypes = [ctypes.POINTER(ForwardArgs), _P]
+    lib.ple_forward.restype = ctypes.c_int
+    lib.ple_forward_profiled.argtypes = [ctypes.POINTER(ForwardArgs), _P, ctypes.POINTER(_P)]
+    lib.ple_forward_profiled.restype = ctypes.c_int
+    lib.ple_forward_workspace_size.argtypes = [I64, I32]
+    lib.ple_forward_workspace_size.restype = ctypes.c_size_t
+    lib.ple_status_string.argtypes = [ctypes.c_int]
+    lib.ple_status_string.restype = ctypes.c_char_p
+    lib.ple_last_error.argtypes = []
+    lib.ple_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != PLE_OK:
+        raise PLEError(status, load_library().ple_last_error().decode())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _dev(t: torch.Tensor, name: str, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    return t.data_ptr()
+
+
+def _opt(t, name, dtype, shape):
+    return None if t is None else _dev(t, name, dtype, shape)
+
+
+def workspace_size(max_T: int, max_S: int) -> int:
+    return int(load_library().ple_forward_workspace_size(max_T, max_S))
+
+
+def ple_hash(tokens, cu_seqlens, hist_ids, hist_len, R: int, vocab_size: int = DEFAULT_VOCAB,
+             row_ids=None, dev_err=None, stream=None):
+    """a1: row IDs int32 [T][2] (bigram, trigram; -1 when missing)."""
+    T = tokens.numel()
+    S = cu_seqlens.numel() - 1
+    if row_ids is None:
+        row_ids = torch.empty((T, 2), dtype=torch.int32, device=tokens.device)
+    _check(load_library().ple_hash(
+        _dev(tokens, "tokens", torch.int32, (T,)), T, _dev(cu_seqlens, "cu_seqlens", torch.int32, (S + 1,)),
+        S, _dev(hist_ids, "hist_ids", torch.int32, (S, 2)), _dev(hist_len, "hist_len", torch.int32, (S,)),
+        vocab_size, R, _dev(row_ids, "row_ids", torch.int32, (T, 2)),
+        _opt(dev_err, "dev_err", torch.int32, (1,)), _stream(stream)))
+    return row_ids
+
+
+def ple_lookup(row_ids, table, scales, x=None, raw=None, dev_err=None, stream=None):
+    """a2: x bf16 [T][2560] = bf16(sum of the two dequantized rows)."""
+    T = row_ids.shape[0]
+    R = table.shape[0]
+    if x is None:
+        x = torch.empty((T, D), dtype=torch.bfloat16, device=row_ids.device)
+    _check(load_library().ple_lookup(
+        _dev(row_ids, "row_ids", torch.int32, (T, 2)), T, _dev(table, "table", torch.uint8, (R, D)),
+        _dev(scales, "scales", torch.float32, (R,)), R, _dev(x, "x", torch.bfloat16, (T, D)),
+        _opt(raw, "raw", torch.uint8, (T, 2, D)), _opt(dev_err, "dev_err", torch.int32, (1,)),
+        _stream(stream)))
+    return x
+
+
+def ple_proj(x, W, e=None, stream=None):
+    """a3: e fp32 [T][2560] = x W^T."""
+    T = x.shape[0]
+    if e is None:
+        e = torch.empty((T, D), dtype=torch.float32, device=x.device)
+    _check(load_library().ple_proj(_dev(x, "x", torch.bfloat16, (T, D)), T,
+                                   _dev(W, "W", torch.bfloat16, (D, D)),
+                                   _dev(e, "e", torch.float32, (T, D)), _stream(stream)))
+    return e
+
+
+class State:
+    """Per-sequence carried state: the last two token IDs and the last three
+    gated vectors of each of S sequences (zeros = fresh sequences)."""
+
+    def __init__(self, S: int, device="cuda"):
+        self.hist_ids = torch.zeros((S, 2), dtype=torch.int32, device=device)
+        self.hist_len = torch.zeros((S,), dtype=torch.int32, device=device)
+        self.conv_state = torch.zeros((S, 3, D), dtype=torch.float32, device=device)
+
+    @property
+    def S(self) -> int:
+        return self.hist_len.numel()
+
+    def clone(self) -> "State":
+        c = State.__new__(State)
+        c.hist_ids = self.hist_ids.clone()
+        c.hist_len = self.hist_len.clone()
+        c.conv_state = self.conv_state.clone()
+        return c
+
+
+class Workspace:
+    """Caller-owned scratch for ple_forward, grown on demand (allocation
+    happens here, in torch, never inside libple)."""
+
+    def __init__(self, device="cuda"):
+        self.device = device
+        self.buf = None
+
+    def get(self, T: int, S: int) -> torch.Tensor:
+        need = workspace_size(T, S)
+        if self.buf is None or self.buf.numel() < need:
+            self.buf = torch.empty((max(need, 256),), dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+def ple_forward(tokens, cu_seqlens, table, scales, W, conv_w, h, state: State, out=None,
+                workspace=None, vocab_size: int = DEFAULT_VOCAB, eps: float = DEFAULT_EPS,
+                dev_err=None, debug: bool = False, stream=None, events=None):
+    """a1..a4 for one chunk. Updates `state` in place; returns out (bf16
+    [T][2560]) or, with debug=True, a dict with out, row_ids, x, e, gate, y.
+    `events`: optional sequence of five hipEvent_t handles (ints) recorded
+    around the four kernels (ple_forward_profiled)."""
+    T = tokens.numel()
+    S = cu_seqlens.numel() - 1
+    R = table.shape[0]
+    dev = tokens.device
+    if out is None:
+        out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    if workspace is None:
+        workspace = Workspace(dev)
+    ws = workspace.get(T, S) if isinstance(workspace, Workspace) else workspace
+    dbg = {}
+    if debug:
+        dbg = dict(row_ids=torch.empty((T, 2), dtype=torch.int32, device=dev),
+                   x=torch.empty((T, D), dtype=torch.bfloat16, device=dev),
+                   e=torch.empty((T, D), dtype=torch.float32, device=dev),
+                   gate=torch.empty((T,), dtype=torch.float32, device=dev),
+                   y=torch.empty((T, D), dtype=torch.float32, device=dev))
+    a = ForwardArgs()
+    a.tokens = _dev(tokens, "tokens", torch.int32, (T,))
+    a.T = T
+    a.cu_seqlens = _dev(cu_seqlens, "cu_seqlens", torch.int32, (S + 1,))
+    a.S = S
+    a.vocab_size = vocab_size
+    a.table = _dev(table, "table", torch.uint8, (R, D))
+    a.scales = _dev(scales, "scales", torch.float32, (R,))
+    a.R = R
+    a.W = _dev(W, "W", torch.bfloat16, (D, D))
+    a.conv_w = _dev(conv_w, "conv_w", torch.bfloat16, (D, CONV_TAPS))
+    a.h = _dev(h, "h", torch.bfloat16, (T, D))
+    a.out = _dev(out, "out", torch.bfloat16, (T, D))
+    a.hist_ids = _dev(state.hist_ids, "hist_ids", torch.int32, (S, 2))
+    a.hist_len = _dev(state.hist_len, "hist_len", torch.int32, (S,))
+    a.conv_state = _dev(state.conv_state, "conv_state", torch.float32, (S, 3, D))
+    a.workspace = _dev(ws, "workspace", torch.uint8)
+    a.workspace_bytes = ws.numel()
+    a.dev_err = _opt(dev_err, "dev_err", torch.int32, (1,))
+    a.eps = eps
+    if debug:
+        a.row_ids_out = dbg["row_ids"].data_ptr()
+        a.x_out = dbg["x"].data_ptr()
+        a.e_out = dbg["e"].data_ptr()
+        a.gate_out = dbg["gate"].data_ptr()
+        a.y_out = dbg["y"].data_ptr()
+    if events is None:
+        _check(load_library().ple_forward(ctypes.byref(a), _stream(stream)))
+    else:
+        ev = (_P * 5)(*[ctypes.c_void_p(int(e)) for e in events])
+        _check(load_library().ple_forward_profiled(ctypes.byref(a), _stream(stream), ev))
+    if debug:
+        dbg["out"] = out
+        return dbg
+    return out

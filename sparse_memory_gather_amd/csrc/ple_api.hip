@@ -1,0 +1,269 @@
+// libple C ABI: argument validation, workspace layout and launch order.
+//
+// Every host-detectable error is reported before anything is enqueued; the
+// kernels then run on the caller's stream in the order of the method
+// (IDs -> gather/dequant -> projection -> gate/conv/fuse), nothing is
+// synchronized and nothing is allocated.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/ple.h"
+#include "ple_kernels.h"
+
+using namespace ple;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int ok() {
+    g_last_error.clear();
+    return PLE_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Range {
+    const char* name;
+    uintptr_t lo, hi;  // [lo, hi)
+    bool writable;
+};
+
+Range rng(const char* name, const void* p, size_t bytes, bool writable) {
+    uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{name, lo, p ? lo + bytes : lo, writable};
+}
+
+// Writable ranges may not overlap any other range; the single exception is
+// the pair (h, out) over the same extent (in-place fuse).
+int check_alias(const Range* r, int n) {
+    for (int i = 0; i < n; ++i) {
+        if (r[i].lo == r[i].hi) continue;
+        for (int j = i + 1; j < n; ++j) {
+            if (r[j].lo == r[j].hi) continue;
+            if (!r[i].writable && !r[j].writable) continue;
+            const bool overlap = r[i].lo < r[j].hi && r[j].lo < r[i].hi;
+            if (!overlap) continue;
+            const bool same = r[i].lo == r[j].lo && r[i].hi == r[j].hi;
+            const std::string a = r[i].name, b = r[j].name;
+            const bool in_place = (a == "h" && b == "out") || (a == "out" && b == "h");
+            if (same && in_place) continue;
+            return fail(PLE_ERR_ALIAS, "%s overlaps %s", r[i].name, r[j].name);
+        }
+    }
+    return PLE_OK;
+}
+
+struct WsLayout {
+    size_t row_ids, x, e16, parts, snap, total;
+};
+
+size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
+
+WsLayout layout(int64_t T, int32_t S) {
+    WsLayout w{};
+    size_t off = 0;
+    w.row_ids = off; off = up256(off + (size_t)T * 2 * sizeof(int32_t));
+    w.x = off;       off = up256(off + (size_t)T * kD * 2);
+    w.e16 = off;     off = up256(off + (size_t)T * kD * 2);
+    w.parts = off;   off = up256(off + (size_t)T * kParts * kPartStride * sizeof(float));
+    w.snap = off;    off = up256(off + (size_t)S * 3 * kD * sizeof(float));
+    w.total = off;
+    return w;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return PLE_OK;
+    return fail(PLE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int check_R(int64_t R) {
+    if (R < 1 || R > 2147483647LL) return fail(PLE_ERR_RANGE, "R = %lld outside [1, 2^31-1]", (long long)R);
+    return PLE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ple_status_string(int status) {
+    switch (status) {
+        case PLE_OK: return "ok";
+        case PLE_ERR_NULL: return "null pointer";
+        case PLE_ERR_SHAPE: return "bad shape";
+        case PLE_ERR_RANGE: return "value out of range";
+        case PLE_ERR_ALIGN: return "misaligned pointer";
+        case PLE_ERR_ALIAS: return "overlapping buffers";
+        case PLE_ERR_WORKSPACE: return "workspace too small";
+        case PLE_ERR_HIP: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+const char* ple_last_error(void) { return g_last_error.c_str(); }
+
+size_t ple_forward_workspace_size(int64_t max_T, int32_t max_S) {
+    if (max_T < 0 || max_S < 0) return 0;
+    return layout(max_T, max_S).total;
+}
+
+int ple_hash(const int32_t* tokens, int64_t T, const int32_t* cu_seqlens, int32_t S,
+             const int32_t* hist_ids, const int32_t* hist_len, int32_t vocab_size, int64_t R,
+             int32_t* row_ids, int32_t* dev_err, void* stream) {
+    if (T < 0) return fail(PLE_ERR_SHAPE, "T = %lld < 0", (long long)T);
+    if (S < 1) return fail(PLE_ERR_SHAPE, "S = %d < 1", S);
+    if (int st = check_R(R)) return st;
+    if (vocab_size < 1 || vocab_size > PLE_MAX_VOCAB)
+        return fail(PLE_ERR_RANGE, "vocab_size = %d outside [1, 2^20]", vocab_size);
+    if (T == 0) return ok();
+    if (!tokens || !cu_seqlens || !hist_ids || !hist_len || !row_ids)
+        return fail(PLE_ERR_NULL, "ple_hash: a required pointer is NULL");
+    if (!aligned(tokens, 4) || !aligned(cu_seqlens, 4) || !aligned(hist_ids, 4) ||
+        !aligned(hist_len, 4) || !aligned(row_ids, 8) || !aligned(dev_err, 4))
+        return fail(PLE_ERR_ALIGN, "ple_hash: misaligned pointer");
+    Range r[] = {rng("tokens", tokens, T * 4, false), rng("cu_seqlens", cu_seqlens, (S + 1) * 4ull, false),
+                 rng("hist_ids", hist_ids, S * 8ull, false), rng("hist_len", hist_len, S * 4ull, false),
+                 rng("row_ids", row_ids, T * 8, true), rng("dev_err", dev_err, 4, true)};
+    if (int st = check_alias(r, 6)) return st;
+    hipError_t e = launch_hash(tokens, T, cu_seqlens, S, hist_ids, hist_len, vocab_size, R, row_ids,
+                               dev_err, nullptr, nullptr, reinterpret_cast<hipStream_t>(stream));
+    if (int st = hip_status(e, "ple_hash launch")) return st;
+    return ok();
+}
+
+int ple_lookup(const int32_t* row_ids, int64_t T, const uint8_t* table, const float* scales,
+               int64_t R, uint16_t* x_bf16, uint8_t* raw_opt, int32_t* dev_err, void* stream) {
+    if (T < 0) return fail(PLE_ERR_SHAPE, "T = %lld < 0", (long long)T);
+    if (int st = check_R(R)) return st;
+    if (T == 0) return ok();
+    if (!row_ids || !table || !scales || !x_bf16)
+        return fail(PLE_ERR_NULL, "ple_lookup: a required pointer is NULL");
+    if (!aligned(row_ids, 8) || !aligned(table, 16) || !aligned(scales, 4) || !aligned(x_bf16, 16) ||
+        !aligned(raw_opt, 16) || !aligned(dev_err, 4))
+        return fail(PLE_ERR_ALIGN, "ple_lookup: misaligned pointer");
+    Range r[] = {rng("row_ids", row_ids, T * 8, false), rng("table", table, (size_t)R * kD, false),
+                 rng("scales", scales, (size_t)R * 4, false), rng("x", x_bf16, (size_t)T * kD * 2, true),
+                 rng("raw", raw_opt, (size_t)T * 2 * kD, true), rng("dev_err", dev_err, 4, true)};
+    if (int st = check_alias(r, 6)) return st;
+    hipError_t e = launch_gather(row_ids, T, table, scales, R, x_bf16, raw_opt, dev_err,
+                                 reinterpret_cast<hipStream_t>(stream));
+    if (int st = hip_status(e, "ple_lookup launch")) return st;
+    return ok();
+}
+
+int ple_proj(const uint16_t* x_bf16, int64_t T, const uint16_t* W_bf16, float* e, void* stream) {
+    if (T < 0) return fail(PLE_ERR_SHAPE, "T = %lld < 0", (long long)T);
+    if (T == 0) return ok();
+    if (!x_bf16 || !W_bf16 || !e) return fail(PLE_ERR_NULL, "ple_proj: a required pointer is NULL");
+    if (!aligned(x_bf16, 16) || !aligned(W_bf16, 16) || !aligned(e, 16))
+        return fail(PLE_ERR_ALIGN, "ple_proj: misaligned pointer");
+    Range r[] = {rng("x", x_bf16, (size_t)T * kD * 2, false), rng("W", W_bf16, (size_t)kD * kD * 2, false),
+                 rng("e", e, (size_t)T * kD * 4, true)};
+    if (int st = check_alias(r, 3)) return st;
+    hipError_t err = launch_proj(x_bf16, T, W_bf16, e, nullptr, nullptr, nullptr,
+                                 reinterpret_cast<hipStream_t>(stream));
+    if (int st = hip_status(err, "ple_proj launch")) return st;
+    return ok();
+}
+
+static int forward_impl(const ple_forward_args* a, void* stream, void* const* events) {
+    if (!a) return fail(PLE_ERR_NULL, "ple_forward: args is NULL");
+    const int64_t T = a->T;
+    const int32_t S = a->S;
+    if (T < 0) return fail(PLE_ERR_SHAPE, "T = %lld < 0", (long long)T);
+    if (S < 1) return fail(PLE_ERR_SHAPE, "S = %d < 1", S);
+    if (int st = check_R(a->R)) return st;
+    if (a->vocab_size < 1 || a->vocab_size > PLE_MAX_VOCAB)
+        return fail(PLE_ERR_RANGE, "vocab_size = %d outside [1, 2^20]", a->vocab_size);
+    if (!(a->eps >= 0.0f) || !isfinite(a->eps)) return fail(PLE_ERR_RANGE, "eps must be finite and >= 0");
+    if (T == 0) return ok();
+    if (!a->tokens || !a->cu_seqlens || !a->table || !a->scales || !a->W || !a->conv_w || !a->h ||
+        !a->out || !a->hist_ids || !a->hist_len || !a->conv_state)
+        return fail(PLE_ERR_NULL, "ple_forward: a required pointer is NULL");
+    if (!a->workspace) return fail(PLE_ERR_WORKSPACE, "ple_forward: workspace is NULL");
+    const WsLayout L = layout(T, S);
+    if (a->workspace_bytes < L.total)
+        return fail(PLE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", a->workspace_bytes, L.total);
+    if (!aligned(a->tokens, 4) || !aligned(a->cu_seqlens, 4) || !aligned(a->table, 16) ||
+        !aligned(a->scales, 4) || !aligned(a->W, 16) || !aligned(a->conv_w, 16) || !aligned(a->h, 16) ||
+        !aligned(a->out, 16) || !aligned(a->hist_ids, 4) || !aligned(a->hist_len, 4) ||
+        !aligned(a->conv_state, 16) || !aligned(a->workspace, 256) || !aligned(a->dev_err, 4) ||
+        !aligned(a->row_ids_out, 8) || !aligned(a->x_out, 16) || !aligned(a->e_out, 16) ||
+        !aligned(a->gate_out, 4) || !aligned(a->y_out, 16))
+        return fail(PLE_ERR_ALIGN, "ple_forward: misaligned pointer");
+    const size_t act = (size_t)T * kD * 2;
+    Range r[] = {
+        rng("tokens", a->tokens, T * 4, false),
+        rng("cu_seqlens", a->cu_seqlens, (S + 1) * 4ull, false),
+        rng("table", a->table, (size_t)a->R * kD, false),
+        rng("scales", a->scales, (size_t)a->R * 4, false),
+        rng("W", a->W, (size_t)kD * kD * 2, false),
+        rng("conv_w", a->conv_w, (size_t)kD * kTaps * 2, false),
+        rng("h", a->h, act, false),
+        rng("out", a->out, act, true),
+        rng("hist_ids", a->hist_ids, S * 8ull, true),
+        rng("hist_len", a->hist_len, S * 4ull, true),
+        rng("conv_state", a->conv_state, (size_t)S * 3 * kD * 4, true),
+        rng("workspace", a->workspace, L.total, true),
+        rng("dev_err", a->dev_err, 4, true),
+        rng("row_ids_out", a->row_ids_out, T * 8, true),
+        rng("x_out", a->x_out, act, true),
+        rng("e_out", a->e_out, (size_t)T * kD * 4, true),
+        rng("gate_out", a->gate_out, T * 4, true),
+        rng("y_out", a->y_out, (size_t)T * kD * 4, true),
+    };
+    if (int st = check_alias(r, (int)(sizeof r / sizeof r[0]))) return st;
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(a->workspace);
+    int32_t* row_ids = a->row_ids_out ? a->row_ids_out : reinterpret_cast<int32_t*>(ws + L.row_ids);
+    uint16_t* x = a->x_out ? a->x_out : reinterpret_cast<uint16_t*>(ws + L.x);
+    uint16_t* e16 = reinterpret_cast<uint16_t*>(ws + L.e16);
+    float* parts = reinterpret_cast<float*>(ws + L.parts);
+    float* snap = reinterpret_cast<float*>(ws + L.snap);
+
+    auto mark = [&](int i) -> hipError_t {
+        return events ? hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), s) : hipSuccess;
+    };
+    hipError_t e = mark(0);
+    if (int st = hip_status(e, "ple_forward: event record")) return st;
+    e = launch_hash(a->tokens, T, a->cu_seqlens, S, a->hist_ids, a->hist_len, a->vocab_size,
+                    a->R, row_ids, a->dev_err, a->conv_state, snap, s);
+    if (int st = hip_status(e, "ple_forward: hash launch")) return st;
+    if (int st = hip_status(mark(1), "ple_forward: event record")) return st;
+    e = launch_gather(row_ids, T, a->table, a->scales, a->R, x, nullptr, a->dev_err, s);
+    if (int st = hip_status(e, "ple_forward: gather launch")) return st;
+    if (int st = hip_status(mark(2), "ple_forward: event record")) return st;
+    e = launch_proj(x, T, a->W, a->e_out, e16, a->h, parts, s);
+    if (int st = hip_status(e, "ple_forward: projection launch")) return st;
+    if (int st = hip_status(mark(3), "ple_forward: event record")) return st;
+    e = launch_fuse(a->h, e16, parts, T, a->cu_seqlens, S, a->tokens, a->conv_w, snap, a->conv_state,
+                    a->hist_ids, a->hist_len, a->out, a->eps, a->gate_out, a->y_out, s);
+    if (int st = hip_status(e, "ple_forward: fuse launch")) return st;
+    if (int st = hip_status(mark(4), "ple_forward: event record")) return st;
+    return ok();
+}
+
+int ple_forward(const ple_forward_args* a, void* stream) { return forward_impl(a, stream, nullptr); }
+
+int ple_forward_profiled(const ple_forward_args* a, void* stream, void* const* events) {
+    if (!events) return fail(PLE_ERR_NULL, "ple_forward_profiled: events is NULL");
+    for (int i = 0; i < 5; ++i)
+        if (!events[i]) return fail(PLE_ERR_NULL, "ple_forward_profiled: events[%d] is NULL", i);
+    return forward_impl(a, stream, events);
+}
+
+}  // extern "C"

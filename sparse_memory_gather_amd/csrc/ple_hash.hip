@@ -1,0 +1,102 @@
+// a1: n-gram row IDs (segment-aware, carried history).
+//
+// The rows an n-gram embedding reads depend only on the recent token IDs,
+// positions and sequence boundaries (mengman.github.io "Qwen3.8-Flash-Next
+// 端侧部署 01", section on the n-gram embedding path; reactapp.top RTX 3090
+// article, section "n-gram表格": hashed bigram and trigram keys). One thread
+// per token: find the token's sequence in cu_seqlens, take the previous one
+// or two IDs from the chunk or from the carried history, and hash
+//   bigram  key (2<<60)|(a<<20)|b,  trigram key (3<<60)|(a<<40)|(b<<20)|c
+// with the SplitMix64 finalizer, reduced mod R (unsigned 64-bit). Missing
+// history gives -1.
+#include "ple_kernels.h"
+
+namespace ple {
+namespace {
+
+__device__ __forceinline__ uint64_t splitmix_finalize(uint64_t z) {
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+    return z ^ (z >> 31);
+}
+
+constexpr int kHashBlock = 256;
+
+__global__ void __launch_bounds__(kHashBlock)
+hash_kernel(const int32_t* __restrict__ tokens, int64_t T, const int32_t* __restrict__ cu, int32_t S,
+            const int32_t* __restrict__ hist_ids, const int32_t* __restrict__ hist_len,
+            int32_t vocab, uint64_t R, int32_t* __restrict__ row_ids, int32_t* dev_err,
+            const float* __restrict__ conv_state, float* __restrict__ state_snap,
+            int64_t snap_vec4) {
+    if (blockIdx.y == 1) {
+        // copy of the carried conv state, float4 at a time
+        const f32x4* src = reinterpret_cast<const f32x4*>(conv_state);
+        f32x4* dst = reinterpret_cast<f32x4*>(state_snap);
+        for (int64_t i = (int64_t)blockIdx.x * kHashBlock + threadIdx.x; i < snap_vec4;
+             i += (int64_t)gridDim.x * kHashBlock)
+            dst[i] = src[i];
+        return;
+    }
+    // boundary checks (block 0 only): cu[0] == 0, non-decreasing, cu[S] == T
+    if (blockIdx.x == 0) {
+        for (int i = threadIdx.x; i <= S; i += kHashBlock) {
+            int32_t c = cu[i];
+            bool bad = (i == 0 && c != 0) || (i == S && c != T) || (i < S && c > cu[i + 1]);
+            if (bad) flag_error(dev_err, 2);
+        }
+    }
+    int64_t t = (int64_t)blockIdx.x * kHashBlock + threadIdx.x;
+    if (t >= T) return;
+    // sequence of token t: the last s with cu[s] <= t
+    int lo = 0, hi = S - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if ((int64_t)cu[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    const int s = lo;
+    int64_t start = cu[s];
+    if (start < 0 || start > t) start = t;  // malformed cu_seqlens (flagged above): stay in bounds
+    int hl = hist_len[s];
+    if (hl < 0 || hl > 2) {
+        flag_error(dev_err, 4);
+        hl = 0;
+    }
+    const int64_t j = hl + (t - start);  // index of token t in history ++ chunk
+    auto seq_at = [&](int64_t idx) -> uint32_t {
+        int32_t v = idx < hl ? hist_ids[2 * s + 2 - hl + idx] : tokens[start + idx - hl];
+        if (v < 0 || v >= vocab) flag_error(dev_err, 1);
+        return (uint32_t)v & 0xFFFFFu;
+    };
+    const uint32_t c = seq_at(j);
+    int32_t r2 = -1, r3 = -1;
+    if (j >= 1) {
+        const uint32_t b = seq_at(j - 1);
+        r2 = (int32_t)(splitmix_finalize((2ULL << 60) | ((uint64_t)b << 20) | c) % R);
+        if (j >= 2) {
+            const uint32_t a = seq_at(j - 2);
+            r3 = (int32_t)(splitmix_finalize((3ULL << 60) | ((uint64_t)a << 40) |
+                                             ((uint64_t)b << 20) | c) % R);
+        }
+    }
+    reinterpret_cast<int2*>(row_ids)[t] = make_int2(r2, r3);
+}
+
+}  // namespace
+
+hipError_t launch_hash(const int32_t* tokens, int64_t T, const int32_t* cu, int32_t S,
+                       const int32_t* hist_ids, const int32_t* hist_len, int32_t vocab, int64_t R,
+                       int32_t* row_ids, int32_t* dev_err, const float* conv_state,
+                       float* state_snap, hipStream_t stream) {
+    int64_t blocks = (T + kHashBlock - 1) / kHashBlock;
+    if (blocks < 1) blocks = 1;
+    int64_t snap_vec4 = state_snap ? (int64_t)S * 3 * kD / 4 : 0;
+    int64_t snap_blocks = (snap_vec4 + kHashBlock - 1) / kHashBlock;
+    if (snap_blocks > blocks) blocks = snap_blocks < 65536 ? snap_blocks : 65536;
+    dim3 grid((unsigned)blocks, state_snap ? 2 : 1);
+    hipLaunchKernelGGL(hash_kernel, grid, dim3(kHashBlock), 0, stream, tokens, T, cu, S, hist_ids,
+                       hist_len, vocab, (uint64_t)R, row_ids, dev_err, conv_state, state_snap,
+                       snap_vec4);
+    return hipGetLastError();
+}
+
+}  // namespace ple

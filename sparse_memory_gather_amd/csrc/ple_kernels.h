@@ -1,0 +1,60 @@
+// Internal declarations shared by the libple HIP sources (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ple {
+
+constexpr int kD = 2560;          // row width = hidden size
+constexpr int kTaps = 4;          // short-conv taps
+constexpr int kPartCols = 128;    // features per gate partial sum
+constexpr int kParts = kD / kPartCols;  // 20 partial sums per token
+constexpr int kPartStride = 4;    // floats per (token, part): sum e^2, sum h*e, sum h^2, pad
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// Two floats -> two bf16 (round to nearest even), low element in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ void flag_error(int32_t* dev_err, int bit) {
+    if (dev_err) atomicOr(dev_err, bit);
+}
+
+// ---- launchers (each returns hipGetLastError()) ----------------------------
+
+// n-gram IDs for T tokens; optionally also copies conv_state [S][3][kD] into
+// state_snap (the fused path reads the old state from the copy while it
+// rewrites conv_state in place).
+hipError_t launch_hash(const int32_t* tokens, int64_t T, const int32_t* cu, int32_t S,
+                       const int32_t* hist_ids, const int32_t* hist_len, int32_t vocab, int64_t R,
+                       int32_t* row_ids, int32_t* dev_err, const float* conv_state,
+                       float* state_snap, hipStream_t stream);
+
+hipError_t launch_gather(const int32_t* row_ids, int64_t T, const uint8_t* table,
+                         const float* scales, int64_t R, uint16_t* x, uint8_t* raw,
+                         int32_t* dev_err, hipStream_t stream);
+
+// e = x W^T. Forward mode (h != nullptr): writes e as bf16 into e16, the gate
+// partial sums into parts [T][kParts][kPartStride], and e as fp32 into e32 if
+// e32 != nullptr. Projection-only mode (h == nullptr): writes fp32 e32.
+hipError_t launch_proj(const uint16_t* x, int64_t T, const uint16_t* W, float* e32,
+                       uint16_t* e16, const uint16_t* h, float* parts, hipStream_t stream);
+
+hipError_t launch_fuse(const uint16_t* h, const uint16_t* e16, const float* parts, int64_t T,
+                       const int32_t* cu, int32_t S, const int32_t* tokens,
+                       const uint16_t* conv_w, const float* state_snap, float* conv_state,
+                       int32_t* hist_ids, int32_t* hist_len, uint16_t* out, float eps,
+                       float* gate_out, float* y_out, hipStream_t stream);
+
+}  // namespace ple

@@ -1,0 +1,118 @@
+"""Shared helpers of the GPU parity tests: host<->device bf16 plumbing and
+the oracle reference for sampled tokens.
+
+Tolerances (derivations in DESIGN.md, "Tolerances"):
+  row IDs, gathered bytes, x           bit-exact
+  e (fp32 MFMA accumulation, K=2560)   |de| <= 2e-4 * sum_c |x_c W_oc| + 1e-7
+  g                                    |dg| <= 1e-4
+  y (v taken from bf16-rounded e)      |dy| <= 2^-8 * sum_k |w_k v_k| + 1e-6
+  out (bf16)                           |dout| <= 2e-2 + 1e-2 |out_ref|
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from gen import inputs, table
+
+D = inputs.D
+
+E_REL = 2e-4
+G_ABS = 1e-4
+Y_REL = 2.0 ** -8
+OUT_ATOL = 2e-2
+OUT_RTOL = 1e-2
+
+
+def dev_bf16(a: np.ndarray, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def dev_i32(a, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+
+
+def rows(ids):
+    return table.rows_cpu(ids)
+
+
+def e_bound(x_bits: np.ndarray, W_bits: np.ndarray) -> np.ndarray:
+    """sum_c |x_c W_oc| for each token row of x (fp64)."""
+    xa = np.abs(inputs.bf16_bits_to_f32(x_bits).astype(np.float64))
+    Wa = np.abs(inputs.bf16_bits_to_f32(W_bits).astype(np.float64))
+    return xa @ Wa.T
+
+
+def oracle_samples(seqs, samples, W, cw, R, eps=1e-6):
+    """Reference outputs of sampled tokens.
+
+    seqs: list of (tokens int32[n], h bf16 bits [n][D]) — whole sequences
+          from their first token (history included).
+    samples: list of (seq index, position) pairs.
+    Each sample becomes its own short segment: the token and up to three
+    before it, with the two tokens before that as n-gram history. Its
+    output depends on nothing earlier, so the last token of each segment is
+    the exact reference of the sampled token."""
+    toks, hs, cu, hid, hln = [], [], [0], [], []
+    for si, p in samples:
+        st, hh = seqs[si]
+        q = max(0, p - 3)
+        toks.append(st[q:p + 1])
+        hs.append(hh[q:p + 1])
+        cu.append(cu[-1] + p + 1 - q)
+        k = min(2, q)
+        hist = np.zeros(2, np.int32)
+        if k:
+            hist[2 - k:] = st[q - k:q]
+        hid.append(hist)
+        hln.append(k)
+    S = len(samples)
+    r = oracle.forward(np.concatenate(toks), np.array(cu, np.int32), np.concatenate(hs), W, cw, R,
+                       rows, np.array(hid, np.int32), np.array(hln, np.int32),
+                       np.zeros((S, 3, D)), eps)
+    last = np.array(cu[1:]) - 1
+    # sum_k |w_k v_k| over the (up to) four taps that feed each sample
+    w = np.abs(inputs.bf16_bits_to_f32(cw).astype(np.float64))
+    v = r["g"][:, None] * r["e"]
+    yabs = np.zeros((S, D))
+    for i in range(S):
+        a, b = cu[i], cu[i + 1]
+        n = b - a
+        for k in range(4):
+            j = n - 4 + k
+            if j >= 0:
+                yabs[i] += w[:, k] * np.abs(v[a + j])
+    return dict(row_ids=r["row_ids"][last], x=r["x"][last], e=r["e"][last], g=r["g"][last],
+                y=r["y"][last], out=r["out"][last], yabs=yabs)
+
+
+def check_samples(got: dict, ref: dict, W, label=""):
+    """Compare GPU debug outputs at sampled tokens against oracle_samples()."""
+    assert np.array_equal(got["row_ids"], ref["row_ids"]), f"{label}: row ids"
+    assert np.array_equal(got["x"], ref["x"]), f"{label}: x"
+    eb = e_bound(ref["x"], W)
+    de = np.abs(got["e"].astype(np.float64) - ref["e"])
+    assert np.all(de <= E_REL * eb + 1e-7), f"{label}: e off by {np.max(de / (eb + 1e-30)):.3g} rel"
+    dg = np.abs(got["g"].astype(np.float64) - ref["g"])
+    assert np.all(dg <= G_ABS), f"{label}: gate off by {dg.max():.3g}"
+    dy = np.abs(got["y"].astype(np.float64) - ref["y"])
+    assert np.all(dy <= Y_REL * ref["yabs"] + 1e-6), f"{label}: y off by {dy.max():.3g}"
+    out = inputs.bf16_bits_to_f32(got["out"]).astype(np.float64)
+    do = np.abs(out - ref["out"])
+    assert np.all(do <= OUT_ATOL + OUT_RTOL * np.abs(ref["out"])), f"{label}: out off by {do.max():.3g}"
+    return dict(max_de_rel=float(np.max(de / (eb + 1e-30))), max_dg=float(dg.max()),
+                max_dy=float(dy.max()), max_dout=float(do.max()))
+
+
+def gather_debug(res: dict, idx) -> dict:
+    """Pick rows `idx` of a debug ple_forward result, as host arrays."""
+    ii = torch.as_tensor(np.asarray(idx, dtype=np.int64), device=res["out"].device)
+    return dict(row_ids=res["row_ids"][ii].cpu().numpy(), x=host_bits(res["x"][ii]),
+                e=res["e"][ii].cpu().numpy(), g=res["gate"][ii].cpu().numpy(),
+                y=res["y"][ii].cpu().numpy(), out=host_bits(res["out"][ii]))

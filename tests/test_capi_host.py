@@ -1,0 +1,126 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, every
+symbol include/ple.h declares is exported, and argument validation rejects
+bad calls before anything is enqueued (so these calls never reach a kernel).
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import sparse_memory_gather_amd as ple
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ple.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(ple.LIB_PATH), reason="libple.so not built")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ple_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declarations_are_exported():
+    names = _declared()
+    assert set(names) == set(ple.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", ple.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    for n in names:
+        assert n in exported, n
+    lib = ple.load_library()
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def test_forward_args_struct_matches_header_field_order():
+    src = open(HEADER).read()
+    body = src[src.index("typedef struct ple_forward_args"):src.index("} ple_forward_args;")]
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"\b([a-zA-Z_]+)\s*;", body)
+    assert fields == [f[0] for f in ple.ForwardArgs._fields_]
+
+
+def test_status_strings_and_workspace_size():
+    lib = ple.load_library()
+    assert lib.ple_status_string(0) == b"ok"
+    assert lib.ple_status_string(-6) == b"workspace too small"
+    # workspace: row ids + x + e (bf16) + partial sums per token, conv-state copy per sequence
+    T, S = 1000, 3
+    need = ple.workspace_size(T, S)
+    assert need >= T * (8 + 2560 * 2 * 2 + 20 * 16) + S * 3 * 2560 * 4
+    assert need % 256 == 0 and ple.workspace_size(0, 0) == 0
+
+
+# Every call below fails validation, so no kernel is launched; fake device
+# addresses are fine. Skipped where a GPU is present, so that a validation
+# bug can never turn one of them into a real launch.
+cpu_only = pytest.mark.skipif(torch.cuda.is_available(), reason="host-only checks")
+FAKE = 0x7F0000000000
+
+
+def _fwd_args(**over):
+    a = ple.ForwardArgs()
+    T, S = 64, 2
+    base = FAKE
+    vals = dict(tokens=base, T=T, cu_seqlens=base + 0x1000, S=S, vocab_size=248320,
+                table=base + 0x100000, scales=base + 0x200000, R=1000, W=base + 0x400000,
+                conv_w=base + 0x1400000, h=base + 0x2000000, out=base + 0x3000000,
+                hist_ids=base + 0x4000000, hist_len=base + 0x4001000, conv_state=base + 0x5000000,
+                workspace=base + 0x6000000, workspace_bytes=ple.workspace_size(T, S), eps=1e-6)
+    vals.update(over)
+    for k, v in vals.items():
+        setattr(a, k, v)
+    return a
+
+
+def _call(a):
+    return ple.load_library().ple_forward(ctypes.byref(a), None)
+
+
+@cpu_only
+@pytest.mark.parametrize("over,status", [
+    (dict(R=0), -3), (dict(R=2 ** 31), -3), (dict(vocab_size=0), -3),
+    (dict(vocab_size=(1 << 20) + 1), -3), (dict(S=0), -2), (dict(T=-1), -2),
+    (dict(eps=-1.0), -3), (dict(eps=float("nan")), -3),
+    (dict(tokens=None), -1), (dict(table=None), -1), (dict(conv_state=None), -1),
+    (dict(workspace=None), -6), (dict(workspace_bytes=1000), -6),
+    (dict(h=FAKE + 0x2000000 + 2), -4), (dict(workspace=FAKE + 0x6000000 + 16), -4),
+    (dict(table=FAKE + 0x100000 + 8), -4),
+    (dict(out=FAKE + 0x2000000 + 256), -5),          # partial overlap with h
+    (dict(conv_state=FAKE + 0x3000000), -5),         # state inside out
+    (dict(x_out=FAKE + 0x2000000), -5),              # debug output over h
+])
+def test_forward_rejects_bad_arguments(over, status):
+    st = _call(_fwd_args(**over))
+    assert st == status
+    assert ple.load_library().ple_last_error() != b""
+
+
+@cpu_only
+def test_forward_in_place_and_empty_calls_pass_validation_without_launch():
+    # T = 0 returns OK without touching anything (pointers may be anything)
+    assert _call(_fwd_args(T=0, tokens=None, h=None)) == 0
+    assert ple.load_library().ple_last_error() == b""
+
+
+@cpu_only
+def test_hash_lookup_proj_reject_bad_arguments():
+    lib = ple.load_library()
+    assert lib.ple_hash(FAKE, 10, FAKE + 0x100, 0, FAKE, FAKE, 100, 10, FAKE + 0x1000, None, None) == -2
+    assert lib.ple_hash(FAKE, 10, FAKE + 0x100, 1, FAKE, FAKE, 100, 0, FAKE + 0x1000, None, None) == -3
+    assert lib.ple_hash(FAKE, 10, FAKE + 0x100, 1, FAKE, FAKE, 100, 10, FAKE + 0x1004, None, None) == -4
+    assert lib.ple_hash(FAKE, 10, FAKE + 0x100, 1, FAKE, FAKE, 100, 10, FAKE, None, None) == -5
+    assert lib.ple_hash(FAKE, 0, None, 1, None, None, 100, 10, None, None, None) == 0
+    assert lib.ple_lookup(FAKE, 4, FAKE + 0x10000, None, 10, FAKE + 0x100000, None, None, None) == -1
+    assert lib.ple_lookup(FAKE, 4, FAKE + 0x10008, FAKE + 0x90000, 10, FAKE + 0x100000, None, None,
+                          None) == -4
+    assert lib.ple_lookup(FAKE, 4, FAKE + 0x10000, FAKE + 0x90000, 10, FAKE + 0x10000, None, None,
+                          None) == -5
+    assert lib.ple_proj(FAKE, 4, FAKE + 0x100000, FAKE + 0x100000, None) == -5
+    assert lib.ple_proj(FAKE, -1, FAKE + 0x100000, FAKE + 0x10000000, None) == -2

@@ -1,0 +1,157 @@
+"""GPU parity at the full workload sizes (20,000,096-row, 51.2 GB FP8 table
+in HBM), in the same launch configuration the bench times: every row ID is
+compared with the oracle; sampled tokens (sequence starts, chunk and step
+boundaries, random interior positions) are recomputed one by one by the
+oracle and compared on x, e, gate, y and out."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_memory_gather_amd as ple
+from gen import inputs, table
+
+from parity_util import (D, check_samples, dev_bf16, dev_i32, gather_debug, host_bits,
+                         oracle_samples)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def full_table(dev):
+    t = table.table_gpu(inputs.R_FULL, device=dev)
+    yield t
+    del t
+    torch.cuda.empty_cache()
+
+
+@pytest.fixture(scope="module")
+def dev_weights(dev, weights):
+    W, cw = weights
+    return dev_bf16(W, dev), dev_bf16(cw, dev)
+
+
+def _run(dev, tab, sc, dw, toks, cu, h, state, ws, debug):
+    return ple.ple_forward(dev_i32(toks, dev), dev_i32(cu, dev), tab, sc, dw[0], dw[1],
+                           dev_bf16(h, dev), state, workspace=ws, debug=debug)
+
+
+def _interior(rng, lo, hi, n):
+    return sorted(set(int(v) for v in rng.integers(lo, hi, n)))
+
+
+def test_full_table_generator_sample_matches_cpu(dev, full_table):
+    tab, sc = full_table
+    ids = np.concatenate([np.random.default_rng(11).integers(0, inputs.R_FULL, 10_000),
+                          [0, inputs.R_FULL - 1]])
+    codes, scales = table.rows_cpu(ids)
+    it = torch.as_tensor(ids, device=dev)
+    assert np.array_equal(tab[it].cpu().numpy(), codes)
+    assert np.array_equal(sc[it].cpu().numpy(), scales)
+
+
+@pytest.mark.parametrize("name", ["prefill", "ragged"])
+def test_single_chunk_workloads(dev, full_table, dev_weights, weights, name):
+    W, cw = weights
+    tab, sc = full_table
+    wl = inputs.make_workload(name)
+    toks, cu = wl.chunks[0]
+    h = wl.hidden(0)
+    ws = ple.Workspace(dev)
+    st_a = ple.State(wl.S, dev)
+    out = host_bits(_run(dev, tab, sc, dev_weights, toks, cu, h, st_a, ws, debug=False))
+    st_b = ple.State(wl.S, dev)
+    res = _run(dev, tab, sc, dev_weights, toks, cu, h, st_b, ws, debug=True)
+    assert np.array_equal(host_bits(res["out"]), out)       # debug outputs change nothing
+    assert torch.equal(st_a.conv_state, st_b.conv_state)
+    # every row id
+    ref_ids = oracle.ngram_ids(toks, cu, np.zeros((wl.S, 2), np.int32), np.zeros(wl.S, np.int32), wl.R)
+    assert np.array_equal(res["row_ids"].cpu().numpy(), ref_ids)
+    # sampled tokens: starts of sequences, their 2nd/3rd/4th tokens, ends, interior
+    rng = np.random.default_rng(12)
+    seqs, samples = [], []
+    pick = [0] if wl.S == 1 else [0, 1, 2, 3, 63]
+    for s in pick:
+        a, b = int(cu[s]), int(cu[s + 1])
+        seqs.append((toks[a:b], h[a:b]))
+        pos = [0, 1, 2, 3, b - a - 1] + _interior(rng, 4, b - a - 1, 6 if wl.S == 1 else 2)
+        samples += [(len(seqs) - 1, p) for p in sorted(set(pos))]
+    ref = oracle_samples(seqs, samples, W, cw, wl.R)
+    idx = [int(cu[pick[si]]) + p for si, p in samples]
+    stats = check_samples(gather_debug(res, idx), ref, W, name)
+    print(name, stats)
+    # carried state of the last sequence: hist = its last two tokens
+    last = wl.S - 1
+    assert list(st_a.hist_ids[last].cpu().numpy()) == list(toks[int(cu[last + 1]) - 2:int(cu[last + 1])])
+
+
+def test_long_context_chunks(dev, full_table, dev_weights, weights):
+    W, cw = weights
+    tab, sc = full_table
+    wl = inputs.make_workload("long")
+    ws = ple.Workspace(dev)
+    st = ple.State(1, dev)
+    all_toks = np.concatenate([c[0] for c in wl.chunks])
+    hs, outs, samples_idx = [], [], []
+    rng = np.random.default_rng(13)
+    check_chunks = {0, 1, 7, 15}
+    got_rows = []
+    pos0 = 0
+    for i, (toks, cu) in enumerate(wl.chunks):
+        h = wl.hidden(i)
+        hs.append(h)
+        debug = i in check_chunks
+        res = _run(dev, tab, sc, dev_weights, toks, cu, h, st, ws, debug=debug)
+        if debug:
+            n = len(toks)
+            pos = sorted(set([0, 1, 2, 3, n - 1] + _interior(rng, 4, n - 1, 5)))
+            got_rows.append(gather_debug(res, pos))
+            samples_idx += [pos0 + p for p in pos]
+            ids = res["row_ids"].cpu().numpy()
+            ref_ids = oracle.ngram_ids(all_toks[:pos0 + n], np.array([0, pos0 + n], np.int32),
+                                       np.zeros((1, 2), np.int32), np.zeros(1, np.int32), wl.R)[pos0:]
+            assert np.array_equal(ids, ref_ids), i
+        pos0 += len(toks)
+    h_all = np.concatenate(hs)
+    ref = oracle_samples([(all_toks, h_all)], [(0, p) for p in samples_idx], W, cw, wl.R)
+    got = {k: np.concatenate([g[k] for g in got_rows]) for k in got_rows[0]}
+    print("long", check_samples(got, ref, W, "long"))
+    assert list(st.hist_ids[0].cpu().numpy()) == list(all_toks[-2:])
+
+
+def test_decode_steps_after_history(dev, full_table, dev_weights, weights):
+    W, cw = weights
+    tab, sc = full_table
+    wl = inputs.make_workload("decode", decode_steps=16)
+    S = wl.S
+    hist = wl.history[0]                                   # [8][4096]
+    hlen = hist.shape[1]
+    h_hist = wl.history_hidden(S * hlen)
+    ws = ple.Workspace(dev)
+    st = ple.State(S, dev)
+    cu_h = np.arange(0, S * hlen + 1, hlen, dtype=np.int32)
+    _run(dev, tab, sc, dev_weights, hist.reshape(-1), cu_h, h_hist, st, ws, debug=False)
+    assert np.array_equal(st.hist_ids.cpu().numpy(), hist[:, -2:])
+    steps = []
+    for k, (toks, cu) in enumerate(wl.chunks):
+        h = wl.hidden(k)
+        res = _run(dev, tab, sc, dev_weights, toks, cu, h, st, ws, debug=True)
+        steps.append((toks, h, gather_debug(res, np.arange(S))))
+    # sequences as the oracle sees them: history then one token per step
+    seqs = []
+    for s in range(S):
+        t = np.concatenate([hist[s], [st_[0][s] for st_ in steps]]).astype(np.int32)
+        hh = np.concatenate([h_hist[s * hlen:(s + 1) * hlen], np.stack([st_[1][s] for st_ in steps])])
+        seqs.append((t, hh))
+    check_k = [0, 1, 2, 15]
+    samples = [(s, hlen + k) for k in check_k for s in range(S)]
+    ref = oracle_samples(seqs, samples, W, cw, wl.R)
+    got = {key: np.concatenate([steps[k][2][key] for k in check_k]) for key in steps[0][2]}
+    print("decode", check_samples(got, ref, W, "decode"))

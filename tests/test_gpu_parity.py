@@ -1,0 +1,230 @@
+"""GPU parity of every entry point against the CPU oracle at small sizes that
+still span several tiles, ragged tails and every sequence-boundary case.
+All calls go through the C ABI (libple.so) via the Python binding."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_memory_gather_amd as ple
+from gen import inputs, table
+
+from parity_util import (D, check_samples, dev_bf16, dev_i32, e_bound, gather_debug, host_bits,
+                         oracle_samples, rows, E_REL, OUT_ATOL, OUT_RTOL)
+
+pytestmark = pytest.mark.gpu
+
+R_SMALL = 65_536
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    ple.load_library()
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def small_table(dev):
+    return table.table_gpu(R_SMALL, device=dev)
+
+
+@pytest.fixture(scope="module")
+def dev_weights(dev, weights):
+    W, cw = weights
+    return dev_bf16(W, dev), dev_bf16(cw, dev)
+
+
+def _case(seed, lengths, hist_lens, vocab=inputs.VOCAB):
+    rng = np.random.default_rng(seed)
+    T = int(sum(lengths))
+    toks = inputs.uniform_tokens(rng, T, vocab)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    S = len(lengths)
+    hist = inputs.uniform_tokens(rng, 2 * S, vocab).reshape(S, 2)
+    hl = np.array(hist_lens, np.int32)
+    h = inputs.normal_bf16(rng, (T, D))
+    return toks, cu, hist, hl, h
+
+
+def test_table_generator_gpu_matches_cpu(dev, small_table):
+    tab, sc = small_table
+    ids = np.concatenate([np.arange(8), np.random.default_rng(0).integers(0, R_SMALL, 2000),
+                          [R_SMALL - 1]])
+    codes, scales = rows(ids)
+    it = torch.as_tensor(ids, device=dev)
+    assert np.array_equal(tab[it].cpu().numpy(), codes)
+    assert np.array_equal(sc[it].cpu().numpy(), scales)
+
+
+def test_hash_parity_sequence_boundaries(dev):
+    lengths = [0, 1, 2, 3, 5, 300, 0, 1, 700]
+    hl = [0, 0, 1, 2, 0, 1, 2, 2, 2]
+    toks, cu, hist, hlen, _ = _case(1, lengths, hl)
+    toks[:4] = [0, inputs.VOCAB - 1, 0, inputs.VOCAB - 1]  # vocabulary edges
+    for R in (1, 7, 1009, 20_000_096, 2 ** 31 - 1):
+        ref = oracle.ngram_ids(toks, cu, hist, hlen, R)
+        got = ple.ple_hash(dev_i32(toks, dev), dev_i32(cu, dev), dev_i32(hist, dev), dev_i32(hlen, dev), R)
+        assert np.array_equal(got.cpu().numpy(), ref), R
+
+
+def test_lookup_parity_raw_bytes_and_x(dev, small_table):
+    tab, sc = small_table
+    rng = np.random.default_rng(2)
+    T = 333
+    ids = rng.integers(-1, R_SMALL, (T, 2)).astype(np.int32)
+    ids[ids[:, 0] < 0, 1] = -1
+    ids[3] = [-1, -1]
+    ids[4] = [17, 17]
+    ids[5] = [-1, 9]          # trigram without bigram: only that row
+    ids[6] = [R_SMALL - 1, 0]
+    raw = torch.empty((T, 2, D), dtype=torch.uint8, device=dev)
+    x = ple.ple_lookup(dev_i32(ids, dev), tab, sc, raw=raw)
+    uniq = np.unique(ids[ids >= 0])
+    codes, scales = rows(uniq)
+    remap = np.full(ids.shape, -1, np.int32)
+    remap[ids >= 0] = np.searchsorted(uniq, ids[ids >= 0])
+    xr, rr = oracle.gather_dequant(remap, codes, scales, raw=True)
+    assert np.array_equal(raw.cpu().numpy(), rr)
+    assert np.array_equal(host_bits(x), xr)
+
+
+def test_lookup_decodes_every_e4m3_code(dev):
+    # 256 rows; row r holds code r everywhere; scale 1 -> x = bf16(decode(r))
+    codes = np.repeat(np.arange(256, dtype=np.uint8)[:, None], D, axis=1)
+    tab = torch.from_numpy(codes).to(dev)
+    sc = torch.ones(256, dtype=torch.float32, device=dev)
+    ids = np.stack([np.arange(256), np.full(256, -1)], axis=1).astype(np.int32)
+    x = host_bits(ple.ple_lookup(dev_i32(ids, dev), tab, sc))
+    ref = oracle.gather_dequant(ids, codes, np.ones(256, np.float32))
+    nan = np.array([c & 0x7F == 0x7F for c in range(256)])
+    assert np.array_equal(x[~nan], ref[~nan])
+    f = torch.from_numpy(x[nan].view(np.int16)).view(torch.bfloat16).float()
+    assert torch.isnan(f).all()
+
+
+def test_proj_parity_ragged_tail(dev, dev_weights, weights):
+    W, _ = weights
+    rng = np.random.default_rng(3)
+    for T in (1, 37, 300, 513):
+        x = inputs.normal_bf16(rng, (T, D), std=0.08)
+        e = ple.ple_proj(dev_bf16(x, dev), dev_weights[0]).cpu().numpy().astype(np.float64)
+        ref = oracle.project(x, W)
+        bound = E_REL * e_bound(x, W) + 1e-7
+        assert np.all(np.abs(e - ref) <= bound), T
+
+
+def _forward(dev, tab, sc, dw, toks, cu, h, state, **kw):
+    return ple.ple_forward(dev_i32(toks, dev), dev_i32(cu, dev), tab, sc, dw[0], dw[1], dev_bf16(h, dev),
+                           state, debug=True, **kw)
+
+
+def test_forward_tiny_workload_full_parity(dev, small_table, dev_weights, weights):
+    W, cw = weights
+    tab, sc = small_table
+    wl = inputs.make_workload("tiny")
+    toks, cu = wl.chunks[0]
+    h = wl.hidden(0)
+    st = ple.State(1, dev)
+    res = _forward(dev, tab, sc, dev_weights, toks, cu, h, st)
+    ref = oracle.forward(toks, cu, h, W, cw, wl.R, rows)
+    got = gather_debug(res, np.arange(len(toks)))
+    assert np.array_equal(got["row_ids"], ref["row_ids"])
+    assert np.array_equal(got["x"], ref["x"])
+    # token 0 of a fresh sequence: nothing to add, out == h bit-exactly
+    assert np.array_equal(got["out"][0], h[0]) and got["g"][0] == 0.5
+    seqs = [(toks, h)]
+    samples = [(0, p) for p in range(len(toks))]
+    refs = oracle_samples(seqs, samples, W, cw, wl.R)
+    check_samples(got, refs, W, "tiny")
+    # carried state equals the oracle's
+    assert np.array_equal(st.hist_ids.cpu().numpy(), ref["hist_ids"])
+    assert np.array_equal(st.hist_len.cpu().numpy(), ref["hist_len"])
+    np.testing.assert_allclose(st.conv_state.cpu().numpy(), ref["conv_state"], rtol=2e-2, atol=1e-4)
+
+
+def test_forward_sequence_edge_cases_with_carried_state(dev, small_table, dev_weights, weights):
+    W, cw = weights
+    tab, sc = small_table
+    lengths = [0, 1, 2, 3, 17, 300, 5, 1]
+    hl = [2, 0, 1, 2, 0, 1, 2, 1]
+    toks, cu, hist, hlen, h = _case(4, lengths, hl)
+    S = len(lengths)
+    rng = np.random.default_rng(5)
+    state0 = (0.05 * rng.standard_normal((S, 3, D))).astype(np.float32)
+    st = ple.State(S, dev)
+    st.hist_ids.copy_(dev_i32(hist, dev))
+    st.hist_len.copy_(dev_i32(hlen, dev))
+    st.conv_state.copy_(torch.from_numpy(state0).to(dev))
+    res = _forward(dev, tab, sc, dev_weights, toks, cu, h, st)
+    ref = oracle.forward(toks, cu, h, W, cw, R_SMALL, rows, hist, hlen, state0.astype(np.float64))
+    got = gather_debug(res, np.arange(len(toks)))
+    assert np.array_equal(got["row_ids"], ref["row_ids"])
+    assert np.array_equal(got["x"], ref["x"])
+    out = inputs.bf16_bits_to_f32(got["out"]).astype(np.float64)
+    assert np.all(np.abs(out - ref["out"]) <= OUT_ATOL + OUT_RTOL * np.abs(ref["out"]))
+    assert np.all(np.abs(got["g"] - ref["g"]) <= 1e-4)
+    assert np.allclose(got["y"], ref["y"], rtol=1e-2, atol=1e-4)
+    hid = st.hist_ids.cpu().numpy()
+    hln = st.hist_len.cpu().numpy()
+    assert np.array_equal(hln, ref["hist_len"])
+    for s in range(S):
+        k = ref["hist_len"][s]
+        assert np.array_equal(hid[s][2 - k:], ref["hist_ids"][s][2 - k:]), s
+    np.testing.assert_allclose(st.conv_state.cpu().numpy(), ref["conv_state"], rtol=2e-2, atol=1e-4)
+    # the empty sequence 0 keeps its state bit-exactly
+    assert np.array_equal(st.conv_state[0].cpu().numpy(), state0[0])
+
+
+def test_chunked_equals_unchunked_and_decode_equals_prefill(dev, small_table, dev_weights):
+    tab, sc = small_table
+    rng = np.random.default_rng(6)
+    n = 270
+    toks = inputs.uniform_tokens(rng, n)
+    h = inputs.normal_bf16(rng, (n, D))
+
+    def run(cuts):
+        st = ple.State(1, dev)
+        outs, pos = [], 0
+        for L in cuts:
+            r = _forward(dev, tab, sc, dev_weights, toks[pos:pos + L], np.array([0, L], np.int32),
+                         h[pos:pos + L], st)
+            outs.append(host_bits(r["out"]))
+            pos += L
+        return np.concatenate(outs), st.conv_state.cpu().numpy(), st.hist_ids.cpu().numpy()
+
+    full = run([n])
+    for cuts in ([1, 2, 3, 264], [256, 14], [100, 0, 170], [1] * 20 + [250]):
+        got = run(cuts)
+        for a, b in zip(got, full):
+            assert np.array_equal(a, b), cuts
+
+
+def test_in_place_out_equals_h(dev, small_table, dev_weights):
+    tab, sc = small_table
+    rng = np.random.default_rng(7)
+    toks = inputs.uniform_tokens(rng, 300)
+    h = inputs.normal_bf16(rng, (300, D))
+    cu = np.array([0, 120, 300], np.int32)
+    ref = _forward(dev, tab, sc, dev_weights, toks, cu, h, ple.State(2, dev))
+    hd = dev_bf16(h, dev)
+    out = ple.ple_forward(dev_i32(toks, dev), dev_i32(cu, dev), tab, sc, dev_weights[0], dev_weights[1],
+                          hd, ple.State(2, dev), out=hd)
+    assert out.data_ptr() == hd.data_ptr()
+    assert np.array_equal(host_bits(hd), host_bits(ref["out"]))
+
+
+def test_save_restore_state_resumes_identically(dev, small_table, dev_weights):
+    tab, sc = small_table
+    rng = np.random.default_rng(8)
+    toks = inputs.uniform_tokens(rng, 64)
+    h = inputs.normal_bf16(rng, (64, D))
+    cu = np.array([0, 32], np.int32)
+    st = ple.State(1, dev)
+    _forward(dev, tab, sc, dev_weights, toks[:32], cu, h[:32], st)
+    saved = st.clone()
+    a = _forward(dev, tab, sc, dev_weights, toks[32:], cu, h[32:], st)
+    b = _forward(dev, tab, sc, dev_weights, toks[32:], cu, h[32:], saved)
+    assert np.array_equal(host_bits(a["out"]), host_bits(b["out"]))
+    assert torch.equal(st.conv_state, saved.conv_state)
