@@ -49,6 +49,15 @@ def e_bound(x_bits: np.ndarray, W_bits: np.ndarray) -> np.ndarray:
     return xa @ Wa.T
 
 
+def y_bound(ref: dict, cu, cw, state) -> np.ndarray:
+    """Y_REL * sum_k |w_k| |v_{t-3+k}| per element (the y tolerance), from the
+    oracle's g and e and the incoming state, via the oracle's own conv on
+    absolute values."""
+    y, _, _ = oracle.conv_fuse(np.zeros(ref["e"].shape, np.uint16), np.abs(ref["e"]), np.abs(ref["g"]),
+                               cu, np.asarray(cw) & 0x7FFF, np.abs(state))
+    return Y_REL * y + 1e-6
+
+
 def oracle_samples(seqs, samples, W, cw, R, eps=1e-6):
     """Reference outputs of sampled tokens.
 
