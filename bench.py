@@ -125,6 +125,8 @@ def main():
     ap.add_argument("--workload", default="prefill", choices=["tiny", "decode", "prefill", "ragged", "long"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -286,6 +288,15 @@ def main():
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         h0 = wl.hidden(0)
         result["cpu_baseline"] = cpu_baseline(wl, name, W, cw, h0, args.cpu_budget)
+    if args.copy_calibration:
+        # a plain copy of known size: FETCH_SIZE / WRITE_SIZE of this dispatch
+        # calibrate the per-kernel counters to bytes
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = 1 << 30
     print(json.dumps(result), flush=True)
 
 

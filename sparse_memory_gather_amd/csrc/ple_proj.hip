@@ -5,13 +5,18 @@
 // section). It is the only dense contraction on the path: [T x 2560] times
 // [2560 x 2560]^T, both operands K-contiguous.
 //
-// Block tile 256 tokens x 256 features x 64 k, four waves in a 2x2 grid,
-// each wave a 128 x 128 sub-tile of 4x4 v_mfma_f32_32x32x16_bf16 tiles. W
-// rows feed the MFMA A operand and tokens the B operand, so a lane's
-// accumulators hold one token and runs of four consecutive features (8-byte
-// bf16 stores). Operands are double-buffered in LDS (128 KB), with the 16-byte
-// chunks of each 128-byte row XOR-swizzled by (row & 7) so that the MFMA
-// fragment reads are bank-conflict free.
+// Block tile 256 features x 256 tokens x 64 k, eight waves (two per SIMD, so
+// one wave's LDS waits overlap the other's MFMAs), each wave a 128-feature x
+// 64-token sub-tile of 4x2 v_mfma_f32_32x32x16_bf16 tiles. W rows feed the
+// MFMA A operand and tokens the B operand, so a lane's accumulators hold one
+// token and runs of four consecutive features (8-byte bf16 stores).
+//
+// Operands move global -> LDS with global_load_lds_dwordx4 (no register
+// staging) into two 64 KB stages; each wave-level load fills 1 KB of LDS
+// (eight 128-byte rows). The 16-byte chunks of a row are XOR-swizzled by
+// (row >> 1) & 7: gfx950's LDS serves a ds_read_b128 sixteen lanes at a time
+// across 256 bytes, and 16 consecutive 128-byte rows then hit 16 distinct
+// 16-byte bank groups.
 //
 // Forward mode also reduces, per token and per 128-feature slice, the sums
 // e^2, h.e and h^2 that the gate needs (fp32, before e is rounded to bf16).
@@ -24,13 +29,24 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_void;
 
 constexpr int BM = 256;  // tokens per block
 constexpr int BN = 256;  // features per block
 constexpr int BK = 64;   // k per stage
 constexpr int KT = kD / BK;
-constexpr int kThreads = 256;
-constexpr int kLdsBytes = 2 * (BM + BN) * BK * 2;  // 131072
+constexpr int CH = BK / 8;               // 16-byte chunks per row of a stage
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int RPL = 64 / CH;             // rows filled by one wave-level load
+constexpr int LPW = BM / (kWaves * RPL); // loads per wave per operand per stage
+constexpr int STAGE = (BM + BN) * BK;    // bf16 elements per stage
+constexpr int kNTiles = kD / BN;         // feature tiles per token tile
+constexpr int kXcds = 8;                 // accelerator complex dies on MI355X
+constexpr int kLdsBytes = 2 * STAGE * 2; // 131072
+
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & (CH - 1); }
 
 template <bool kFwd>
 __global__ void __launch_bounds__(kThreads, 1)
@@ -38,81 +54,85 @@ proj_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __restric
             float* __restrict__ e32, uint16_t* __restrict__ e16, const uint16_t* __restrict__ h,
             float* __restrict__ parts) {
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-    uint16_t* sW = lds;                  // [2][BN][BK]
-    uint16_t* sX = lds + 2 * BN * BK;    // [2][BM][BK]
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int fh = wave & 1, th = wave >> 1;
-    const int n0 = blockIdx.x * BN;
-    const int64_t m0 = (int64_t)blockIdx.y * BM;
+    const int fh = wave & 1, tq = wave >> 1;  // 128-feature half, 64-token quarter
+    // Workgroups are handed to the 8 XCDs round-robin (block b -> XCD b % 8).
+    // Give each XCD a contiguous run of tiles, feature tiles fastest, so the
+    // blocks resident on one XCD share their x panels in that XCD's L2.
+    const int nb = gridDim.x, b = blockIdx.x;
+    const int per = nb / kXcds, rem = nb % kXcds, xcd = b % kXcds;
+    const int tile = xcd * per + (xcd < rem ? xcd : rem) + b / kXcds;
+    const int n0 = (tile % kNTiles) * BN;
+    const int64_t m0 = (int64_t)(tile / kNTiles) * BM;
 
-    // global -> LDS copy assignment: chunk (row = lrow + 32 i, 16-byte column lc)
-    const int lrow = tid >> 3, lc = tid & 7;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    u32x4 gw[8], gx[8];
-
-    auto gload = [&](int kt) {
-        const int k0 = kt * BK + lc * 8;
+    // DMA assignment: load i of this wave fills rows R = (wave*LPW + i)*RPL ..
+    // +RPL of both operands; lane l writes row R + l/CH, physical chunk l%CH,
+    // which holds logical chunk (l%CH) ^ swz(row).
+    const uint16_t* gW[LPW];
+    const uint16_t* gX[LPW];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int row = lrow + 32 * i;
-            gw[i] = *reinterpret_cast<const u32x4*>(W + (int64_t)(n0 + row) * kD + k0);
-            const int64_t tok = m0 + row;
-            gx[i] = tok < M ? *reinterpret_cast<const u32x4*>(x + tok * kD + k0) : zero;
+    for (int i = 0; i < LPW; ++i) {
+        const int row = (wave * LPW + i) * RPL + lane / CH;
+        const int c = (lane % CH) ^ swz(row);
+        gW[i] = W + (int64_t)(n0 + row) * kD + c * 8;
+        const int64_t tok = m0 + row;
+        // rows past the last token read token 0 (in bounds); their results are never stored
+        gX[i] = x + (tok < M ? tok : 0) * kD + c * 8;
+    }
+    auto issue = [&](int kt) {
+        uint16_t* sbase = lds + (kt & 1) * STAGE;
+        const int k0 = kt * BK;
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) {
+            uint16_t* dW = sbase + (wave * LPW + i) * RPL * BK;
+            __builtin_amdgcn_global_load_lds((gbl_void*)(gW[i] + k0), (lds_void*)dW, 16, 0, 0);
+            uint16_t* dX = sbase + BN * BK + (wave * LPW + i) * RPL * BK;
+            __builtin_amdgcn_global_load_lds((gbl_void*)(gX[i] + k0), (lds_void*)dX, 16, 0, 0);
         }
     };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int row = lrow + 32 * i;
-            const int off = row * BK + ((lc ^ (row & 7)) * 8);
-            *reinterpret_cast<u32x4*>(sW + buf * BN * BK + off) = gw[i];
-            *reinterpret_cast<u32x4*>(sX + buf * BM * BK + off) = gx[i];
-        }
-    };
 
-    f32x16 acc[4][4];
+    f32x16 acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    gload(0);
-    lstore(0);
-    __syncthreads();
-
-    const int fr = lane & 31, kh = lane >> 5, sw = fr & 7;
+    issue(0);
+    const int fr = lane & 31, kh = lane >> 5, sw = swz(fr);
     for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < KT) gload(kt + 1);
-        const uint16_t* cW = sW + cur * BN * BK;
-        const uint16_t* cX = sX + cur * BM * BK;
+        // stage kt has landed for this wave (vmcnt counts the LDS-DMA loads);
+        // the barrier makes every wave's part visible and marks the other
+        // stage, read during kt-1, free for the next DMA
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt, lgkmcnt untouched
+        __builtin_amdgcn_s_barrier();
+        if (kt + 1 < KT) issue(kt + 1);
+        const uint16_t* cW = lds + (kt & 1) * STAGE;
+        const uint16_t* cX = cW + BN * BK;
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
             const int c = ((ks * 2 + kh) ^ sw) * 8;
-            bf16x8 a[4], b[4];
+            bf16x8 a[4], bb[2];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 a[i] = *reinterpret_cast<const bf16x8*>(cW + (fh * 128 + i * 32 + fr) * BK + c);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                b[j] = *reinterpret_cast<const bf16x8*>(cX + (th * 128 + j * 32 + fr) * BK + c);
+            for (int j = 0; j < 2; ++j)
+                bb[j] = *reinterpret_cast<const bf16x8*>(cX + (tq * 64 + j * 32 + fr) * BK + c);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
         }
-        if (kt + 1 < KT) lstore(cur ^ 1);
-        __syncthreads();
     }
 
     // epilogue: lane holds token (.. + fr) and features (.. + 8 g + 4 kh + 0..3)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int64_t tok = m0 + th * 128 + j * 32 + fr;
+    for (int j = 0; j < 2; ++j) {
+        const int64_t tok = m0 + tq * 64 + j * 32 + fr;
         const bool live = tok < M;
         float ee = 0.0f, he = 0.0f, hh = 0.0f;
 #pragma unroll
@@ -170,7 +190,7 @@ hipError_t launch(const uint16_t* x, int64_t T, const uint16_t* W, float* e32, u
         if (err != hipSuccess) return err;
         allowed.fetch_or(bit, std::memory_order_acq_rel);
     }
-    dim3 grid(kD / BN, (unsigned)((T + BM - 1) / BM));
+    dim3 grid((unsigned)(kNTiles * ((T + BM - 1) / BM)));
     hipLaunchKernelGGL(proj_kernel<kFwd>, grid, dim3(kThreads), kLdsBytes, stream, x, T, W, e32,
                        e16, h, parts);
     return hipGetLastError();
