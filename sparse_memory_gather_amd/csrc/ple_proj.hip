@@ -45,8 +45,56 @@ constexpr int STAGE = (BM + BN) * BK;    // bf16 elements per stage
 constexpr int kNTiles = kD / BN;         // feature tiles per token tile
 constexpr int kXcds = 8;                 // accelerator complex dies on MI355X
 constexpr int kLdsBytes = 2 * STAGE * 2; // 131072
+constexpr int kSmallT = 256;            // token counts served by proj_small_kernel
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & (CH - 1); }
+
+// Output of one lane for one 32-token tile of a 128-feature slice: vals[i] are
+// the lane's 16 accumulators of feature tile i (features fbase + 32 i + 8 g +
+// 4 kh + 0..3, g = r / 4) for token `tok`. Writes e (fp32 and/or bf16) and, in
+// forward mode, the slice's gate sums e^2, h.e, h^2 in one fixed order.
+template <bool kFwd>
+__device__ __forceinline__ void emit_slice(const float (&vals)[4][16], int64_t tok, int64_t M, int fbase,
+                                           int kh, float* __restrict__ e32, uint16_t* __restrict__ e16,
+                                           const uint16_t* __restrict__ h, float* __restrict__ parts) {
+    const bool live = tok < M;
+    float ee = 0.0f, he = 0.0f, hh = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int f = fbase + i * 32 + g * 8 + kh * 4;
+            const float v0 = vals[i][4 * g + 0], v1 = vals[i][4 * g + 1];
+            const float v2 = vals[i][4 * g + 2], v3 = vals[i][4 * g + 3];
+            if (!live) continue;
+            const int64_t off = tok * kD + f;
+            if (!kFwd || e32) {
+                f32x4 o = {v0, v1, v2, v3};
+                *reinterpret_cast<f32x4*>(e32 + off) = o;
+            }
+            if (kFwd) {
+                u32x2 hb = *reinterpret_cast<const u32x2*>(h + off);
+                const float h0 = bf16_to_f32(hb[0] & 0xFFFFu), h1 = bf16_to_f32(hb[0] >> 16);
+                const float h2 = bf16_to_f32(hb[1] & 0xFFFFu), h3 = bf16_to_f32(hb[1] >> 16);
+                ee = ee + fmaf(v3, v3, fmaf(v2, v2, fmaf(v1, v1, v0 * v0)));
+                he = he + fmaf(h3, v3, fmaf(h2, v2, fmaf(h1, v1, h0 * v0)));
+                hh = hh + fmaf(h3, h3, fmaf(h2, h2, fmaf(h1, h1, h0 * h0)));
+                u32x2 ob = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+                *reinterpret_cast<u32x2*>(e16 + off) = ob;
+            }
+        }
+    }
+    if (kFwd) {
+        ee += __shfl_xor(ee, 32);
+        he += __shfl_xor(he, 32);
+        hh += __shfl_xor(hh, 32);
+        if (live && kh == 0) {
+            const int part = fbase / kPartCols;
+            f32x4 p = {ee, he, hh, 0.0f};
+            *reinterpret_cast<f32x4*>(parts + (tok * kParts + part) * kPartStride) = p;
+        }
+    }
+}
 
 template <bool kFwd>
 __global__ void __launch_bounds__(kThreads, 1)
@@ -132,47 +180,68 @@ proj_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __restric
     // epilogue: lane holds token (.. + fr) and features (.. + 8 g + 4 kh + 0..3)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const int64_t tok = m0 + tq * 64 + j * 32 + fr;
-        const bool live = tok < M;
-        float ee = 0.0f, he = 0.0f, hh = 0.0f;
+        float vals[4][16];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int f = n0 + fh * 128 + i * 32 + g * 8 + kh * 4;
-                const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
-                const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
-                if (!live) continue;
-                const int64_t off = tok * kD + f;
-                if (!kFwd || e32) {
-                    f32x4 o = {v0, v1, v2, v3};
-                    *reinterpret_cast<f32x4*>(e32 + off) = o;
-                }
-                if (kFwd) {
-                    u32x2 hb = *reinterpret_cast<const u32x2*>(h + off);
-                    const float h0 = bf16_to_f32(hb[0] & 0xFFFFu), h1 = bf16_to_f32(hb[0] >> 16);
-                    const float h2 = bf16_to_f32(hb[1] & 0xFFFFu), h3 = bf16_to_f32(hb[1] >> 16);
-                    ee += v0 * v0 + v1 * v1 + v2 * v2 + v3 * v3;
-                    he += h0 * v0 + h1 * v1 + h2 * v2 + h3 * v3;
-                    hh += h0 * h0 + h1 * h1 + h2 * h2 + h3 * h3;
-                    u32x2 ob = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-                    *reinterpret_cast<u32x2*>(e16 + off) = ob;
-                }
-            }
-        }
-        if (kFwd) {
-            ee += __shfl_xor(ee, 32);
-            he += __shfl_xor(he, 32);
-            hh += __shfl_xor(hh, 32);
-            if (live && kh == 0) {
-                const int part = (n0 + fh * 128) / kPartCols;
-                f32x4 p = {ee, he, hh, 0.0f};
-                *reinterpret_cast<f32x4*>(parts + (tok * kParts + part) * kPartStride) = p;
-            }
-        }
+            for (int r = 0; r < 16; ++r) vals[i][r] = acc[i][j][r];
+        emit_slice<kFwd>(vals, m0 + tq * 64 + j * 32 + fr, M, n0 + fh * 128, kh, e32, e16, h, parts);
         // keep each token tile's loads and stores together (bounds register pressure)
         __builtin_amdgcn_sched_barrier(0);
     }
+}
+
+// Small-T projection (decode steps, short chunks): one block per (128-feature
+// slice, 32-token tile), one wave per 32-feature tile, each wave one MFMA
+// chain over the whole K in the same k order as proj_kernel, fragments loaded
+// straight from global memory eight k-steps ahead. The four tiles meet in LDS
+// and wave 0 runs the same epilogue as proj_kernel, so every output element
+// (e and the gate sums) is bit-identical to what proj_kernel produces.
+template <bool kFwd>
+__global__ void __launch_bounds__(256)
+proj_small_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __restrict__ W,
+                  float* __restrict__ e32, uint16_t* __restrict__ e16, const uint16_t* __restrict__ h,
+                  float* __restrict__ parts) {
+    __shared__ float tile_s[4][64][17];  // [feature tile][lane][accumulator], padded
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int fr = lane & 31, kh = lane >> 5;
+    const int fbase = blockIdx.x * 128;
+    const int64_t tok = (int64_t)blockIdx.y * 32 + fr;
+    const bool live_tok = tok < M;
+    const uint16_t* wrow = W + (int64_t)(fbase + wave * 32 + fr) * kD + kh * 8;
+    const uint16_t* xrow = x + (live_tok ? tok : 0) * kD + kh * 8;
+    constexpr int KS = kD / 16;  // 160 k-steps
+    bf16x8 fa[2][8], fb[2][8];
+    const bf16x8 zero = {};
+    auto load8 = [&](int s0, int buf) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            fa[buf][q] = *reinterpret_cast<const bf16x8*>(wrow + (s0 + q) * 16);
+            fb[buf][q] = live_tok ? *reinterpret_cast<const bf16x8*>(xrow + (s0 + q) * 16) : zero;
+        }
+    };
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    load8(0, 0);
+    for (int s0 = 0; s0 < KS; s0 += 16) {
+        load8(s0 + 8, 1);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][q], fb[0][q], acc, 0, 0, 0);
+        if (s0 + 16 < KS) load8(s0 + 16, 0);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][q], fb[1][q], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) tile_s[wave][lane][r] = acc[r];
+    __syncthreads();
+    if (wave != 0) return;
+    float vals[4][16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) vals[i][r] = tile_s[i][lane][r];
+    emit_slice<kFwd>(vals, tok, M, fbase, kh, e32, e16, h, parts);
 }
 
 template <bool kFwd>
@@ -189,6 +258,12 @@ hipError_t launch(const uint16_t* x, int64_t T, const uint16_t* W, float* e32, u
                                   hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
         if (err != hipSuccess) return err;
         allowed.fetch_or(bit, std::memory_order_acq_rel);
+    }
+    if (T <= kSmallT) {
+        dim3 grid(kD / 128, (unsigned)((T + 31) / 32));
+        hipLaunchKernelGGL(proj_small_kernel<kFwd>, grid, dim3(256), 0, stream, x, T, W, e32, e16, h,
+                           parts);
+        return hipGetLastError();
     }
     dim3 grid((unsigned)(kNTiles * ((T + BM - 1) / BM)));
     hipLaunchKernelGGL(proj_kernel<kFwd>, grid, dim3(kThreads), kLdsBytes, stream, x, T, W, e32,
