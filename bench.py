@@ -44,6 +44,35 @@ PROJ_FLOP_PER_TOKEN = 2 * D * D
 FUSE_BYTES_PER_TOKEN = 3 * 2 * D + 20 * 16
 
 
+KERNEL_SOURCES = {
+    "proj_kernel": ["sparse_memory_gather_amd/csrc/ple_proj.hip", "sparse_memory_gather_amd/csrc/ple_kernels.h"],
+    "gather_kernel": ["sparse_memory_gather_amd/csrc/ple_gather.hip", "sparse_memory_gather_amd/csrc/ple_kernels.h"],
+    "fuse_kernel": ["sparse_memory_gather_amd/csrc/ple_fuse.hip", "sparse_memory_gather_amd/csrc/ple_kernels.h"],
+}
+
+
+def recorded_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary
+    (profiles/hbm_traffic_<workload>.md), or None when there is none or the
+    kernel's source has changed since the counters were taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
+    if not os.path.exists(path) or kernel not in KERNEL_SOURCES:
+        return None
+    h = hashlib.sha256()
+    for src in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    digest = h.hexdigest()[:16]
+    with open(path) as f:
+        for line in f:
+            m = re.match(r"traffic: kernel=(\S+) source_sha256=(\S+) bytes_per_launch=(\d+)", line.strip())
+            if m and m.group(1) == kernel and m.group(2) == digest:
+                return int(m.group(3))
+    return None
+
+
 class HipEvents:
     """Raw hipEvent_t handles from the HIP runtime torch already loaded."""
 
@@ -247,19 +276,22 @@ def main():
     if dominant == 2:
         roofline = {"kernel": "ple_proj (proj_kernel, forward variant)", "bound": "mfma",
                     "achieved": round(proj_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(proj_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "frac": round(proj_tflops / BF16_PEAK_TFLOPS, 4),
+                    "traffic": recorded_traffic("proj_kernel", name),
                     "per_launch": {"flop": proj_flop, "avg_us": round(float(stage_us[2]), 2)}}
     elif dominant == 1:
         roofline = {"kernel": "ple_gather_dequant (gather_kernel)", "bound": "hbm",
                     "achieved": round(gather_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(gather_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                    "frac": round(gather_gbs / HBM_PEAK_GBS, 4),
+                    "traffic": recorded_traffic("gather_kernel", name),
                     "per_launch": {"bytes": gather_bytes, "avg_us": round(float(stage_us[1]), 2)}}
     else:
         k = ["ple_hash (hash_kernel)", "", "", "ple_gate_conv_fuse (fuse_kernel)"][dominant]
         nb = fuse_bytes if dominant == 3 else tokens_per_call * 12
         gbs = nb / (stage_us[dominant] * 1e-6) / 1e9
         roofline = {"kernel": k, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                    "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                    "traffic": recorded_traffic("fuse_kernel", name) if dominant == 3 else None,
                     "per_launch": {"bytes": nb, "avg_us": round(float(stage_us[dominant]), 2)}}
 
     result = {
@@ -274,7 +306,8 @@ def main():
                       "proj": round(float(stage_us[2]), 2), "fuse": round(float(stage_us[3]), 2)},
         "gather": {"bound": "hbm", "achieved": round(gather_gbs, 1), "peak": HBM_PEAK_GBS,
                    "unit": "GB/s", "frac": round(gather_gbs / HBM_PEAK_GBS, 4),
-                   "bytes_per_launch": gather_bytes, "lookups_per_launch": lookups},
+                   "bytes_per_launch": gather_bytes, "lookups_per_launch": lookups,
+                   "traffic": recorded_traffic("gather_kernel", name)},
         "proj": {"bound": "mfma", "achieved": round(proj_tflops, 2), "peak": BF16_PEAK_TFLOPS,
                  "unit": "TFLOP/s", "frac": round(proj_tflops / BF16_PEAK_TFLOPS, 4)},
         "fuse": {"bound": "hbm", "achieved": round(fuse_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
