@@ -150,7 +150,7 @@ fuse_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ e16,
             for (int q = 0; q < FPT; ++q) y[q] = conv4(w[q], e[i][q], e[i + 1][q], e[i + 2][q], e[i + 3][q]);
             u32x2 o = {pack_bf16x2(hv[i][0] + y[0], hv[i][1] + y[1]),
                        pack_bf16x2(hv[i][2] + y[2], hv[i][3] + y[3])};
-            *reinterpret_cast<u32x2*>(out + t * kD + c0) = o;
+            __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(out + t * kD + c0));
             if (y_out) *reinterpret_cast<f32x4*>(y_out + t * kD + c0) = f32x4{y[0], y[1], y[2], y[3]};
         }
         return;
@@ -189,7 +189,7 @@ fuse_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ e16,
 #pragma unroll
         for (int q = 0; q < FPT; ++q) y[q] = conv4(w[q], win[0][q], win[1][q], win[2][q], vt[q]);
         u32x2 o = {pack_bf16x2(hv[0] + y[0], hv[1] + y[1]), pack_bf16x2(hv[2] + y[2], hv[3] + y[3])};
-        *reinterpret_cast<u32x2*>(out + t * kD + c0) = o;
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(out + t * kD + c0));
         if (y_out) *reinterpret_cast<f32x4*>(y_out + t * kD + c0) = f32x4{y[0], y[1], y[2], y[3]};
 #pragma unroll
         for (int q = 0; q < FPT; ++q) {
