@@ -53,10 +53,16 @@ __device__ __forceinline__ int swz(int row) { return (row >> 1) & (CH - 1); }
 // the lane's 16 accumulators of feature tile i (features fbase + 32 i + 8 g +
 // 4 kh + 0..3, g = r / 4) for token `tok`. Writes e (fp32 and/or bf16) and, in
 // forward mode, the slice's gate sums e^2, h.e, h^2 in one fixed order.
-template <bool kFwd>
+//
+// With kStage, the bf16 e values go to the wave's LDS staging tile instead of
+// global memory: row `srow` (the token within the wave's 64), 16-byte chunk
+// (feature offset / 8) XOR (srow & 15), so that the 32 rows a store
+// instruction touches spread over all 64 banks.
+template <bool kFwd, bool kStage>
 __device__ __forceinline__ void emit_slice(const float (&vals)[4][16], int64_t tok, int64_t M, int fbase,
                                            int kh, float* __restrict__ e32, uint16_t* __restrict__ e16,
-                                           const uint16_t* __restrict__ h, float* __restrict__ parts) {
+                                           const uint16_t* __restrict__ h, float* __restrict__ parts,
+                                           uint16_t* stage = nullptr, int srow = 0) {
     const bool live = tok < M;
     float ee = 0.0f, he = 0.0f, hh = 0.0f;
 #pragma unroll
@@ -80,7 +86,10 @@ __device__ __forceinline__ void emit_slice(const float (&vals)[4][16], int64_t t
                 he = he + fmaf(h3, v3, fmaf(h2, v2, fmaf(h1, v1, h0 * v0)));
                 hh = hh + fmaf(h3, h3, fmaf(h2, h2, fmaf(h1, h1, h0 * h0)));
                 u32x2 ob = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-                *reinterpret_cast<u32x2*>(e16 + off) = ob;
+                if (kStage)
+                    *reinterpret_cast<u32x2*>(stage + srow * 128 + ((4 * i + g) ^ (srow & 15)) * 8 + kh * 4) = ob;
+                else
+                    *reinterpret_cast<u32x2*>(e16 + off) = ob;
             }
         }
     }
@@ -177,7 +186,11 @@ proj_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __restric
         }
     }
 
-    // epilogue: lane holds token (.. + fr) and features (.. + 8 g + 4 kh + 0..3)
+    // epilogue: lane holds token (.. + fr) and features (.. + 8 g + 4 kh + 0..3).
+    // In forward mode the bf16 e tile of each wave (64 tokens x 128 features,
+    // 16 KB) is staged in LDS, which every wave must have finished reading.
+    uint16_t* stage = lds + wave * (64 * 128);
+    if (kFwd) __syncthreads();
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         float vals[4][16];
@@ -185,9 +198,24 @@ proj_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __restric
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) vals[i][r] = acc[i][j][r];
-        emit_slice<kFwd>(vals, m0 + tq * 64 + j * 32 + fr, M, n0 + fh * 128, kh, e32, e16, h, parts);
+        emit_slice<kFwd, kFwd>(vals, m0 + tq * 64 + j * 32 + fr, M, n0 + fh * 128, kh, e32, e16, h, parts,
+                               stage, j * 32 + fr);
         // keep each token tile's loads and stores together (bounds register pressure)
         __builtin_amdgcn_sched_barrier(0);
+    }
+    if (kFwd) {
+        // the wave's own LDS writes are complete before its reads (in-order LDS
+        // queue per wave); each store instruction writes four 256-byte token
+        // rows, non-temporal since e is only read back once, by the fuse kernel
+        const int c = lane & 15;
+#pragma unroll 4
+        for (int q = 0; q < 16; ++q) {
+            const int r = q * 4 + (lane >> 4);
+            const int64_t tok = m0 + tq * 64 + r;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * 128 + (c ^ (r & 15)) * 8);
+            if (tok < M)
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(e16 + tok * kD + n0 + fh * 128 + c * 8));
+        }
     }
 }
 
@@ -241,7 +269,7 @@ proj_small_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __r
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) vals[i][r] = tile_s[i][lane][r];
-    emit_slice<kFwd>(vals, tok, M, fbase, kh, e32, e16, h, parts);
+    emit_slice<kFwd, false>(vals, tok, M, fbase, kh, e32, e16, h, parts);
 }
 
 template <bool kFwd>
