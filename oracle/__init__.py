@@ -6,8 +6,8 @@ import this package; the product path (`sparse_memory_gather_amd`) never
 does and shares no source with it.
 
 `forward()` strings the definition's steps together for one chunk of S
-sequences: n-gram IDs -> gather/dequant -> projection -> gate -> causal
-short conv with carried state -> residual add. Table rows come from a
+sequences: n-gram IDs -> gather/dequant -> projection (bf16 output) ->
+gate -> causal short conv with carried state -> residual add. Table rows come from a
 `row_source(ids) -> (codes uint8[n][2560], scales float32[n])` callable so
 that a 51.2 GB table never has to be materialised on the host.
 
@@ -18,6 +18,8 @@ Parity status of each step (see the pins under tests/):
   gather_dequant          pinned (raw bytes vs generator rows; rounding
                           properties against the exact rational sum)
   project                 pinned (numpy fp64 matmul; W = I)
+  round_bf16              pinned (exact rational round-half-even; ties,
+                          single rounding, subnormal step, overflow)
   gate                    pinned (closed forms e = +/-h, e = 0)
   conv_fuse               pinned (torch conv1d; impulse response; chunked
                           equals unchunked)
@@ -57,6 +59,7 @@ def _load():
             "oracle_bf16_rne": ([ctypes.c_float], ctypes.c_uint16),
             "oracle_gather_dequant": ([_P, _I64, _P, _P, _P, _P], None),
             "oracle_project": ([_P, _I64, _P, _P], None),
+            "oracle_round_bf16": ([_P, _I64, _P], None),
             "oracle_gate": ([_P, _P, _I64, ctypes.c_double, _P], None),
             "oracle_conv_fuse": ([_P, _P, _P, _I64, _P, _I32, _P, _P, _P, _P, _P], None),
         }
@@ -149,6 +152,15 @@ def project(x_bf16, W_bf16) -> np.ndarray:
     return e
 
 
+def round_bf16(a) -> np.ndarray:
+    """Nearest bf16 value of each fp64 element (ties to even, one rounding),
+    returned as fp64."""
+    a = _c(a, np.float64)
+    out = np.empty_like(a)
+    _load().oracle_round_bf16(_ptr(a), a.size, _ptr(out))
+    return out
+
+
 def gate(h_bf16, e, eps: float = 1e-6) -> np.ndarray:
     h = _c(h_bf16, np.uint16).reshape(-1, D)
     e = _c(e, np.float64).reshape(-1, D)
@@ -178,9 +190,11 @@ def conv_fuse(h_bf16, e, g, cu_seqlens, conv_w_bf16, state):
 
 def forward(tokens, cu_seqlens, h_bf16, W_bf16, conv_w_bf16, R: int, row_source,
             hist_ids=None, hist_len=None, conv_state=None, eps: float = 1e-6):
-    """One chunk through the whole path. Returns a dict with row_ids, x, e,
-    g, y, out (fp64, unrounded), and the new hist_ids / hist_len / conv_state
-    (conv_state kept in fp64 so chained chunks equal one long chunk)."""
+    """One chunk through the whole path. Returns a dict with row_ids, x, e
+    (the exact projection, fp64), e_b (its bf16 rounding: the projection's
+    output tensor, which the gate and the conv consume), g, y, out (fp64,
+    unrounded), and the new hist_ids / hist_len / conv_state (conv_state kept
+    in fp64 so chained chunks equal one long chunk)."""
     tokens = _c(tokens, np.int32)
     cu = _c(cu_seqlens, np.int32)
     S = len(cu) - 1
@@ -198,8 +212,9 @@ def forward(tokens, cu_seqlens, h_bf16, W_bf16, conv_w_bf16, R: int, row_source,
     compact[row_ids >= 0] = inv.astype(np.int32)
     x = gather_dequant(compact, codes, scales)
     e = project(x, W_bf16)
-    g = gate(h_bf16, e, eps)
-    y, out, st = conv_fuse(h_bf16, e, g, cu, conv_w_bf16, conv_state)
+    e_b = round_bf16(e)
+    g = gate(h_bf16, e_b, eps)
+    y, out, st = conv_fuse(h_bf16, e_b, g, cu, conv_w_bf16, conv_state)
     hid, hln = hist_update(tokens, cu, hist_ids, hist_len)
-    return dict(row_ids=row_ids, x=x, e=e, g=g, y=y, out=out,
+    return dict(row_ids=row_ids, x=x, e=e, e_b=e_b, g=g, y=y, out=out,
                 hist_ids=hid, hist_len=hln, conv_state=st)

@@ -22,9 +22,11 @@
  *    history at a sequence start) has row -1 and contributes zero.
  *  - x = bf16_rne( fl32( fl32(dec(code_bi)*s_bi) + fl32(dec(code_tri)*s_tri) ) ),
  *    E4M3FN decode, one fp32 scale per row.
- *  - e = x W^T (W[out][in]), fp64 here.
- *  - g = sigmoid( <h/rms(h), e/rms(e)> / sqrt(2560) ), rms(z) = sqrt(mean(z^2)+eps).
- *  - v = g e; y[t][c] = sum_{k=0..3} w[c][k] v[t-3+k][c] (causal depthwise,
+ *  - e = x W^T (W[out][in]), fp64 here; the projection is a bf16 layer, so
+ *    its output is the bf16 tensor e_b = bf16_rne(e) (one rounding from the
+ *    exact value), and the gate and the conv below act on e_b.
+ *  - g = sigmoid( <h/rms(h), e_b/rms(e_b)> / sqrt(2560) ), rms(z) = sqrt(mean(z^2)+eps).
+ *  - v = g e_b; y[t][c] = sum_{k=0..3} w[c][k] v[t-3+k][c] (causal depthwise,
  *    w[c][3] on the current token; v before a sequence start comes from the
  *    carried state, oldest first); out = h + y.
  * Floating point beyond the dequant step is fp64 throughout.
@@ -198,6 +200,31 @@ void oracle_project(const uint16_t* x, int64_t T, const uint16_t* W, double* e) 
             for (int c = 0; c < D; ++c) acc += xr[c] * oracle_bf16_value(w[c]);
             e[t * D + o] = acc;
         }
+    }
+}
+
+/* out[i] = the bf16 value nearest to in[i], ties to the even significand,
+ * rounded once from the fp64 value: bf16 keeps 8 significant bits and
+ * fp32's exponent range (subnormal step 2^-133); magnitudes at or beyond
+ * the midpoint above the largest finite bf16 become infinite. */
+void oracle_round_bf16(const double* in, int64_t n, double* out) {
+    const double max_finite = ldexp(255.0, 120);   /* (2 - 2^-7) * 2^127 */
+    const double overflow = ldexp(511.0, 119);     /* max_finite + half its step */
+    for (int64_t i = 0; i < n; ++i) {
+        double v = in[i];
+        if (v == 0.0 || isnan(v) || isinf(v)) {
+            out[i] = v;
+            continue;
+        }
+        int ex;
+        frexp(v, &ex);                              /* |v| = m 2^ex, 0.5 <= m < 1 */
+        int q = ex - 8;                             /* step of an 8-bit significand */
+        if (q < -133) q = -133;
+        double r = nearbyint(ldexp(v, -q));        /* default mode: nearest, ties even */
+        r = ldexp(r, q);
+        if (fabs(v) >= overflow) r = copysign(INFINITY, v);
+        else if (fabs(r) > max_finite) r = copysign(max_finite, v);
+        out[i] = (r == 0.0) ? copysign(0.0, v) : r;
     }
 }
 

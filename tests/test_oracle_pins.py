@@ -273,6 +273,67 @@ def test_project_uses_w_rows_as_outputs():
     assert e[0, 11] == 3.0 and np.count_nonzero(e) == 1
 
 
+def _rne_bf16_exact(v: float) -> float:
+    """Round-half-even of a double to 8 significant bits with bf16's range,
+    in exact rational arithmetic (independent of the oracle's frexp/nearbyint)."""
+    if v == 0.0 or math.isinf(v) or math.isnan(v):
+        return v
+    a = abs(Fraction(v))
+    ex = a.numerator.bit_length() - a.denominator.bit_length()   # 2^ex <= a < 2^(ex+1), up to one
+    if Fraction(2) ** ex > a:
+        ex -= 1
+    step = Fraction(2) ** max(ex - 7, -133)
+    n, rem = divmod(a, step)
+    if rem > step / 2 or (rem == step / 2 and n % 2 == 1):
+        n += 1
+    r = n * step
+    if r > Fraction(255) * Fraction(2) ** 120:                    # beyond the largest finite bf16
+        return math.copysign(math.inf, v)
+    return math.copysign(float(r), v)
+
+
+def test_round_bf16_matches_exact_rational_rne():
+    rng = np.random.default_rng(31)
+    # random 53-bit significands over normal and subnormal bf16 exponents
+    m = 1.0 + rng.random(4000)
+    ex = rng.integers(-140, 128, 4000)
+    v = np.ldexp(m, ex) * np.where(rng.random(4000) < 0.5, -1.0, 1.0)
+    # exact ties and near-ties at a few scales
+    base = np.ldexp(1.0 + np.arange(1, 60) * 2.0 ** -7, rng.integers(-20, 20, 59))
+    ulp = base * 2.0 ** -8 / (1.0 + np.arange(1, 60) * 2.0 ** -7)
+    v = np.concatenate([v, base + ulp, base - ulp, base + ulp * (1 + 2 ** -30), base + ulp * (1 - 2 ** -30)])
+    got = oracle.round_bf16(v)
+    want = np.array([_rne_bf16_exact(float(a)) for a in v])
+    np.testing.assert_array_equal(got, want)
+
+
+def test_round_bf16_ties_single_rounding_and_range():
+    r = oracle.round_bf16(np.array([
+        1 + 2.0 ** -8,               # tie -> 1 (even)
+        1 + 3 * 2.0 ** -8,           # tie -> 1 + 2^-6 (even)
+        1 + 2.0 ** -8 + 2.0 ** -40,  # just above the tie: up; a pass through fp32 would give 1
+        -(1 + 2.0 ** -8 + 2.0 ** -40),
+        1.5 * 2.0 ** -133,           # subnormal tie -> 2^-132 (even)
+        2.0 ** -134,                 # tie between 0 and 2^-133 -> +0
+        -(2.0 ** -134),
+        3.4e38,                      # past the overflow midpoint -> inf
+        3.3961e38,                   # below it -> largest finite
+        -0.0]))
+    want = [1.0, 1 + 2.0 ** -6, 1 + 2.0 ** -7, -(1 + 2.0 ** -7), 2.0 ** -132, 0.0, -0.0,
+            math.inf, 255 * 2.0 ** 120, -0.0]
+    for a, b in zip(r, want):
+        assert a == b and math.copysign(1, a) == math.copysign(1, b)
+
+
+def test_round_bf16_matches_torch_on_fp32_inputs():
+    # torch rounds float32 -> bfloat16 directly (RNE); on float32 inputs the
+    # single rounding from fp64 must agree with it
+    rng = np.random.default_rng(32)
+    f = (rng.standard_normal(20000) * np.exp(rng.uniform(-30, 30, 20000))).astype(np.float32)
+    want = torch.from_numpy(f).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(oracle.round_bf16(f.astype(np.float64)), want)
+
+
 def test_gate_closed_forms():
     rng = np.random.default_rng(10)
     h = inputs.normal_bf16(rng, (4, D))
@@ -400,6 +461,33 @@ def test_fresh_sequence_token0_is_identity_and_token1_uses_bigram_only(weights):
     codes, scales = _rows([r["row_ids"][1][0]])
     x1 = oracle.gather_dequant(np.array([[0, -1]], np.int32), codes, scales)
     assert np.array_equal(x1[0], r["x"][1])
+
+
+def test_forward_gate_and_conv_consume_the_bf16_projection(weights):
+    # the gate and the conv act on e_b = bf16(e); recompute both in torch
+    # (fp64) from forward()'s own exact e and check the rounding matters
+    W, cw = weights
+    n = 7
+    toks, h = _small_stream(n, seed=33)
+    r = oracle.forward(toks, np.array([0, n], np.int32), h, W, cw, 65_536, _rows)
+    flat = r["e"].ravel()
+    e_b = np.array([_rne_bf16_exact(float(a)) for a in flat]).reshape(r["e"].shape)
+    np.testing.assert_array_equal(r["e_b"], e_b)
+    hf = torch.from_numpy(inputs.bf16_bits_to_f32(h).astype(np.float64))
+    w = inputs.bf16_bits_to_f32(cw).astype(np.float64)
+
+    def gate_and_y(e):
+        et = torch.from_numpy(e)
+        hn = hf / torch.sqrt((hf * hf).mean(dim=1, keepdim=True) + 1e-6)
+        en = et / torch.sqrt((et * et).mean(dim=1, keepdim=True) + 1e-6)
+        g = torch.sigmoid((hn * en).sum(dim=1) / math.sqrt(D)).numpy()
+        return g, _conv_torch(g[:, None] * e, w, np.zeros((3, D)))
+
+    g_ref, y_ref = gate_and_y(e_b)
+    np.testing.assert_allclose(r["g"], g_ref, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(r["y"], y_ref, rtol=1e-12, atol=1e-13)
+    g_raw, y_raw = gate_and_y(r["e"])
+    assert np.max(np.abs(y_raw - r["y"])) > 1e-5      # a dropped rounding would fail the check above
 
 
 def _run_chunks(toks, h, cuts, W, cw, R):
