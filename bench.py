@@ -36,12 +36,12 @@ D = 2560
 #  gather: per valid lookup 2560 B of codes + 4 B scale; per token 8 B of row
 #          ids read and 5120 B of bf16 x written
 #  proj:   2 * 2560 * 2560 flop per token
-#  fuse:   per token h 5120 B + e 5120 B + out 5120 B + 320 B gate partials
+#  fuse:   per token h 5120 B + e 5120 B read, out 5120 B written
 #  hash:   per token 4 B token read (+ history), 8 B ids written
 GATHER_BYTES_PER_LOOKUP = 2560 + 4
 GATHER_BYTES_PER_TOKEN = 8 + 2 * D
 PROJ_FLOP_PER_TOKEN = 2 * D * D
-FUSE_BYTES_PER_TOKEN = 3 * 2 * D + 20 * 16
+FUSE_BYTES_PER_TOKEN = 3 * 2 * D
 
 
 KERNEL_SOURCES = {

@@ -24,7 +24,8 @@
  *    (history + chunk) has too few tokens; a missing row contributes zero.
  *  - x = bf16_rne(fl32(fl32(dec(code_r2)*scale[r2]) + fl32(dec(code_r3)*scale[r3])))
  *    with dec = OCP FP8 E4M3FN decode and one fp32 scale per row.
- *  - e = x W^T, W bf16 [2560 out][2560 in], fp32 accumulation.
+ *  - e = bf16_rne(x W^T), W bf16 [2560 out][2560 in], fp32 accumulation: the
+ *    projection is a bf16 layer, and the gate and the conv read its bf16 output.
  *  - g = sigmoid(<h/rms(h), e/rms(e)> / sqrt(2560)), rms(z) = sqrt(mean(z^2) + eps).
  *  - v = g e; y[t][c] = sum_{k=0..3} conv_w[c][k] v[t-3+k][c] (causal,
  *    depthwise, conv_w[c][3] on the current token, v before a sequence's
@@ -138,7 +139,7 @@ typedef struct ple_forward_args {
     /* optional debug outputs, NULL to skip */
     int32_t* row_ids_out;       /* int32 [T][2], 8-byte aligned */
     uint16_t* x_out;            /* bf16 [T][2560] */
-    float* e_out;               /* float [T][2560], projection before rounding */
+    float* e_out;               /* float [T][2560], projection accumulators before the bf16 rounding */
     float* gate_out;            /* float [T] */
     float* y_out;               /* float [T][2560], conv output before the residual add */
 } ple_forward_args;

@@ -68,7 +68,7 @@ int check_alias(const Range* r, int n) {
 }
 
 struct WsLayout {
-    size_t row_ids, x, e16, parts, snap, total;
+    size_t row_ids, x, e16, snap, total;
 };
 
 size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -79,7 +79,6 @@ WsLayout layout(int64_t T, int32_t S) {
     w.row_ids = off; off = up256(off + (size_t)T * 2 * sizeof(int32_t));
     w.x = off;       off = up256(off + (size_t)T * kD * 2);
     w.e16 = off;     off = up256(off + (size_t)T * kD * 2);
-    w.parts = off;   off = up256(off + (size_t)T * kParts * kPartStride * sizeof(float));
     w.snap = off;    off = up256(off + (size_t)S * 3 * kD * sizeof(float));
     w.total = off;
     return w;
@@ -173,7 +172,7 @@ int ple_proj(const uint16_t* x_bf16, int64_t T, const uint16_t* W_bf16, float* e
     Range r[] = {rng("x", x_bf16, (size_t)T * kD * 2, false), rng("W", W_bf16, (size_t)kD * kD * 2, false),
                  rng("e", e, (size_t)T * kD * 4, true)};
     if (int st = check_alias(r, 3)) return st;
-    hipError_t err = launch_proj(x_bf16, T, W_bf16, e, nullptr, nullptr, nullptr,
+    hipError_t err = launch_proj(x_bf16, T, W_bf16, e, nullptr,
                                  reinterpret_cast<hipStream_t>(stream));
     if (int st = hip_status(err, "ple_proj launch")) return st;
     return ok();
@@ -232,7 +231,6 @@ static int forward_impl(const ple_forward_args* a, void* stream, void* const* ev
     int32_t* row_ids = a->row_ids_out ? a->row_ids_out : reinterpret_cast<int32_t*>(ws + L.row_ids);
     uint16_t* x = a->x_out ? a->x_out : reinterpret_cast<uint16_t*>(ws + L.x);
     uint16_t* e16 = reinterpret_cast<uint16_t*>(ws + L.e16);
-    float* parts = reinterpret_cast<float*>(ws + L.parts);
     float* snap = reinterpret_cast<float*>(ws + L.snap);
 
     auto mark = [&](int i) -> hipError_t {
@@ -247,10 +245,10 @@ static int forward_impl(const ple_forward_args* a, void* stream, void* const* ev
     e = launch_gather(row_ids, T, a->table, a->scales, a->R, x, nullptr, a->dev_err, s);
     if (int st = hip_status(e, "ple_forward: gather launch")) return st;
     if (int st = hip_status(mark(2), "ple_forward: event record")) return st;
-    e = launch_proj(x, T, a->W, a->e_out, e16, a->h, parts, s);
+    e = launch_proj(x, T, a->W, a->e_out, e16, s);
     if (int st = hip_status(e, "ple_forward: projection launch")) return st;
     if (int st = hip_status(mark(3), "ple_forward: event record")) return st;
-    e = launch_fuse(a->h, e16, parts, T, a->cu_seqlens, S, a->tokens, a->conv_w, snap, a->conv_state,
+    e = launch_fuse(a->h, e16, T, a->cu_seqlens, S, a->tokens, a->conv_w, snap, a->conv_state,
                     a->hist_ids, a->hist_len, a->out, a->eps, a->gate_out, a->y_out, s);
     if (int st = hip_status(e, "ple_forward: fuse launch")) return st;
     if (int st = hip_status(mark(4), "ple_forward: event record")) return st;

@@ -3,23 +3,26 @@
 // After the projection the looked-up vector is gated, short-convolved and
 // fused into the hidden states (mengman.github.io "Qwen3.8-Flash-Next 端侧部署
 // 01", n-gram embedding section); the short conv is its own op in the vLLM
-// port (kipfel.ltd Thor article, section 5, qwen4_exp_ple_short_conv). Here:
+// port (kipfel.ltd Thor article, section 5, qwen4_exp_ple_short_conv). Here,
+// with e the projection's bf16 output:
 //   g = sigmoid(<h/rms(h), e/rms(e)> / sqrt(2560)), rms(z) = sqrt(mean(z^2)+eps),
 //   v = g e,  y[t][c] = sum_k w[c][k] v[t-3+k][c],  out = bf16(h + y),
 // with v before a sequence's first token taken from the carried state.
 //
 // One block of 640 threads owns 16 consecutive tokens; thread i owns
-// features 4i .. 4i+3. The gates of the block's tokens and of the three
-// before them are finished once per block from the projection's per-slice
-// partial sums: 380 partial vectors are loaded in parallel into LDS, then
-// summed in a fixed order. A block whose 19-token window lies inside one
-// sequence that goes on past the block (every block of a long prefill but
-// the first and the last) issues all its e and h loads up front and
-// convolves from registers. Other blocks walk their tokens with a
-// three-token window that restarts from the carried state at a sequence
-// start; the block holding a sequence's last token writes the new conv state
-// and n-gram history. The old state is read from a copy taken before this
-// kernel, so the in-place update cannot race with readers.
+// features 4i .. 4i+3 and loads, up front, e of the block's tokens and the
+// three before them and h of its own tokens (packed bf16, 8 bytes a row).
+// The gates of those 19 tokens are formed by whole waves: wave w takes
+// tokens w and w + 10 of the window, reads the two 5 KB rows with 16-byte
+// loads (L2 hits: the block's own loads of the same rows are in flight),
+// sums e^2, h.e and h^2 over its 40 features per lane and reduces across the
+// wave with DPP, always in the same order, so a token's gate does not depend
+// on which block or chunk computes it. Each output then takes its four taps
+// from registers, or from the carried state where a tap lies before its
+// sequence's first token (a wave-uniform test). The block holding a
+// sequence's last token writes the new conv state and n-gram history; the
+// old state is read from a copy taken before this kernel, so the in-place
+// update cannot race with readers.
 #include "ple_kernels.h"
 
 namespace ple {
@@ -28,20 +31,38 @@ namespace {
 constexpr int BT = 16;                 // tokens per block
 constexpr int FPT = 4;                 // features per thread
 constexpr int kThreads = kD / FPT;     // 640
-constexpr int kWin = BT + 3;           // tokens whose gate the block needs
+constexpr int kWaves = kThreads / 64;  // 10
+constexpr int kWin = BT + 3;           // tokens whose v the block needs
+constexpr int kXcds = 8;               // accelerator complex dies on MI355X
 
-__device__ __forceinline__ void load4_bf16(const uint16_t* p, float v[4]) {
-    u32x2 q = *reinterpret_cast<const u32x2*>(p);
+__device__ __forceinline__ void unpack4(const u32x2& q, float v[4]) {
     v[0] = bf16_to_f32(q[0] & 0xFFFFu);
     v[1] = bf16_to_f32(q[0] >> 16);
     v[2] = bf16_to_f32(q[1] & 0xFFFFu);
     v[3] = bf16_to_f32(q[1] >> 16);
 }
 
-// y = sum_k w_k v_k in one fixed FMA order, shared by both paths so that a
-// token's result does not depend on which path (or chunking) produced it
+// y = sum_k w_k v_k in one fixed FMA order
 __device__ __forceinline__ float conv4(const float w[kTaps], float v0, float v1, float v2, float v3) {
     return fmaf(w[3], v3, fmaf(w[2], v2, fmaf(w[1], v1, w[0] * v0)));
+}
+
+// v moved across lanes by a DPP pattern; lanes of rows outside kRowMask get 0
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl,
+                                                                 kRowMask, 0xF, false));
+}
+
+// sum over the 64 lanes of a wave, complete in lane 63
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp<0xB1>(v);        // quad_perm [1,0,3,2]: pairs
+    v += dpp<0x4E>(v);        // quad_perm [2,3,0,1]: quads
+    v += dpp<0x141>(v);       // row_half_mirror: eights
+    v += dpp<0x140>(v);       // row_mirror: rows of 16
+    v += dpp<0x142, 0xA>(v);  // row_bcast15: rows 1, 3 add rows 0, 2
+    v += dpp<0x143, 0xC>(v);  // row_bcast31: rows 2, 3 add rows 0 + 1
+    return v;
 }
 
 __device__ __forceinline__ int seq_of(const int32_t* cu, int32_t S, int64_t t) {
@@ -54,41 +75,76 @@ __device__ __forceinline__ int seq_of(const int32_t* cu, int32_t S, int64_t t) {
 }
 
 __global__ void __launch_bounds__(kThreads)
-fuse_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ e16,
-            const float* __restrict__ parts, int64_t T, const int32_t* __restrict__ cu, int32_t S,
-            const int32_t* __restrict__ tokens, const uint16_t* __restrict__ conv_w,
-            const float* __restrict__ snap, float* __restrict__ conv_state,
-            int32_t* __restrict__ hist_ids, int32_t* __restrict__ hist_len, uint16_t* out,
-            float eps, float* __restrict__ gate_out, float* __restrict__ y_out) {
-    __shared__ f32x4 part_s[kWin][kParts];
+fuse_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ e16, int64_t T,
+            const int32_t* __restrict__ cu, int32_t S, const int32_t* __restrict__ tokens,
+            const uint16_t* __restrict__ conv_w, const float* __restrict__ snap,
+            float* __restrict__ conv_state, int32_t* __restrict__ hist_ids,
+            int32_t* __restrict__ hist_len, uint16_t* out, float eps, float* __restrict__ gate_out,
+            float* __restrict__ y_out) {
+    __shared__ float sum_s[kWin][3];
     __shared__ float g_s[kWin];
     __shared__ int seg_s[kWin], start_s[kWin], end_s[kWin];
-    __shared__ int fast_s;
-    const int tid = threadIdx.x;
-    const int64_t t0 = (int64_t)blockIdx.x * BT;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // consecutive token blocks on one XCD, so that the three-token overlap of
+    // neighbouring blocks is served by that XCD's L2
+    const int nb = gridDim.x, b = blockIdx.x;
+    const int per = nb / kXcds, rem = nb % kXcds, xcd = b % kXcds;
+    const int64_t t0 = (int64_t)(xcd * per + (xcd < rem ? xcd : rem) + b / kXcds) * BT;
+    const int c0 = tid * FPT;
 
-    // gate partial sums of tokens t0-3 .. t0+BT-1, one 16-byte vector per thread
-    if (tid < kWin * kParts) {
-        const int i = tid / kParts, k = tid % kParts;
+    // this thread's e of the 19-token window and h of the block's tokens
+    const u32x2 zero = {0u, 0u};
+    u32x2 ep[kWin], hp[BT];
+#pragma unroll
+    for (int i = 0; i < kWin; ++i) {
         const int64_t t = t0 - 3 + i;
-        if (t >= 0 && t < T)
-            part_s[i][k] = *reinterpret_cast<const f32x4*>(parts + (t * kParts + k) * kPartStride);
+        ep[i] = (t >= 0 && t < T) ? *reinterpret_cast<const u32x2*>(e16 + t * kD + c0) : zero;
+    }
+#pragma unroll
+    for (int i = 0; i < BT; ++i) {
+        const int64_t t = t0 + i;
+        hp[i] = t < T ? *reinterpret_cast<const u32x2*>(h + t * kD + c0) : zero;
+    }
+
+    // gate sums: one wave per window token, lane l holds features 8l + 512 s + 0..7
+    for (int i = wave; i < kWin; i += kWaves) {
+        const int64_t t = t0 - 3 + i;
+        if (t < 0 || t >= T) continue;
+        const u32x4* hr = reinterpret_cast<const u32x4*>(h + t * kD) + lane;
+        const u32x4* er = reinterpret_cast<const u32x4*>(e16 + t * kD) + lane;
+        u32x4 hv[5], ev[5];
+#pragma unroll
+        for (int s = 0; s < 5; ++s) {
+            hv[s] = hr[s * 64];
+            ev[s] = er[s * 64];
+        }
+        float ee = 0.0f, he = 0.0f, hh = 0.0f;
+#pragma unroll
+        for (int s = 0; s < 5; ++s)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float h0 = bf16_to_f32(hv[s][q] & 0xFFFFu), h1 = bf16_to_f32(hv[s][q] >> 16);
+                const float e0 = bf16_to_f32(ev[s][q] & 0xFFFFu), e1 = bf16_to_f32(ev[s][q] >> 16);
+                ee = fmaf(e1, e1, fmaf(e0, e0, ee));
+                he = fmaf(h1, e1, fmaf(h0, e0, he));
+                hh = fmaf(h1, h1, fmaf(h0, h0, hh));
+            }
+        ee = wave_sum(ee);
+        he = wave_sum(he);
+        hh = wave_sum(hh);
+        if (lane == 63) {
+            sum_s[i][0] = ee;
+            sum_s[i][1] = he;
+            sum_s[i][2] = hh;
+        }
     }
     __syncthreads();
     if (tid < kWin) {
         const int64_t t = t0 - 3 + tid;
         if (t >= 0 && t < T) {
-            float ee = 0.0f, he = 0.0f, hh = 0.0f;
-#pragma unroll
-            for (int k = 0; k < kParts; ++k) {  // fixed order: deterministic
-                const f32x4 q = part_s[tid][k];
-                ee += q[0];
-                he += q[1];
-                hh += q[2];
-            }
-            const float rh = sqrtf(hh * (1.0f / kD) + eps);
-            const float re = sqrtf(ee * (1.0f / kD) + eps);
-            const float z = he / (rh * re) * (1.0f / 50.596443f);  // 1/sqrt(2560)
+            const float rh = sqrtf(sum_s[tid][2] * (1.0f / kD) + eps);
+            const float re = sqrtf(sum_s[tid][0] * (1.0f / kD) + eps);
+            const float z = sum_s[tid][1] / (rh * re) * (1.0f / 50.596443f);  // 1/sqrt(2560)
             const float g = 1.0f / (1.0f + expf(-z));
             g_s[tid] = g;
             if (gate_out && tid >= 3) gate_out[t] = g;
@@ -101,20 +157,13 @@ fuse_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ e16,
             end_s[tid] = (int)en;
         } else {
             g_s[tid] = 0.0f;
-            seg_s[tid] = -1;
+            seg_s[tid] = 0;
             start_s[tid] = 0;
             end_s[tid] = 0;
         }
     }
     __syncthreads();
-    if (tid == 0) {
-        // fast: the 19-token window lies in one sequence that goes on past the block
-        const int64_t tl = t0 + BT - 1;
-        fast_s = (t0 >= 3 && tl < T && start_s[kWin - 1] <= t0 - 3 && end_s[kWin - 1] > tl + 1) ? 1 : 0;
-    }
-    __syncthreads();
 
-    const int c0 = tid * FPT;
     float w[FPT][kTaps];
     {
         const u32x4* wp = reinterpret_cast<const u32x4*>(conv_w + c0 * kTaps);
@@ -130,79 +179,42 @@ fuse_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ e16,
         }
     }
 
-    if (fast_s) {
-        float e[kWin][FPT], hv[BT][FPT];
 #pragma unroll
-        for (int i = 0; i < kWin; ++i) load4_bf16(e16 + (t0 - 3 + i) * kD + c0, e[i]);
-#pragma unroll
-        for (int i = 0; i < BT; ++i) load4_bf16(h + (t0 + i) * kD + c0, hv[i]);
-#pragma unroll
-        for (int i = 0; i < kWin; ++i) {
-            const float g = g_s[i];
-#pragma unroll
-            for (int q = 0; q < FPT; ++q) e[i][q] *= g;  // e[i] now holds v
-        }
-#pragma unroll
-        for (int i = 0; i < BT; ++i) {
-            const int64_t t = t0 + i;
-            float y[FPT];
-#pragma unroll
-            for (int q = 0; q < FPT; ++q) y[q] = conv4(w[q], e[i][q], e[i + 1][q], e[i + 2][q], e[i + 3][q]);
-            u32x2 o = {pack_bf16x2(hv[i][0] + y[0], hv[i][1] + y[1]),
-                       pack_bf16x2(hv[i][2] + y[2], hv[i][3] + y[3])};
-            __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(out + t * kD + c0));
-            if (y_out) *reinterpret_cast<f32x4*>(y_out + t * kD + c0) = f32x4{y[0], y[1], y[2], y[3]};
-        }
-        return;
-    }
-
-    // general path: sequence starts and ends inside the block, the first block, the tail
-    auto v_at = [&](int64_t p, int s, int64_t st, float v[FPT]) {
-        if (p >= st) {
-            float e[FPT];
-            load4_bf16(e16 + p * kD + c0, e);
-            const float g = g_s[p - t0 + 3];
-#pragma unroll
-            for (int q = 0; q < FPT; ++q) v[q] = g * e[q];
-        } else {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(
-                snap + ((int64_t)s * 3 + 3 - (st - p)) * kD + c0);
-#pragma unroll
-            for (int q = 0; q < FPT; ++q) v[q] = a[q];
-        }
-    };
-    float win[3][FPT];
     for (int i = 0; i < BT; ++i) {
         const int64_t t = t0 + i;
         if (t >= T) break;
         const int s = seg_s[i + 3];
         const int64_t st = start_s[i + 3], en = end_s[i + 3];
-        if (i == 0 || t == st) {
-            v_at(t - 3, s, st, win[0]);
-            v_at(t - 2, s, st, win[1]);
-            v_at(t - 1, s, st, win[2]);
-        }
-        float vt[FPT], hv[FPT];
-        v_at(t, s, st, vt);
-        load4_bf16(h + t * kD + c0, hv);
-        float y[FPT];
+        // v at positions t-3 .. t (window slots i .. i+3)
+        float v[kTaps][FPT];
 #pragma unroll
-        for (int q = 0; q < FPT; ++q) y[q] = conv4(w[q], win[0][q], win[1][q], win[2][q], vt[q]);
-        u32x2 o = {pack_bf16x2(hv[0] + y[0], hv[1] + y[1]), pack_bf16x2(hv[2] + y[2], hv[3] + y[3])};
+        for (int k = 0; k < kTaps; ++k) {
+            const int64_t p = t - 3 + k;
+            if (p >= st) {
+                float e[FPT];
+                unpack4(ep[i + k], e);
+                const float g = g_s[i + k];
+#pragma unroll
+                for (int q = 0; q < FPT; ++q) v[k][q] = g * e[q];
+            } else {
+                const f32x4 a = *reinterpret_cast<const f32x4*>(snap + ((int64_t)s * 3 + 3 - (st - p)) * kD + c0);
+#pragma unroll
+                for (int q = 0; q < FPT; ++q) v[k][q] = a[q];
+            }
+        }
+        float hv[FPT], y[FPT];
+        unpack4(hp[i], hv);
+#pragma unroll
+        for (int q = 0; q < FPT; ++q) y[q] = conv4(w[q], v[0][q], v[1][q], v[2][q], v[3][q]);
+        const u32x2 o = {pack_bf16x2(hv[0] + y[0], hv[1] + y[1]), pack_bf16x2(hv[2] + y[2], hv[3] + y[3])};
         __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(out + t * kD + c0));
         if (y_out) *reinterpret_cast<f32x4*>(y_out + t * kD + c0) = f32x4{y[0], y[1], y[2], y[3]};
-#pragma unroll
-        for (int q = 0; q < FPT; ++q) {
-            win[0][q] = win[1][q];
-            win[1][q] = win[2][q];
-            win[2][q] = vt[q];
-        }
         if (t == en - 1) {
-            // last token of sequence s: new conv state = last three v, oldest first
+            // last token of sequence s: new conv state = v at t-2, t-1, t
 #pragma unroll
             for (int r = 0; r < 3; ++r)
                 *reinterpret_cast<f32x4*>(conv_state + ((int64_t)s * 3 + r) * kD + c0) =
-                    f32x4{win[r][0], win[r][1], win[r][2], win[r][3]};
+                    f32x4{v[r + 1][0], v[r + 1][1], v[r + 1][2], v[r + 1][3]};
             if (tid == 0) {
                 int hl = hist_len[s];
                 if (hl < 0 || hl > 2) hl = 0;
@@ -226,15 +238,15 @@ fuse_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ e16,
 
 }  // namespace
 
-hipError_t launch_fuse(const uint16_t* h, const uint16_t* e16, const float* parts, int64_t T,
-                       const int32_t* cu, int32_t S, const int32_t* tokens,
-                       const uint16_t* conv_w, const float* state_snap, float* conv_state,
-                       int32_t* hist_ids, int32_t* hist_len, uint16_t* out, float eps,
-                       float* gate_out, float* y_out, hipStream_t stream) {
+hipError_t launch_fuse(const uint16_t* h, const uint16_t* e16, int64_t T, const int32_t* cu,
+                       int32_t S, const int32_t* tokens, const uint16_t* conv_w,
+                       const float* state_snap, float* conv_state, int32_t* hist_ids,
+                       int32_t* hist_len, uint16_t* out, float eps, float* gate_out, float* y_out,
+                       hipStream_t stream) {
     const int64_t blocks = (T + BT - 1) / BT;
-    hipLaunchKernelGGL(fuse_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, h, e16, parts,
-                       T, cu, S, tokens, conv_w, state_snap, conv_state, hist_ids, hist_len, out,
-                       eps, gate_out, y_out);
+    hipLaunchKernelGGL(fuse_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, h, e16, T, cu,
+                       S, tokens, conv_w, state_snap, conv_state, hist_ids, hist_len, out, eps,
+                       gate_out, y_out);
     return hipGetLastError();
 }
 

@@ -9,9 +9,6 @@ namespace ple {
 
 constexpr int kD = 2560;          // row width = hidden size
 constexpr int kTaps = 4;          // short-conv taps
-constexpr int kPartCols = 128;    // features per gate partial sum
-constexpr int kParts = kD / kPartCols;  // 20 partial sums per token
-constexpr int kPartStride = 4;    // floats per (token, part): sum e^2, sum h*e, sum h^2, pad
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -45,16 +42,17 @@ hipError_t launch_gather(const int32_t* row_ids, int64_t T, const uint8_t* table
                          const float* scales, int64_t R, uint16_t* x, uint8_t* raw,
                          int32_t* dev_err, hipStream_t stream);
 
-// e = x W^T. Forward mode (h != nullptr): writes e as bf16 into e16, the gate
-// partial sums into parts [T][kParts][kPartStride], and e as fp32 into e32 if
-// e32 != nullptr. Projection-only mode (h == nullptr): writes fp32 e32.
+// e = x W^T. Forward mode (e16 != nullptr): writes e as bf16 into e16, and
+// as fp32 into e32 if e32 != nullptr. Projection-only mode: fp32 into e32.
 hipError_t launch_proj(const uint16_t* x, int64_t T, const uint16_t* W, float* e32,
-                       uint16_t* e16, const uint16_t* h, float* parts, hipStream_t stream);
+                       uint16_t* e16, hipStream_t stream);
 
-hipError_t launch_fuse(const uint16_t* h, const uint16_t* e16, const float* parts, int64_t T,
-                       const int32_t* cu, int32_t S, const int32_t* tokens,
-                       const uint16_t* conv_w, const float* state_snap, float* conv_state,
-                       int32_t* hist_ids, int32_t* hist_len, uint16_t* out, float eps,
-                       float* gate_out, float* y_out, hipStream_t stream);
+// Gate (from h and the bf16 e), causal short conv with carried state,
+// residual add; updates conv_state and the n-gram history in place.
+hipError_t launch_fuse(const uint16_t* h, const uint16_t* e16, int64_t T, const int32_t* cu,
+                       int32_t S, const int32_t* tokens, const uint16_t* conv_w,
+                       const float* state_snap, float* conv_state, int32_t* hist_ids,
+                       int32_t* hist_len, uint16_t* out, float eps, float* gate_out, float* y_out,
+                       hipStream_t stream);
 
 }  // namespace ple

@@ -18,8 +18,15 @@
 // across 256 bytes, and 16 consecutive 128-byte rows then hit 16 distinct
 // 16-byte bank groups.
 //
-// Forward mode also reduces, per token and per 128-feature slice, the sums
-// e^2, h.e and h^2 that the gate needs (fp32, before e is rounded to bf16).
+// The k loop is software-pipelined: the fragment reads of k-step ks+1 are
+// interleaved with the MFMAs of ks (pinned with sched_group_barrier), and
+// the wait for the next stage, the barrier and the DMA into the stage just
+// read sit inside the last k-step of each stage, so the first fragments of
+// the next stage load while its MFMAs drain.
+//
+// Forward mode writes e as bf16 (the projection's output tensor), staged
+// through LDS into 256-byte token rows; the fp32 accumulators can also be
+// written for checking.
 #include <atomic>
 
 #include "ple_kernels.h"
@@ -51,20 +58,16 @@ __device__ __forceinline__ int swz(int row) { return (row >> 1) & (CH - 1); }
 
 // Output of one lane for one 32-token tile of a 128-feature slice: vals[i] are
 // the lane's 16 accumulators of feature tile i (features fbase + 32 i + 8 g +
-// 4 kh + 0..3, g = r / 4) for token `tok`. Writes e (fp32 and/or bf16) and, in
-// forward mode, the slice's gate sums e^2, h.e, h^2 in one fixed order.
-//
-// With kStage, the bf16 e values go to the wave's LDS staging tile instead of
-// global memory: row `srow` (the token within the wave's 64), 16-byte chunk
+// 4 kh + 0..3, g = r / 4) for token `tok`. Writes e as fp32 (if e32) and, in
+// forward mode, as bf16: to global memory, or with kStage to the wave's LDS
+// staging tile, row `srow` (the token within the wave's 64), 16-byte chunk
 // (feature offset / 8) XOR (srow & 15), so that the 32 rows a store
 // instruction touches spread over all 64 banks.
 template <bool kFwd, bool kStage>
 __device__ __forceinline__ void emit_slice(const float (&vals)[4][16], int64_t tok, int64_t M, int fbase,
                                            int kh, float* __restrict__ e32, uint16_t* __restrict__ e16,
-                                           const uint16_t* __restrict__ h, float* __restrict__ parts,
                                            uint16_t* stage = nullptr, int srow = 0) {
-    const bool live = tok < M;
-    float ee = 0.0f, he = 0.0f, hh = 0.0f;
+    if (tok >= M) return;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -72,20 +75,10 @@ __device__ __forceinline__ void emit_slice(const float (&vals)[4][16], int64_t t
             const int f = fbase + i * 32 + g * 8 + kh * 4;
             const float v0 = vals[i][4 * g + 0], v1 = vals[i][4 * g + 1];
             const float v2 = vals[i][4 * g + 2], v3 = vals[i][4 * g + 3];
-            if (!live) continue;
             const int64_t off = tok * kD + f;
-            if (!kFwd || e32) {
-                f32x4 o = {v0, v1, v2, v3};
-                *reinterpret_cast<f32x4*>(e32 + off) = o;
-            }
+            if (!kFwd || e32) *reinterpret_cast<f32x4*>(e32 + off) = f32x4{v0, v1, v2, v3};
             if (kFwd) {
-                u32x2 hb = *reinterpret_cast<const u32x2*>(h + off);
-                const float h0 = bf16_to_f32(hb[0] & 0xFFFFu), h1 = bf16_to_f32(hb[0] >> 16);
-                const float h2 = bf16_to_f32(hb[1] & 0xFFFFu), h3 = bf16_to_f32(hb[1] >> 16);
-                ee = ee + fmaf(v3, v3, fmaf(v2, v2, fmaf(v1, v1, v0 * v0)));
-                he = he + fmaf(h3, v3, fmaf(h2, v2, fmaf(h1, v1, h0 * v0)));
-                hh = hh + fmaf(h3, h3, fmaf(h2, h2, fmaf(h1, h1, h0 * h0)));
-                u32x2 ob = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+                const u32x2 ob = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
                 if (kStage)
                     *reinterpret_cast<u32x2*>(stage + srow * 128 + ((4 * i + g) ^ (srow & 15)) * 8 + kh * 4) = ob;
                 else
@@ -93,23 +86,12 @@ __device__ __forceinline__ void emit_slice(const float (&vals)[4][16], int64_t t
             }
         }
     }
-    if (kFwd) {
-        ee += __shfl_xor(ee, 32);
-        he += __shfl_xor(he, 32);
-        hh += __shfl_xor(hh, 32);
-        if (live && kh == 0) {
-            const int part = fbase / kPartCols;
-            f32x4 p = {ee, he, hh, 0.0f};
-            *reinterpret_cast<f32x4*>(parts + (tok * kParts + part) * kPartStride) = p;
-        }
-    }
 }
 
 template <bool kFwd>
 __global__ void __launch_bounds__(kThreads, 1)
 proj_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __restrict__ W,
-            float* __restrict__ e32, uint16_t* __restrict__ e16, const uint16_t* __restrict__ h,
-            float* __restrict__ parts) {
+            float* __restrict__ e32, uint16_t* __restrict__ e16) {
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -149,6 +131,18 @@ proj_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __restric
         }
     };
 
+    // fragments of one k-step: 4 W tiles (A operand) and 2 token tiles (B)
+    const int fr = lane & 31, kh = lane >> 5, sw = swz(fr);
+    const int offA = (fh * 128 + fr) * BK, offB = BN * BK + (tq * 64 + fr) * BK;
+    bf16x8 fa[2][4], fb[2][2];
+    auto read = [&](int kt, int ks, int buf) {
+        const uint16_t* base = lds + (kt & 1) * STAGE;
+        const int c = ((ks * 2 + kh) ^ sw) * 8;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[buf][i] = *reinterpret_cast<const bf16x8*>(base + offA + i * 32 * BK + c);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) fb[buf][j] = *reinterpret_cast<const bf16x8*>(base + offB + j * 32 * BK + c);
+    };
     f32x16 acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -156,34 +150,45 @@ proj_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __restric
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    // MFMAs lo .. hi-1 of one k-step (q = 2 i + j), each tile's k order unchanged
+    auto mfma = [&](int buf, int lo, int hi) {
+#pragma unroll
+        for (int q = lo; q < hi; ++q)
+            acc[q >> 1][q & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][q >> 1], fb[buf][q & 1],
+                                                                         acc[q >> 1][q & 1], 0, 0, 0);
+    };
 
     issue(0);
-    const int fr = lane & 31, kh = lane >> 5, sw = swz(fr);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt, lgkmcnt untouched
+    __builtin_amdgcn_s_barrier();
+    issue(1);
+    read(0, 0, 0);
     for (int kt = 0; kt < KT; ++kt) {
-        // stage kt has landed for this wave (vmcnt counts the LDS-DMA loads);
-        // the barrier makes every wave's part visible and marks the other
-        // stage, read during kt-1, free for the next DMA
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt, lgkmcnt untouched
-        __builtin_amdgcn_s_barrier();
-        if (kt + 1 < KT) issue(kt + 1);
-        const uint16_t* cW = lds + (kt & 1) * STAGE;
-        const uint16_t* cX = cW + BN * BK;
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            const int c = ((ks * 2 + kh) ^ sw) * 8;
-            bf16x8 a[4], bb[2];
+        for (int ks = 0; ks < BK / 16 - 1; ++ks) {
+            read(kt, ks + 1, (ks + 1) & 1);
+            mfma(ks & 1, 0, 8);
+            // one fragment read between consecutive MFMAs
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                a[i] = *reinterpret_cast<const bf16x8*>(cW + (fh * 128 + i * 32 + fr) * BK + c);
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                bb[j] = *reinterpret_cast<const bf16x8*>(cX + (tq * 64 + j * 32 + fr) * BK + c);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
+            for (int q = 0; q < 6; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         }
+        // last k-step of stage kt (fragments in buffer 1): this wave's reads
+        // of the stage are complete; once every wave has passed the barrier
+        // the stage may be refilled, and stage kt+1 (DMA issued one stage
+        // ago) has landed for every wave
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        mfma(1, 0, 4);
+        if (kt + 1 < KT) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            __builtin_amdgcn_s_barrier();
+            if (kt + 2 < KT) issue(kt + 2);
+            read(kt + 1, 0, 0);
+        }
+        mfma(1, 4, 8);
     }
 
     // epilogue: lane holds token (.. + fr) and features (.. + 8 g + 4 kh + 0..3).
@@ -198,10 +203,8 @@ proj_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __restric
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) vals[i][r] = acc[i][j][r];
-        emit_slice<kFwd, kFwd>(vals, m0 + tq * 64 + j * 32 + fr, M, n0 + fh * 128, kh, e32, e16, h, parts,
-                               stage, j * 32 + fr);
-        // keep each token tile's loads and stores together (bounds register pressure)
-        __builtin_amdgcn_sched_barrier(0);
+        emit_slice<kFwd, kFwd>(vals, m0 + tq * 64 + j * 32 + fr, M, n0 + fh * 128, kh, e32, e16, stage,
+                               j * 32 + fr);
     }
     if (kFwd) {
         // the wave's own LDS writes are complete before its reads (in-order LDS
@@ -223,13 +226,12 @@ proj_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __restric
 // slice, 32-token tile), one wave per 32-feature tile, each wave one MFMA
 // chain over the whole K in the same k order as proj_kernel, fragments loaded
 // straight from global memory eight k-steps ahead. The four tiles meet in LDS
-// and wave 0 runs the same epilogue as proj_kernel, so every output element
-// (e and the gate sums) is bit-identical to what proj_kernel produces.
+// and wave 0 writes them out with the same rounding as proj_kernel, so every
+// output element is bit-identical to what proj_kernel produces.
 template <bool kFwd>
 __global__ void __launch_bounds__(256)
 proj_small_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __restrict__ W,
-                  float* __restrict__ e32, uint16_t* __restrict__ e16, const uint16_t* __restrict__ h,
-                  float* __restrict__ parts) {
+                  float* __restrict__ e32, uint16_t* __restrict__ e16) {
     __shared__ float tile_s[4][64][17];  // [feature tile][lane][accumulator], padded
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int fr = lane & 31, kh = lane >> 5;
@@ -269,12 +271,12 @@ proj_small_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __r
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) vals[i][r] = tile_s[i][lane][r];
-    emit_slice<kFwd, false>(vals, tok, M, fbase, kh, e32, e16, h, parts);
+    emit_slice<kFwd, false>(vals, tok, M, fbase, kh, e32, e16);
 }
 
 template <bool kFwd>
 hipError_t launch(const uint16_t* x, int64_t T, const uint16_t* W, float* e32, uint16_t* e16,
-                  const uint16_t* h, float* parts, hipStream_t stream) {
+                  hipStream_t stream) {
     // the 128 KB of dynamic LDS must be allowed once per device
     static std::atomic<uint64_t> allowed{0};
     int dev = 0;
@@ -289,22 +291,20 @@ hipError_t launch(const uint16_t* x, int64_t T, const uint16_t* W, float* e32, u
     }
     if (T <= kSmallT) {
         dim3 grid(kD / 128, (unsigned)((T + 31) / 32));
-        hipLaunchKernelGGL(proj_small_kernel<kFwd>, grid, dim3(256), 0, stream, x, T, W, e32, e16, h,
-                           parts);
+        hipLaunchKernelGGL(proj_small_kernel<kFwd>, grid, dim3(256), 0, stream, x, T, W, e32, e16);
         return hipGetLastError();
     }
     dim3 grid((unsigned)(kNTiles * ((T + BM - 1) / BM)));
-    hipLaunchKernelGGL(proj_kernel<kFwd>, grid, dim3(kThreads), kLdsBytes, stream, x, T, W, e32,
-                       e16, h, parts);
+    hipLaunchKernelGGL(proj_kernel<kFwd>, grid, dim3(kThreads), kLdsBytes, stream, x, T, W, e32, e16);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_proj(const uint16_t* x, int64_t T, const uint16_t* W, float* e32,
-                       uint16_t* e16, const uint16_t* h, float* parts, hipStream_t stream) {
-    if (h) return launch<true>(x, T, W, e32, e16, h, parts, stream);
-    return launch<false>(x, T, W, e32, nullptr, nullptr, nullptr, stream);
+                       uint16_t* e16, hipStream_t stream) {
+    if (e16) return launch<true>(x, T, W, e32, e16, stream);
+    return launch<false>(x, T, W, e32, nullptr, stream);
 }
 
 }  // namespace ple

@@ -165,7 +165,7 @@ def test_forward_sequence_edge_cases_with_carried_state(dev, small_table, dev_we
     out = inputs.bf16_bits_to_f32(got["out"]).astype(np.float64)
     assert np.all(np.abs(out - ref["out"]) <= OUT_ATOL + OUT_RTOL * np.abs(ref["out"]))
     assert np.all(np.abs(got["g"] - ref["g"]) <= 1e-4)
-    assert np.all(np.abs(got["y"] - ref["y"]) <= y_bound(ref, cu, cw, state0.astype(np.float64)))
+    assert np.all(np.abs(got["y"] - ref["y"]) <= y_bound(ref, cu, cw, state0.astype(np.float64), W))
     hid = st.hist_ids.cpu().numpy()
     hln = st.hist_len.cpu().numpy()
     assert np.array_equal(hln, ref["hist_len"])
