@@ -10,30 +10,33 @@
 // with v before a sequence's first token taken from the carried state.
 //
 // One block of 640 threads owns 16 consecutive tokens; thread i owns
-// features 4i .. 4i+3 and loads, up front, e of the block's tokens and the
-// three before them and h of its own tokens (packed bf16, 8 bytes a row).
-// The gates of those 19 tokens are formed by whole waves: wave w takes
-// tokens w and w + 10 of the window, reads the two 5 KB rows with 16-byte
-// loads (L2 hits: the block's own loads of the same rows are in flight),
-// sums e^2, h.e and h^2 over its 40 features per lane and reduces across the
-// wave with DPP, always in the same order, so a token's gate does not depend
-// on which block or chunk computes it. Each output then takes its four taps
-// from registers, or from the carried state where a tap lies before its
-// sequence's first token (a wave-uniform test). The block holding a
-// sequence's last token writes the new conv state and n-gram history; the
-// old state is read from a copy taken before this kernel, so the in-place
-// update cannot race with readers.
+// features 4i .. 4i+3 and loads, up front, e and h of the block's tokens and
+// of the three before them (packed bf16, 8 bytes a row). The kernel is bound
+// by vector ALU issue (no packed fp32 here), so the arithmetic is kept lean:
+//   - gate sums e^2, h.e, h^2 straight from the packed pairs with the bf16
+//     dot-product instruction (products of bf16 values are exact in fp32);
+//     each wave reduces its lanes to four row sums with DPP, and after a
+//     barrier one thread per token adds the 40 row sums of the block, always
+//     in the same order, so a token's gate does not depend on which block or
+//     chunk computes it;
+//   - v = g e is formed once per window position; an output whose four taps
+//     lie in its own sequence (all but a sequence's first three tokens)
+//     convolves straight from those registers, the others take the taps
+//     before the sequence start from the carried state (a scalar test:
+//     sequence bounds are wave-uniform).
+// The block holding a sequence's last token writes the new conv state and
+// n-gram history; the old state is read from a copy taken before this
+// kernel, so the in-place update cannot race with readers.
 #include "ple_kernels.h"
 
 namespace ple {
 namespace {
 
-constexpr int BT = 16;                 // tokens per block
+constexpr int BT = 16;                   // tokens per block
 constexpr int FPT = 4;                 // features per thread
 constexpr int kThreads = kD / FPT;     // 640
 constexpr int kWaves = kThreads / 64;  // 10
 constexpr int kWin = BT + 3;           // tokens whose v the block needs
-constexpr int kXcds = 8;               // accelerator complex dies on MI355X
 
 __device__ __forceinline__ void unpack4(const u32x2& q, float v[4]) {
     v[0] = bf16_to_f32(q[0] & 0xFFFFu);
@@ -47,22 +50,28 @@ __device__ __forceinline__ float conv4(const float w[kTaps], float v0, float v1,
     return fmaf(w[3], v3, fmaf(w[2], v2, fmaf(w[1], v1, w[0] * v0)));
 }
 
-// v moved across lanes by a DPP pattern; lanes of rows outside kRowMask get 0
-template <int kCtrl, int kRowMask = 0xF>
+// v moved across lanes by a DPP pattern (rows of 16 lanes)
+template <int kCtrl>
 __device__ __forceinline__ float dpp(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl,
-                                                                 kRowMask, 0xF, false));
+                                                                 0xF, 0xF, false));
 }
 
-// sum over the 64 lanes of a wave, complete in lane 63
-__device__ __forceinline__ float wave_sum(float v) {
-    v += dpp<0xB1>(v);        // quad_perm [1,0,3,2]: pairs
-    v += dpp<0x4E>(v);        // quad_perm [2,3,0,1]: quads
-    v += dpp<0x141>(v);       // row_half_mirror: eights
-    v += dpp<0x140>(v);       // row_mirror: rows of 16
-    v += dpp<0x142, 0xA>(v);  // row_bcast15: rows 1, 3 add rows 0, 2
-    v += dpp<0x143, 0xC>(v);  // row_bcast31: rows 2, 3 add rows 0 + 1
+// sum over each row of 16 lanes, complete in every lane of the row
+__device__ __forceinline__ float row_sum(float v) {
+    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]: pairs
+    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]: quads
+    v += dpp<0x141>(v);  // row_half_mirror: eights
+    v += dpp<0x140>(v);  // row_mirror: sixteens
     return v;
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// c + a.lo * b.lo + a.hi * b.hi on packed bf16 pairs
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c,
+                                           false);
 }
 
 __device__ __forceinline__ int seq_of(const int32_t* cu, int32_t S, int64_t t) {
@@ -81,70 +90,74 @@ fuse_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ e16, in
             float* __restrict__ conv_state, int32_t* __restrict__ hist_ids,
             int32_t* __restrict__ hist_len, uint16_t* out, float eps, float* __restrict__ gate_out,
             float* __restrict__ y_out) {
-    __shared__ float sum_s[kWin][3];
+    constexpr int kRows = kWaves * 4;  // rows of 16 lanes in the block
+    __shared__ float red_s[kRows][kWin][3];
     __shared__ float g_s[kWin];
     __shared__ int seg_s[kWin], start_s[kWin], end_s[kWin];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // consecutive token blocks on one XCD, so that the three-token overlap of
-    // neighbouring blocks is served by that XCD's L2
-    const int nb = gridDim.x, b = blockIdx.x;
-    const int per = nb / kXcds, rem = nb % kXcds, xcd = b % kXcds;
-    const int64_t t0 = (int64_t)(xcd * per + (xcd < rem ? xcd : rem) + b / kXcds) * BT;
-    const int c0 = tid * FPT;
+    const int64_t t0 = (int64_t)blockIdx.x * BT;
+    const uint32_t cb = (uint32_t)tid * FPT * 2;  // byte offset of this thread's features in a row
 
-    // this thread's e of the 19-token window and h of the block's tokens
+    // this thread's e and h of the 19-token window
     const u32x2 zero = {0u, 0u};
-    u32x2 ep[kWin], hp[BT];
+    u32x2 ep[kWin], hp[kWin];
+    if (t0 >= 3 && t0 + BT <= T) {
+        // interior block: one uniform base, 32-bit per-lane offsets
+        const char* eb = reinterpret_cast<const char*>(e16) + (t0 - 3) * (kD * 2);
+        const char* hb = reinterpret_cast<const char*>(h) + (t0 - 3) * (kD * 2);
+#pragma unroll
+        for (int i = 0; i < kWin; ++i) {
+            const uint32_t off = cb + (uint32_t)(i * kD * 2);
+            ep[i] = *reinterpret_cast<const u32x2*>(eb + off);
+            hp[i] = *reinterpret_cast<const u32x2*>(hb + off);
+        }
+    } else {
+        // first and last blocks: unconditional loads from a clamped (in-bounds)
+        // row, then a select, so no branches around the loads
+#pragma unroll
+        for (int i = 0; i < kWin; ++i) {
+            const int64_t t = t0 - 3 + i;
+            const bool in = t >= 0 && t < T;
+            const int64_t tc = t < 0 ? 0 : (t >= T ? T - 1 : t);
+            const u32x2 qe = *reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(e16) + tc * (kD * 2) + cb);
+            const u32x2 qh = *reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(h) + tc * (kD * 2) + cb);
+            ep[i] = in ? qe : zero;
+            hp[i] = in ? qh : zero;
+        }
+    }
+
+    // gate sums: four features per thread (bf16 dot products), then the rows
+    // of 16 lanes; lane 15 of each row keeps the row's sums
 #pragma unroll
     for (int i = 0; i < kWin; ++i) {
-        const int64_t t = t0 - 3 + i;
-        ep[i] = (t >= 0 && t < T) ? *reinterpret_cast<const u32x2*>(e16 + t * kD + c0) : zero;
-    }
-#pragma unroll
-    for (int i = 0; i < BT; ++i) {
-        const int64_t t = t0 + i;
-        hp[i] = t < T ? *reinterpret_cast<const u32x2*>(h + t * kD + c0) : zero;
-    }
-
-    // gate sums: one wave per window token, lane l holds features 8l + 512 s + 0..7
-    for (int i = wave; i < kWin; i += kWaves) {
-        const int64_t t = t0 - 3 + i;
-        if (t < 0 || t >= T) continue;
-        const u32x4* hr = reinterpret_cast<const u32x4*>(h + t * kD) + lane;
-        const u32x4* er = reinterpret_cast<const u32x4*>(e16 + t * kD) + lane;
-        u32x4 hv[5], ev[5];
-#pragma unroll
-        for (int s = 0; s < 5; ++s) {
-            hv[s] = hr[s * 64];
-            ev[s] = er[s * 64];
-        }
-        float ee = 0.0f, he = 0.0f, hh = 0.0f;
-#pragma unroll
-        for (int s = 0; s < 5; ++s)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float h0 = bf16_to_f32(hv[s][q] & 0xFFFFu), h1 = bf16_to_f32(hv[s][q] >> 16);
-                const float e0 = bf16_to_f32(ev[s][q] & 0xFFFFu), e1 = bf16_to_f32(ev[s][q] >> 16);
-                ee = fmaf(e1, e1, fmaf(e0, e0, ee));
-                he = fmaf(h1, e1, fmaf(h0, e0, he));
-                hh = fmaf(h1, h1, fmaf(h0, h0, hh));
-            }
-        ee = wave_sum(ee);
-        he = wave_sum(he);
-        hh = wave_sum(hh);
-        if (lane == 63) {
-            sum_s[i][0] = ee;
-            sum_s[i][1] = he;
-            sum_s[i][2] = hh;
+        const u32x2 qe = ep[i], qh = hp[i];
+        float ee = dot2(qe[1], qe[1], dot2(qe[0], qe[0], 0.0f));
+        float he = dot2(qh[1], qe[1], dot2(qh[0], qe[0], 0.0f));
+        float hh = dot2(qh[1], qh[1], dot2(qh[0], qh[0], 0.0f));
+        ee = row_sum(ee);
+        he = row_sum(he);
+        hh = row_sum(hh);
+        if ((lane & 15) == 15) {
+            const int r = wave * 4 + (lane >> 4);
+            red_s[r][i][0] = ee;
+            red_s[r][i][1] = he;
+            red_s[r][i][2] = hh;
         }
     }
     __syncthreads();
     if (tid < kWin) {
         const int64_t t = t0 - 3 + tid;
         if (t >= 0 && t < T) {
-            const float rh = sqrtf(sum_s[tid][2] * (1.0f / kD) + eps);
-            const float re = sqrtf(sum_s[tid][0] * (1.0f / kD) + eps);
-            const float z = sum_s[tid][1] / (rh * re) * (1.0f / 50.596443f);  // 1/sqrt(2560)
+            float ee = 0.0f, he = 0.0f, hh = 0.0f;
+#pragma unroll 8
+            for (int r = 0; r < kRows; ++r) {
+                ee += red_s[r][tid][0];
+                he += red_s[r][tid][1];
+                hh += red_s[r][tid][2];
+            }
+            const float rh = sqrtf(hh * (1.0f / kD) + eps);
+            const float re = sqrtf(ee * (1.0f / kD) + eps);
+            const float z = he / (rh * re) * (1.0f / 50.596443f);  // 1/sqrt(2560)
             const float g = 1.0f / (1.0f + expf(-z));
             g_s[tid] = g;
             if (gate_out && tid >= 3) gate_out[t] = g;
@@ -166,7 +179,7 @@ fuse_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ e16, in
 
     float w[FPT][kTaps];
     {
-        const u32x4* wp = reinterpret_cast<const u32x4*>(conv_w + c0 * kTaps);
+        const u32x4* wp = reinterpret_cast<const u32x4*>(conv_w + tid * FPT * kTaps);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             u32x4 q = wp[i];
@@ -179,46 +192,70 @@ fuse_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ e16, in
         }
     }
 
+    // v = g e at every window position
+    float v[kWin][FPT];
+#pragma unroll
+    for (int j = 0; j < kWin; ++j) {
+        float e[FPT];
+        unpack4(ep[j], e);
+        const float g = g_s[j];
+#pragma unroll
+        for (int q = 0; q < FPT; ++q) v[j][q] = g * e[q];
+    }
+    char* ob = reinterpret_cast<char*>(out) + t0 * (kD * 2);
 #pragma unroll
     for (int i = 0; i < BT; ++i) {
         const int64_t t = t0 + i;
         if (t >= T) break;
-        const int s = seg_s[i + 3];
-        const int64_t st = start_s[i + 3], en = end_s[i + 3];
-        // v at positions t-3 .. t (window slots i .. i+3)
-        float v[kTaps][FPT];
-#pragma unroll
-        for (int k = 0; k < kTaps; ++k) {
-            const int64_t p = t - 3 + k;
+        // sequence bounds of token t are the same in every lane: keep them scalar
+        const int s = __builtin_amdgcn_readfirstlane(seg_s[i + 3]);
+        const int st = __builtin_amdgcn_readfirstlane(start_s[i + 3]);
+        const int en = __builtin_amdgcn_readfirstlane(end_s[i + 3]);
+        // tap k is position t-3+k (window slot i+k); before the sequence start
+        // it comes from the carried state
+        auto tap = [&](int k, float a[FPT]) {
+            const int p = (int)t - 3 + k;
             if (p >= st) {
-                float e[FPT];
-                unpack4(ep[i + k], e);
-                const float g = g_s[i + k];
 #pragma unroll
-                for (int q = 0; q < FPT; ++q) v[k][q] = g * e[q];
+                for (int q = 0; q < FPT; ++q) a[q] = v[i + k][q];
             } else {
-                const f32x4 a = *reinterpret_cast<const f32x4*>(snap + ((int64_t)s * 3 + 3 - (st - p)) * kD + c0);
+                const f32x4 c = *reinterpret_cast<const f32x4*>(snap + ((int64_t)s * 3 + 3 - (st - p)) * kD +
+                                                                tid * FPT);
 #pragma unroll
-                for (int q = 0; q < FPT; ++q) v[k][q] = a[q];
+                for (int q = 0; q < FPT; ++q) a[q] = c[q];
             }
-        }
-        float hv[FPT], y[FPT];
-        unpack4(hp[i], hv);
+        };
+        float y[FPT];
+        if ((int)t - 3 >= st) {
 #pragma unroll
-        for (int q = 0; q < FPT; ++q) y[q] = conv4(w[q], v[0][q], v[1][q], v[2][q], v[3][q]);
+            for (int q = 0; q < FPT; ++q) y[q] = conv4(w[q], v[i][q], v[i + 1][q], v[i + 2][q], v[i + 3][q]);
+        } else {
+            float a0[FPT], a1[FPT], a2[FPT], a3[FPT];
+            tap(0, a0);
+            tap(1, a1);
+            tap(2, a2);
+            tap(3, a3);
+#pragma unroll
+            for (int q = 0; q < FPT; ++q) y[q] = conv4(w[q], a0[q], a1[q], a2[q], a3[q]);
+        }
+        float hv[FPT];
+        unpack4(hp[i + 3], hv);
         const u32x2 o = {pack_bf16x2(hv[0] + y[0], hv[1] + y[1]), pack_bf16x2(hv[2] + y[2], hv[3] + y[3])};
-        __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(out + t * kD + c0));
-        if (y_out) *reinterpret_cast<f32x4*>(y_out + t * kD + c0) = f32x4{y[0], y[1], y[2], y[3]};
-        if (t == en - 1) {
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(ob + (cb + (uint32_t)(i * kD * 2))));
+        if (y_out) *reinterpret_cast<f32x4*>(y_out + t * kD + tid * FPT) = f32x4{y[0], y[1], y[2], y[3]};
+        if ((int)t == en - 1) {
             // last token of sequence s: new conv state = v at t-2, t-1, t
 #pragma unroll
-            for (int r = 0; r < 3; ++r)
-                *reinterpret_cast<f32x4*>(conv_state + ((int64_t)s * 3 + r) * kD + c0) =
-                    f32x4{v[r + 1][0], v[r + 1][1], v[r + 1][2], v[r + 1][3]};
+            for (int r = 0; r < 3; ++r) {
+                float a[FPT];
+                tap(r + 1, a);
+                *reinterpret_cast<f32x4*>(conv_state + ((int64_t)s * 3 + r) * kD + tid * FPT) =
+                    f32x4{a[0], a[1], a[2], a[3]};
+            }
             if (tid == 0) {
                 int hl = hist_len[s];
                 if (hl < 0 || hl > 2) hl = 0;
-                const int64_t L = en - st;
+                const int L = en - st;
                 if (L >= 2) {
                     hist_ids[2 * s] = tokens[en - 2];
                     hist_ids[2 * s + 1] = tokens[en - 1];
