@@ -9,9 +9,11 @@
 //   v = g e,  y[t][c] = sum_k w[c][k] v[t-3+k][c],  out = bf16(h + y),
 // with v before a sequence's first token taken from the carried state.
 //
-// One block of 640 threads owns 16 consecutive tokens; thread i owns
+// One block of 640 threads owns BT consecutive tokens; thread i owns
 // features 4i .. 4i+3 and loads, up front, e and h of the block's tokens and
-// of the three before them (packed bf16, 8 bytes a row). The kernel is bound
+// of the three before them (packed bf16, 8 bytes a row). BT is 16 for long
+// calls and 1 for short ones (decode steps), whose tokens then run side by
+// side; a token's result does not depend on BT. The kernel is bound
 // by vector ALU issue (no packed fp32 here), so the arithmetic is kept lean:
 //   - gate sums e^2, h.e, h^2 straight from the packed pairs with the bf16
 //     dot-product instruction (products of bf16 values are exact in fp32);
@@ -32,11 +34,10 @@
 namespace ple {
 namespace {
 
-constexpr int BT = 16;                   // tokens per block
 constexpr int FPT = 4;                 // features per thread
 constexpr int kThreads = kD / FPT;     // 640
 constexpr int kWaves = kThreads / 64;  // 10
-constexpr int kWin = BT + 3;           // tokens whose v the block needs
+constexpr int kSmallT = 1024;          // calls up to this many tokens run one token per block
 
 __device__ __forceinline__ void unpack4(const u32x2& q, float v[4]) {
     v[0] = bf16_to_f32(q[0] & 0xFFFFu);
@@ -83,6 +84,9 @@ __device__ __forceinline__ int seq_of(const int32_t* cu, int32_t S, int64_t t) {
     return lo;
 }
 
+// BT tokens per block (16 for long calls; 1 for short ones, so that decode
+// steps, whose tokens each start a sequence, run side by side)
+template <int BT>
 __global__ void __launch_bounds__(kThreads)
 fuse_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ e16, int64_t T,
             const int32_t* __restrict__ cu, int32_t S, const int32_t* __restrict__ tokens,
@@ -90,6 +94,7 @@ fuse_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ e16, in
             float* __restrict__ conv_state, int32_t* __restrict__ hist_ids,
             int32_t* __restrict__ hist_len, uint16_t* out, float eps, float* __restrict__ gate_out,
             float* __restrict__ y_out) {
+    constexpr int kWin = BT + 3;       // tokens whose v the block needs
     constexpr int kRows = kWaves * 4;  // rows of 16 lanes in the block
     __shared__ float red_s[kRows][kWin][3];
     __shared__ float g_s[kWin];
@@ -280,10 +285,16 @@ hipError_t launch_fuse(const uint16_t* h, const uint16_t* e16, int64_t T, const 
                        const float* state_snap, float* conv_state, int32_t* hist_ids,
                        int32_t* hist_len, uint16_t* out, float eps, float* gate_out, float* y_out,
                        hipStream_t stream) {
-    const int64_t blocks = (T + BT - 1) / BT;
-    hipLaunchKernelGGL(fuse_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, h, e16, T, cu,
-                       S, tokens, conv_w, state_snap, conv_state, hist_ids, hist_len, out, eps,
-                       gate_out, y_out);
+    if (T <= kSmallT) {
+        hipLaunchKernelGGL(fuse_kernel<1>, dim3((unsigned)T), dim3(kThreads), 0, stream, h, e16, T, cu,
+                           S, tokens, conv_w, state_snap, conv_state, hist_ids, hist_len, out, eps,
+                           gate_out, y_out);
+    } else {
+        const int64_t blocks = (T + 15) / 16;
+        hipLaunchKernelGGL(fuse_kernel<16>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, h, e16, T,
+                           cu, S, tokens, conv_w, state_snap, conv_state, hist_ids, hist_len, out, eps,
+                           gate_out, y_out);
+    }
     return hipGetLastError();
 }
 

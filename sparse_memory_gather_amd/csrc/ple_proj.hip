@@ -222,56 +222,55 @@ proj_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __restric
     }
 }
 
-// Small-T projection (decode steps, short chunks): one block per (128-feature
-// slice, 32-token tile), one wave per 32-feature tile, each wave one MFMA
-// chain over the whole K in the same k order as proj_kernel, fragments loaded
-// straight from global memory eight k-steps ahead. The four tiles meet in LDS
-// and wave 0 writes them out with the same rounding as proj_kernel, so every
-// output element is bit-identical to what proj_kernel produces.
+// Small-T projection (decode steps, short chunks): one block per (32-feature,
+// 32-token) tile, eight waves, wave w holding the fragments of k-steps
+// 20w .. 20w+19, all loaded up front. The tile's accumulator passes from
+// wave to wave through LDS, so it sees the same MFMA sequence over k as in
+// proj_kernel and every output element is bit-identical to what proj_kernel
+// produces; the loads of all eight waves are in flight together.
 template <bool kFwd>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(512)
 proj_small_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __restrict__ W,
                   float* __restrict__ e32, uint16_t* __restrict__ e16) {
-    __shared__ float tile_s[4][64][17];  // [feature tile][lane][accumulator], padded
+    constexpr int KS = kD / 16;        // 160 k-steps
+    constexpr int kW = 8;              // waves
+    constexpr int SPW = KS / kW;       // k-steps per wave
+    __shared__ f32x16 acc_s[64];       // the accumulator between waves
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int fr = lane & 31, kh = lane >> 5;
-    const int fbase = blockIdx.x * 128;
+    const int f0 = blockIdx.x * 32;
     const int64_t tok = (int64_t)blockIdx.y * 32 + fr;
-    const bool live_tok = tok < M;
-    const uint16_t* wrow = W + (int64_t)(fbase + wave * 32 + fr) * kD + kh * 8;
-    const uint16_t* xrow = x + (live_tok ? tok : 0) * kD + kh * 8;
-    constexpr int KS = kD / 16;  // 160 k-steps
-    bf16x8 fa[2][8], fb[2][8];
+    const bool live = tok < M;
+    const uint16_t* wrow = W + (int64_t)(f0 + fr) * kD + wave * SPW * 16 + kh * 8;
+    const uint16_t* xrow = x + (live ? tok : 0) * kD + wave * SPW * 16 + kh * 8;
+    bf16x8 fa[SPW], fb[SPW];
     const bf16x8 zero = {};
-    auto load8 = [&](int s0, int buf) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            fa[buf][q] = *reinterpret_cast<const bf16x8*>(wrow + (s0 + q) * 16);
-            fb[buf][q] = live_tok ? *reinterpret_cast<const bf16x8*>(xrow + (s0 + q) * 16) : zero;
-        }
-    };
+    for (int q = 0; q < SPW; ++q) {
+        fa[q] = *reinterpret_cast<const bf16x8*>(wrow + q * 16);
+        fb[q] = live ? *reinterpret_cast<const bf16x8*>(xrow + q * 16) : zero;
+    }
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-    load8(0, 0);
-    for (int s0 = 0; s0 < KS; s0 += 16) {
-        load8(s0 + 8, 1);
+    for (int w = 0; w < kW; ++w) {
+        if (wave == w) {
+            if (w > 0) acc = acc_s[lane];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][q], fb[0][q], acc, 0, 0, 0);
-        if (s0 + 16 < KS) load8(s0 + 16, 0);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][q], fb[1][q], acc, 0, 0, 0);
+            for (int q = 0; q < SPW; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[q], fb[q], acc, 0, 0, 0);
+            if (w + 1 < kW) acc_s[lane] = acc;
+        }
+        __syncthreads();
     }
+    if (wave != kW - 1 || !live) return;
+    // lane holds token `tok` and features f0 + 8 g + 4 kh + 0..3
 #pragma unroll
-    for (int r = 0; r < 16; ++r) tile_s[wave][lane][r] = acc[r];
-    __syncthreads();
-    if (wave != 0) return;
-    float vals[4][16];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) vals[i][r] = tile_s[i][lane][r];
-    emit_slice<kFwd, false>(vals, tok, M, fbase, kh, e32, e16);
+    for (int g = 0; g < 4; ++g) {
+        const float v0 = acc[4 * g], v1 = acc[4 * g + 1], v2 = acc[4 * g + 2], v3 = acc[4 * g + 3];
+        const int64_t off = tok * kD + f0 + g * 8 + kh * 4;
+        if (!kFwd || e32) *reinterpret_cast<f32x4*>(e32 + off) = f32x4{v0, v1, v2, v3};
+        if (kFwd) *reinterpret_cast<u32x2*>(e16 + off) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+    }
 }
 
 template <bool kFwd>
@@ -290,8 +289,8 @@ hipError_t launch(const uint16_t* x, int64_t T, const uint16_t* W, float* e32, u
         allowed.fetch_or(bit, std::memory_order_acq_rel);
     }
     if (T <= kSmallT) {
-        dim3 grid(kD / 128, (unsigned)((T + 31) / 32));
-        hipLaunchKernelGGL(proj_small_kernel<kFwd>, grid, dim3(256), 0, stream, x, T, W, e32, e16);
+        dim3 grid(kD / 32, (unsigned)((T + 31) / 32));
+        hipLaunchKernelGGL(proj_small_kernel<kFwd>, grid, dim3(512), 0, stream, x, T, W, e32, e16);
         return hipGetLastError();
     }
     dim3 grid((unsigned)(kNTiles * ((T + BM - 1) / BM)));

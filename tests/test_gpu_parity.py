@@ -201,6 +201,33 @@ def test_chunked_equals_unchunked_and_decode_equals_prefill(dev, small_table, de
             assert np.array_equal(a, b), cuts
 
 
+def test_kernel_variants_agree_bit_exactly(dev, small_table, dev_weights):
+    # a 1300-token call runs the tiled projection and 16-token fuse blocks;
+    # its pieces (<= 256 and <= 1024 tokens) run the small-T projection and
+    # one-token fuse blocks: every output and the carried state must match
+    tab, sc = small_table
+    rng = np.random.default_rng(16)
+    n = 1300
+    toks = inputs.uniform_tokens(rng, n)
+    h = inputs.normal_bf16(rng, (n, D))
+
+    def run(cuts):
+        st = ple.State(1, dev)
+        outs, pos = [], 0
+        for L in cuts:
+            r = _forward(dev, tab, sc, dev_weights, toks[pos:pos + L], np.array([0, L], np.int32),
+                         h[pos:pos + L], st)
+            outs.append(host_bits(r["out"]))
+            pos += L
+        return np.concatenate(outs), st.conv_state.cpu().numpy(), st.hist_ids.cpu().numpy()
+
+    full = run([n])
+    for cuts in ([1024, 276], [200, 1100], [257, 255, 788], [3, 1297]):
+        got = run(cuts)
+        for a, b in zip(got, full):
+            assert np.array_equal(a, b), cuts
+
+
 def test_in_place_out_equals_h(dev, small_table, dev_weights):
     tab, sc = small_table
     rng = np.random.default_rng(7)
