@@ -254,17 +254,16 @@ def main():
         else:
             step(k, events=ev[k])
     torch.cuda.synchronize()
-    stage = np.zeros(4)
-    for e in ev:
-        for i in range(4):
-            stage[i] += hev.elapsed_ms(e[i], e[i + 1])
-    stage_us = 1e3 * stage / len(ev)  # average per launch
+    per_launch = np.array([[hev.elapsed_ms(e[i], e[i + 1]) for i in range(4)] for e in ev])
+    stage_us = 1e3 * per_launch.mean(axis=0)  # average per launch
+    stage_med_us = 1e3 * np.median(per_launch, axis=0)
     tokens_per_call = tokens_per_step / n_calls
 
     # valid lookups per call (for the gather's algorithmic bytes)
     rid = ple.ple_hash(batches[0][0], batches[0][1], torch.zeros((wl.S, 2), dtype=torch.int32, device=dev),
                        torch.full((wl.S,), 2 if name == "decode" else 0, dtype=torch.int32, device=dev), wl.R)
     lookups = int((rid >= 0).sum().item()) if name != "decode" else 2 * batches[0][0].numel()
+    unique_rows = int(torch.unique(rid[rid >= 0]).numel()) if name != "decode" else None
     gather_bytes = lookups * GATHER_BYTES_PER_LOOKUP + tokens_per_call * GATHER_BYTES_PER_TOKEN
     gather_gbs = gather_bytes / (stage_us[1] * 1e-6) / 1e9
     proj_flop = tokens_per_call * PROJ_FLOP_PER_TOKEN
@@ -304,9 +303,12 @@ def main():
         "roofline": roofline,
         "stages_us": {"hash": round(float(stage_us[0]), 2), "gather": round(float(stage_us[1]), 2),
                       "proj": round(float(stage_us[2]), 2), "fuse": round(float(stage_us[3]), 2)},
+        "stages_median_us": {k: round(float(v), 2) for k, v in zip(("hash", "gather", "proj", "fuse"),
+                                                                    stage_med_us)},
         "gather": {"bound": "hbm", "achieved": round(gather_gbs, 1), "peak": HBM_PEAK_GBS,
                    "unit": "GB/s", "frac": round(gather_gbs / HBM_PEAK_GBS, 4),
                    "bytes_per_launch": gather_bytes, "lookups_per_launch": lookups,
+                   "unique_rows_per_launch": unique_rows,
                    "traffic": recorded_traffic("gather_kernel", name)},
         "proj": {"bound": "mfma", "achieved": round(proj_tflops, 2), "peak": BF16_PEAK_TFLOPS,
                  "unit": "TFLOP/s", "frac": round(proj_tflops / BF16_PEAK_TFLOPS, 4)},

@@ -89,3 +89,15 @@ extern "C" int gen_fill_table(uint8_t* table, float* scales, int64_t R, uint64_t
                        scale_lo, scale_span);
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }
+
+// scales number 0 .. n-1 (e.g. the 16 R scales of the 16 x 160-byte head view)
+extern "C" int gen_fill_scales(float* scales, int64_t n, uint64_t seed, uint32_t scale_lo,
+                               uint32_t scale_span, void* stream) {
+    if (!scales || n <= 0) return -1;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    uint64_t want_s = ((uint64_t)n + 255) / 256;
+    unsigned grid_s = (unsigned)(want_s < 65536 ? want_s : 65536);
+    hipLaunchKernelGGL(fill_scales, dim3(grid_s), dim3(256), 0, s, scales, (uint64_t)n, seed, scale_lo,
+                       scale_span);
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+}

@@ -12,6 +12,9 @@
  *          magnitude code is the number of thresholds <= u.
  *   scale: counter = (r, 1, 0, 0); m = lo + (hi32(out[0]) % span);
  *          scale = m * 2^-23 (an exact fp32 with at most 20 significant bits).
+ * The same bytes, read as 16 head tables of R rows x 160 bytes, give row r of
+ * head h at element g = (h R + r) 160; its scale is scale number h R + r of
+ * the same recipe (the first R being the 2560-wide rows' scales).
  */
 #include <stdint.h>
 #include <string.h>
@@ -77,5 +80,31 @@ void gen_table_rows(uint64_t seed, const int64_t* ids, int64_t n, const uint32_t
         float s = (float)m;            /* exact: m < 2^24 */
         s *= 1.0f / 8388608.0f;        /* * 2^-23, exact */
         scales_out[i] = s;
+    }
+}
+
+/* Codes of elements g0 .. g0+n-1 (g0 and n multiples of 8) into out[n]. */
+void gen_table_span(uint64_t seed, uint64_t g0, int64_t n, const uint32_t* thr, uint8_t* out) {
+    const uint64_t key[2] = {seed, 0};
+    for (int64_t c8 = 0; c8 < n / 8; ++c8) {
+        uint64_t ctr[4] = {g0 / 8 + (uint64_t)c8, 0, 0, 0}, o[4];
+        gen_philox4x64_10(ctr, key, o);
+        for (int j = 0; j < 8; ++j) {
+            uint64_t word = o[j / 2];
+            uint32_t w = (j & 1) ? (uint32_t)(word >> 32) : (uint32_t)word;
+            out[c8 * 8 + j] = code_of(w, thr);
+        }
+    }
+}
+
+/* Scales number ids[0..n) into out[n]. */
+void gen_scales(uint64_t seed, const int64_t* ids, int64_t n, uint32_t scale_lo, uint32_t scale_span,
+                float* out) {
+    const uint64_t key[2] = {seed, 0};
+    for (int64_t i = 0; i < n; ++i) {
+        uint64_t sc[4] = {(uint64_t)ids[i], 1, 0, 0}, so[4];
+        gen_philox4x64_10(sc, key, so);
+        uint32_t m = scale_lo + (uint32_t)(so[0] >> 32) % scale_span;
+        out[i] = (float)m * (1.0f / 8388608.0f);
     }
 }

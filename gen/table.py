@@ -41,6 +41,12 @@ def _host_lib():
         lib.gen_table_rows.restype = None
         lib.gen_philox4x64_10.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         lib.gen_philox4x64_10.restype = None
+        lib.gen_table_span.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int64, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+        lib.gen_table_span.restype = None
+        lib.gen_scales.argtypes = [ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32,
+                                   ctypes.c_uint32, ctypes.c_void_p]
+        lib.gen_scales.restype = None
         _host = lib
     return _host
 
@@ -67,6 +73,29 @@ def rows_cpu(ids, seed: int = inputs.TABLE_SEED):
     return rows, scales
 
 
+HEADS = 16
+SLICE = inputs.D // HEADS   # 160 bytes per head-table row
+
+
+def slices_cpu(heads, ids, R: int, seed: int = inputs.TABLE_SEED):
+    """Rows `ids` of head tables `heads` in the 16 x [R][160] view of the same
+    table bytes: (codes uint8[n][160], scales float32[n]); element g =
+    (h R + r) 160 + j, scale number h R + r."""
+    heads = np.asarray(heads, dtype=np.int64).reshape(-1)
+    ids = np.asarray(ids, dtype=np.int64).reshape(-1)
+    n = len(ids)
+    codes = np.empty((n, SLICE), dtype=np.uint8)
+    q = np.ascontiguousarray(heads * R + ids)
+    thr = np.ascontiguousarray(thresholds())
+    lib = _host_lib()
+    for i in range(n):
+        lib.gen_table_span(seed, int(q[i]) * SLICE, SLICE, thr.ctypes.data, codes[i].ctypes.data)
+    scales = np.empty(n, dtype=np.float32)
+    if n:
+        lib.gen_scales(seed, q.ctypes.data, n, inputs.SCALE_M_LO, inputs.SCALE_M_SPAN, scales.ctypes.data)
+    return codes, scales
+
+
 def _hip_lib():
     global _hip
     if _hip is None:
@@ -78,6 +107,9 @@ def _hip_lib():
                                        ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint32,
                                        ctypes.c_uint32, ctypes.c_void_p]
         lib.gen_fill_table.restype = ctypes.c_int
+        lib.gen_fill_scales.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32,
+                                        ctypes.c_uint32, ctypes.c_void_p]
+        lib.gen_fill_scales.restype = ctypes.c_int
         _hip = lib
     return _hip
 
@@ -96,3 +128,16 @@ def table_gpu(R: int, seed: int = inputs.TABLE_SEED, device="cuda"):
     torch.cuda.current_stream(table.device).synchronize()
     del thr
     return table, scales
+
+
+def head_scales_gpu(R: int, seed: int = inputs.TABLE_SEED, device="cuda"):
+    """The 16 R row scales of the 16 x [R][160] head view, float32 [16][R], on the GPU."""
+    import torch
+    scales = torch.empty((HEADS, R), dtype=torch.float32, device=device)
+    stream = torch.cuda.current_stream(scales.device).cuda_stream
+    rc = _hip_lib().gen_fill_scales(scales.data_ptr(), HEADS * R, seed, inputs.SCALE_M_LO,
+                                    inputs.SCALE_M_SPAN, stream)
+    if rc != 0:
+        raise RuntimeError(f"gen_fill_scales failed: {rc}")
+    torch.cuda.current_stream(scales.device).synchronize()
+    return scales

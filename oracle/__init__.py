@@ -17,6 +17,9 @@ Parity status of each step (see the pins under tests/):
   e4m3_value              pinned (all 256 codes vs torch.float8_e4m3fn)
   gather_dequant          pinned (raw bytes vs generator rows; rounding
                           properties against the exact rational sum)
+  ngram_ids_heads,        pinned (SplitMix64 published stream for the head
+  gather_dequant_heads    offsets; heads 0/8 equal the 2-lookup IDs; raw
+                          bytes vs generator; torch fp32 product; placement)
   project                 pinned (numpy fp64 matmul; W = I)
   round_bf16              pinned (exact rational round-half-even; ties,
                           single rounding, subnormal step, overflow)
@@ -54,6 +57,9 @@ def _load():
             "oracle_key2": ([ctypes.c_uint32, ctypes.c_uint32], ctypes.c_uint64),
             "oracle_key3": ([ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32], ctypes.c_uint64),
             "oracle_ngram_ids": ([_P, _P, _I32, _P, _P, _I64, _P], None),
+            "oracle_head_mix": ([ctypes.c_uint64, ctypes.c_int32], ctypes.c_uint64),
+            "oracle_ngram_ids_heads": ([_P, _P, _I32, _P, _P, _I64, _P], None),
+            "oracle_gather_dequant_heads": ([_P, _I64, _P, _P, _P, _P], None),
             "oracle_hist_update": ([_P, _P, _I32, _P, _P, _P, _P], None),
             "oracle_e4m3_value": ([ctypes.c_uint8], ctypes.c_double),
             "oracle_bf16_rne": ([ctypes.c_float], ctypes.c_uint16),
@@ -118,6 +124,22 @@ def ngram_ids(tokens, cu_seqlens, hist_ids, hist_len, R: int) -> np.ndarray:
     return out
 
 
+def head_mix(key: int, head: int) -> int:
+    return int(_load().oracle_head_mix(key, head))
+
+
+def ngram_ids_heads(tokens, cu_seqlens, hist_ids, hist_len, R: int) -> np.ndarray:
+    """Row IDs [T][16] of the 16-lookup layout (R rows per head table)."""
+    tokens = _c(tokens, np.int32)
+    cu = _c(cu_seqlens, np.int32)
+    S = len(cu) - 1
+    hist_ids = _c(hist_ids, np.int32).reshape(S, 2)
+    hist_len = _c(hist_len, np.int32).reshape(S)
+    out = np.full((len(tokens), 16), -7, dtype=np.int32)
+    _load().oracle_ngram_ids_heads(_ptr(tokens), _ptr(cu), S, _ptr(hist_ids), _ptr(hist_len), R, _ptr(out))
+    return out
+
+
 def hist_update(tokens, cu_seqlens, hist_ids, hist_len):
     tokens = _c(tokens, np.int32)
     cu = _c(cu_seqlens, np.int32)
@@ -141,6 +163,20 @@ def gather_dequant(row_ids, table, scales, raw: bool = False):
     x = np.empty((T, D), dtype=np.uint16)
     r = np.empty((T, 2, D), dtype=np.uint8) if raw else None
     _load().oracle_gather_dequant(_ptr(row_ids), T, _ptr(table), _ptr(scales), _ptr(x), _ptr(r))
+    return (x, r) if raw else x
+
+
+def gather_dequant_heads(idx, slices, scales, raw: bool = False):
+    """x (bf16 bits [T][2560]) of the 16-lookup layout from 160-byte rows
+    `slices` (uint8[n][160]) and `scales` (float32[n]); idx[t][h] indexes
+    them (-1 = missing)."""
+    idx = _c(idx, np.int32).reshape(-1, 16)
+    slices = _c(slices, np.uint8)
+    scales = _c(scales, np.float32)
+    T = idx.shape[0]
+    x = np.empty((T, D), dtype=np.uint16)
+    r = np.empty((T, 16, 160), dtype=np.uint8) if raw else None
+    _load().oracle_gather_dequant_heads(_ptr(idx), T, _ptr(slices), _ptr(scales), _ptr(x), _ptr(r))
     return (x, r) if raw else x
 
 
@@ -211,6 +247,39 @@ def forward(tokens, cu_seqlens, h_bf16, W_bf16, conv_w_bf16, R: int, row_source,
     compact = np.full(row_ids.shape, -1, dtype=np.int32)
     compact[row_ids >= 0] = inv.astype(np.int32)
     x = gather_dequant(compact, codes, scales)
+    e = project(x, W_bf16)
+    e_b = round_bf16(e)
+    g = gate(h_bf16, e_b, eps)
+    y, out, st = conv_fuse(h_bf16, e_b, g, cu, conv_w_bf16, conv_state)
+    hid, hln = hist_update(tokens, cu, hist_ids, hist_len)
+    return dict(row_ids=row_ids, x=x, e=e, e_b=e_b, g=g, y=y, out=out,
+                hist_ids=hid, hist_len=hln, conv_state=st)
+
+
+def forward_heads(tokens, cu_seqlens, h_bf16, W_bf16, conv_w_bf16, R: int, slice_source,
+                  hist_ids=None, hist_len=None, conv_state=None, eps: float = 1e-6):
+    """forward() for the 16-lookup layout: row IDs [T][16] into 16 head
+    tables of R rows x 160 bytes, rows from slice_source(heads, rows) ->
+    (codes uint8[n][160], scales float32[n]); the rest of the path is the
+    same."""
+    tokens = _c(tokens, np.int32)
+    cu = _c(cu_seqlens, np.int32)
+    S = len(cu) - 1
+    if hist_ids is None:
+        hist_ids = np.zeros((S, 2), np.int32)
+    if hist_len is None:
+        hist_len = np.zeros(S, np.int32)
+    if conv_state is None:
+        conv_state = np.zeros((S, 3, D), np.float64)
+    row_ids = ngram_ids_heads(tokens, cu, hist_ids, hist_len, R)
+    heads = np.broadcast_to(np.arange(16, dtype=np.int64), row_ids.shape)
+    valid = row_ids >= 0
+    q = heads[valid] * R + row_ids[valid]
+    uniq, inv = np.unique(q, return_inverse=True)
+    codes, scales = slice_source(uniq // R, uniq % R)
+    compact = np.full(row_ids.shape, -1, dtype=np.int32)
+    compact[valid] = inv.astype(np.int32)
+    x = gather_dequant_heads(compact, codes, scales)
     e = project(x, W_bf16)
     e_b = round_bf16(e)
     g = gate(h_bf16, e_b, eps)

@@ -101,6 +101,47 @@ void oracle_ngram_ids(const int32_t* tokens, const int32_t* cu, int32_t S,
     }
 }
 
+/* The 16-lookup layout (the model card's 16 lookups of 160-byte rows per
+ * token, SSD-streaming page, "技术细节"): the same table read as 16 head
+ * tables of R rows x 160 bytes. Heads 0..7 hash the bigram, heads 8..15 the
+ * trigram; head h's key is offset by (h mod 8) steps of SplitMix64's
+ * increment before the same finalizer, i.e. the head-th output of a
+ * SplitMix64 stream started at the key, so head 0 and head 8 give the
+ * 2-lookup layout's bigram and trigram rows. */
+#define GOLDEN_GAMMA 0x9E3779B97F4A7C15ULL
+
+uint64_t oracle_head_mix(uint64_t key, int32_t head) {
+    return oracle_mix64(key + (uint64_t)(head % 8) * GOLDEN_GAMMA);
+}
+
+/* row_ids[t][h], h = 0..15, -1 when the head's n-gram is missing. */
+void oracle_ngram_ids_heads(const int32_t* tokens, const int32_t* cu, int32_t S,
+                            const int32_t* hist_ids, const int32_t* hist_len, int64_t R,
+                            int32_t* row_ids) {
+    for (int32_t s = 0; s < S; ++s) {
+        int32_t start = cu[s], end = cu[s + 1];
+        int32_t hl = hist_len[s];
+        int64_t n = hl + (end - start);
+        for (int64_t j = hl; j < n; ++j) {
+            int32_t t = start + (int32_t)(j - hl);
+#define HS(idx) ((idx) < hl ? hist_ids[2 * s + 2 - hl + (idx)] : tokens[start + (idx) - hl])
+            uint32_t cur = (uint32_t)HS(j);
+            for (int h = 0; h < 16; ++h) {
+                int32_t r = -1;
+                if (h < 8 && j >= 1) {
+                    uint32_t p1 = (uint32_t)HS(j - 1);
+                    r = (int32_t)(oracle_head_mix(oracle_key2(p1, cur), h) % (uint64_t)R);
+                } else if (h >= 8 && j >= 2) {
+                    uint32_t p1 = (uint32_t)HS(j - 1), p2 = (uint32_t)HS(j - 2);
+                    r = (int32_t)(oracle_head_mix(oracle_key3(p2, p1, cur), h) % (uint64_t)R);
+                }
+                row_ids[16 * (int64_t)t + h] = r;
+            }
+#undef HS
+        }
+    }
+}
+
 /* New history after a chunk: the last min(2, hist_len + L) IDs, right-aligned. */
 void oracle_hist_update(const int32_t* tokens, const int32_t* cu, int32_t S,
                         const int32_t* hist_ids, const int32_t* hist_len,
@@ -179,6 +220,29 @@ void oracle_gather_dequant(const int32_t* row_ids, int64_t T, const uint8_t* tab
                 uint8_t* dst = raw + (t * 2 + k) * D;
                 if (r >= 0) memcpy(dst, table + (int64_t)r * D, D);
                 else memset(dst, 0, D);
+            }
+        }
+    }
+}
+
+/* 16-lookup layout: x[t][160 h + j] = bf16( fl32(dec(code_h[j]) * scale_h) )
+ * for a present head row, +0 for a missing one; `slices` holds the rows
+ * referenced by idx[t][h] (uint8 [n][160]) with their scales. raw (optional)
+ * gets the 16 rows' bytes, zero for a missing row. */
+void oracle_gather_dequant_heads(const int32_t* idx, int64_t T, const uint8_t* slices,
+                                 const float* scales, uint16_t* x, uint8_t* raw) {
+    for (int64_t t = 0; t < T; ++t) {
+        for (int h = 0; h < 16; ++h) {
+            int32_t r = idx[16 * t + h];
+            for (int j = 0; j < 160; ++j) {
+                float v = 0.0f;
+                if (r >= 0) v = (float)oracle_e4m3_value(slices[(int64_t)r * 160 + j]) * scales[r];
+                x[t * D + 160 * h + j] = oracle_bf16_rne(v);
+            }
+            if (raw) {
+                uint8_t* dst = raw + (t * 16 + h) * 160;
+                if (r >= 0) memcpy(dst, slices + (int64_t)r * 160, 160);
+                else memset(dst, 0, 160);
             }
         }
     }

@@ -443,6 +443,98 @@ def test_conv_short_segments_carry_state():
 
 
 # ---------------------------------------------------------------------------
+# 16-lookup layout (16 head tables of 160-byte rows)
+# ---------------------------------------------------------------------------
+
+GAMMA = 0x9E3779B97F4A7C15
+
+
+def test_head_mix_is_the_published_splitmix64_stream():
+    # head h of a key is output h + 1 of SplitMix64 started one increment
+    # before the key; heads 8..15 repeat heads 0..7 on the trigram key
+    for seed, idx, out in _golden("splitmix64.txt"):
+        k = int(idx) - 1
+        if 0 <= k < 8:
+            key = (int(seed) + GAMMA) & M64
+            assert oracle.head_mix(key, k) == int(out)
+            assert oracle.head_mix(key, 8 + k) == int(out)
+
+
+def test_ngram_ids_heads_against_keys_and_two_lookup_ids():
+    R = 20_000_096
+    rng = np.random.default_rng(41)
+    toks = inputs.uniform_tokens(rng, 40)
+    cu = np.array([0, 1, 2, 5, 40], np.int32)
+    hist = np.array([[0, 0], [0, 11], [3, 4], [0, 0]], np.int32)
+    hl = np.array([0, 1, 2, 0], np.int32)
+    heads = oracle.ngram_ids_heads(toks, cu, hist, hl, R)
+    two = oracle.ngram_ids(toks, cu, hist, hl, R)
+    assert np.array_equal(heads[:, 0], two[:, 0]) and np.array_equal(heads[:, 8], two[:, 1])
+    for s in range(4):
+        seq = list(hist[s][2 - hl[s]:]) + list(toks[cu[s]:cu[s + 1]])
+        for i in range(cu[s], cu[s + 1]):
+            j = hl[s] + i - cu[s]
+            for h in range(16):
+                if h < 8:
+                    want = -1 if j < 1 else oracle.head_mix(oracle.key2(seq[j - 1], seq[j]), h) % R
+                else:
+                    want = -1 if j < 2 else oracle.head_mix(oracle.key3(seq[j - 2], seq[j - 1], seq[j]), h) % R
+                assert heads[i, h] == want, (s, i, h)
+    full = heads[heads[:, 15] >= 0]
+    assert all(len(set(r[:8])) == 8 and len(set(r[8:])) == 8 for r in full)   # heads read distinct rows
+
+
+def test_head_slices_are_the_table_bytes_at_their_linear_offset():
+    R = 65_536
+    rng = np.random.default_rng(42)
+    hs, rs = rng.integers(0, 16, 40), rng.integers(0, R, 40)
+    codes, scales = table.slices_cpu(hs, rs, R)
+    for h, r, c in zip(hs, rs, codes):
+        g = (int(h) * R + int(r)) * 160
+        row, _ = table.rows_cpu([g // 2560])
+        assert np.array_equal(c, row[0][g % 2560:g % 2560 + 160])
+    _, sc_rows = table.rows_cpu(rs)
+    _, sc_head0 = table.slices_cpu(np.zeros(40, np.int64), rs, R)
+    assert np.array_equal(sc_head0, sc_rows)          # head 0 shares the 2560-wide rows' scales
+
+
+def test_gather_dequant_heads_torch_product_placement_and_missing_rows():
+    rng = np.random.default_rng(43)
+    n = 50
+    codes = rng.integers(0, 256, (n, 160), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x80             # no NaN codes; keep some -0
+    scales = (rng.uniform(0.01, 0.1, n)).astype(np.float32)
+    idx = rng.integers(0, n, (12, 16)).astype(np.int32)
+    idx[rng.random((12, 16)) < 0.25] = -1
+    x, raw = oracle.gather_dequant_heads(idx, codes, scales, raw=True)
+    dec = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32)
+    sc = torch.from_numpy(scales)
+    for t in range(12):
+        for h in range(16):
+            r = idx[t, h]
+            got = x[t, 160 * h:160 * h + 160]
+            if r < 0:
+                assert np.all(got == 0) and np.all(raw[t, h] == 0)      # +0, not -0
+            else:
+                want = (dec[r] * sc[r]).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+                assert np.array_equal(got, want), (t, h)
+                assert np.array_equal(raw[t, h], codes[r])
+
+
+def test_forward_heads_fresh_sequence_and_bigram_only_token(weights):
+    W, cw = weights
+    R = 65_536
+    toks, h = _small_stream(5, seed=44)
+    r = oracle.forward_heads(toks, np.array([0, 5], np.int32), h, W, cw, R,
+                             lambda hs, rs: table.slices_cpu(hs, rs, R))
+    assert np.all(r["x"][0] == 0) and r["g"][0] == 0.5
+    assert np.array_equal(r["out"][0], inputs.bf16_bits_to_f32(h[0]).astype(np.float64))
+    assert np.all(r["row_ids"][1, :8] >= 0) and np.all(r["row_ids"][1, 8:] == -1)
+    assert np.any(r["x"][1, :1280] != 0) and np.all(r["x"][1, 1280:] == 0)
+    assert np.all(r["row_ids"][2:] >= 0)
+
+
+# ---------------------------------------------------------------------------
 # Whole path
 # ---------------------------------------------------------------------------
 
