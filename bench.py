@@ -40,6 +40,10 @@ D = 2560
 #  hash:   per token 4 B token read (+ history), 8 B ids written
 GATHER_BYTES_PER_LOOKUP = 2560 + 4
 GATHER_BYTES_PER_TOKEN = 8 + 2 * D
+# 16-lookup layout: per valid head lookup 160 B of codes + 4 B scale; per
+# token 64 B of row ids and 5120 B of bf16 x
+HEADS_BYTES_PER_LOOKUP = 160 + 4
+HEADS_BYTES_PER_TOKEN = 64 + 2 * D
 PROJ_FLOP_PER_TOKEN = 2 * D * D
 FUSE_BYTES_PER_TOKEN = 3 * 2 * D
 
@@ -47,6 +51,8 @@ FUSE_BYTES_PER_TOKEN = 3 * 2 * D
 KERNEL_SOURCES = {
     "proj_kernel": ["sparse_memory_gather_amd/csrc/ple_proj.hip", "sparse_memory_gather_amd/csrc/ple_kernels.h"],
     "gather_kernel": ["sparse_memory_gather_amd/csrc/ple_gather.hip", "sparse_memory_gather_amd/csrc/ple_kernels.h"],
+    "gather_heads_kernel": ["sparse_memory_gather_amd/csrc/ple_gather.hip",
+                            "sparse_memory_gather_amd/csrc/ple_kernels.h"],
     "fuse_kernel": ["sparse_memory_gather_amd/csrc/ple_fuse.hip", "sparse_memory_gather_amd/csrc/ple_kernels.h"],
 }
 
@@ -103,7 +109,9 @@ class HipEvents:
         return float(ms.value)
 
 
-def describe(name, wl):
+def describe(name, wl, heads=False):
+    if heads:
+        return describe(name, wl) + ", read as 16 head tables of 160-byte rows (16 lookups per token)"
     T = len(wl.chunks[0][0])
     if name == "prefill":
         return f"prefill: 1 sequence x 32768 Zipf(1.1) tokens, {wl.R:,}-row x 2560 FP8 E4M3 table (51.2 GB) in HBM"
@@ -116,7 +124,7 @@ def describe(name, wl):
     return f"tiny: 1 x {T} uniform tokens, {wl.R:,}-row FP8 table"
 
 
-def cpu_baseline(wl, name, W, cw, h0, budget_s=12.0):
+def cpu_baseline(wl, name, W, cw, h0, budget_s=12.0, heads=False):
     """The CPU oracle (as it stands) on the first N tokens of the workload's
     first chunk, N sized so that the run takes about `budget_s` seconds."""
     import numpy as np
@@ -131,8 +139,13 @@ def cpu_baseline(wl, name, W, cw, h0, budget_s=12.0):
         # the first n tokens, cut at the same sequence boundaries
         cut = np.minimum(cu, n).astype(np.int32)
         t0 = time.perf_counter()
-        oracle.forward(toks[:n], cut, h0[:n], W, cw, wl.R, table.rows_cpu,
-                       np.zeros((S, 2), np.int32), np.zeros(S, np.int32), np.zeros((S, 3, D)))
+        if heads:
+            oracle.forward_heads(toks[:n], cut, h0[:n], W, cw, wl.R,
+                                 lambda hs, rs: table.slices_cpu(hs, rs, wl.R),
+                                 np.zeros((S, 2), np.int32), np.zeros(S, np.int32), np.zeros((S, 3, D)))
+        else:
+            oracle.forward(toks[:n], cut, h0[:n], W, cw, wl.R, table.rows_cpu,
+                           np.zeros((S, 2), np.int32), np.zeros(S, np.int32), np.zeros((S, 3, D)))
         return time.perf_counter() - t0
 
     T = len(toks)
@@ -152,6 +165,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill", choices=["tiny", "decode", "prefill", "ragged", "long"])
+    ap.add_argument("--layout", default="two", choices=["two", "heads"],
+                    help="two: 2 lookups of 2560-byte rows per token; heads: 16 lookups of 160-byte rows")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -180,6 +195,9 @@ def main():
 
     print(f"[bench] {name}: generating the {wl.R:,}-row table", file=sys.stderr, flush=True)
     tab, sc = table.table_gpu(wl.R, device=dev)
+    heads = args.layout == "heads"
+    if heads:
+        sc = table.head_scales_gpu(wl.R, device=dev)
     Wd, cwd = bf16(W), bf16(cw)
     ws = ple.Workspace(dev)
 
@@ -201,7 +219,7 @@ def main():
         hh = bf16(wl.history_hidden(hist.size))
         cu_h = torch.arange(0, hist.size + 1, hist.shape[1], dtype=torch.int32, device=dev)
         ple.ple_forward(torch.from_numpy(hist.reshape(-1)).to(dev), cu_h, tab, sc, Wd, cwd, hh, state,
-                        workspace=ws)
+                        workspace=ws, heads=heads)
         del hh
     outs = [torch.empty_like(b[2]) for b in batches] if name in ("long", "decode") else \
         [torch.empty_like(batches[0][2])]
@@ -211,18 +229,18 @@ def main():
     if name == "long":
         def step(k, events=None):
             for (t, c, h), o in zip(batches, outs):
-                ple.ple_forward(t, c, tab, sc, Wd, cwd, h, state, out=o, workspace=ws, events=events)
+                ple.ple_forward(t, c, tab, sc, Wd, cwd, h, state, out=o, workspace=ws, events=events, heads=heads)
         tokens_per_step = sum(b[0].numel() for b in batches)
     elif name == "decode":
         def step(k, events=None):
             t, c, h = batches[k % len(batches)]
             ple.ple_forward(t, c, tab, sc, Wd, cwd, h, state, out=outs[k % len(outs)], workspace=ws,
-                            events=events)
+                            events=events, heads=heads)
         tokens_per_step = batches[0][0].numel()
     else:
         def step(k, events=None):
             t, c, h = batches[0]
-            ple.ple_forward(t, c, tab, sc, Wd, cwd, h, state, out=outs[0], workspace=ws, events=events)
+            ple.ple_forward(t, c, tab, sc, Wd, cwd, h, state, out=outs[0], workspace=ws, events=events, heads=heads)
         tokens_per_step = batches[0][0].numel()
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
@@ -250,7 +268,7 @@ def main():
         if name == "long":
             for j, ((t, c, h), o) in enumerate(zip(batches, outs)):
                 ple.ple_forward(t, c, tab, sc, Wd, cwd, h, state, out=o, workspace=ws,
-                                events=ev[k * n_calls + j])
+                                events=ev[k * n_calls + j], heads=heads)
         else:
             step(k, events=ev[k])
     torch.cuda.synchronize()
@@ -261,10 +279,19 @@ def main():
 
     # valid lookups per call (for the gather's algorithmic bytes)
     rid = ple.ple_hash(batches[0][0], batches[0][1], torch.zeros((wl.S, 2), dtype=torch.int32, device=dev),
-                       torch.full((wl.S,), 2 if name == "decode" else 0, dtype=torch.int32, device=dev), wl.R)
-    lookups = int((rid >= 0).sum().item()) if name != "decode" else 2 * batches[0][0].numel()
-    unique_rows = int(torch.unique(rid[rid >= 0]).numel()) if name != "decode" else None
-    gather_bytes = lookups * GATHER_BYTES_PER_LOOKUP + tokens_per_call * GATHER_BYTES_PER_TOKEN
+                       torch.full((wl.S,), 2 if name == "decode" else 0, dtype=torch.int32, device=dev), wl.R,
+                       heads=heads)
+    n_ids = 16 if heads else 2
+    lookups = int((rid >= 0).sum().item()) if name != "decode" else n_ids * batches[0][0].numel()
+    if heads:   # distinct (head, row) pairs
+        key = rid.to(torch.int64) + torch.arange(16, device=dev, dtype=torch.int64)[None, :] * wl.R
+        unique_rows = int(torch.unique(key[rid >= 0]).numel()) if name != "decode" else None
+    else:
+        unique_rows = int(torch.unique(rid[rid >= 0]).numel()) if name != "decode" else None
+    if heads:
+        gather_bytes = lookups * HEADS_BYTES_PER_LOOKUP + tokens_per_call * HEADS_BYTES_PER_TOKEN
+    else:
+        gather_bytes = lookups * GATHER_BYTES_PER_LOOKUP + tokens_per_call * GATHER_BYTES_PER_TOKEN
     gather_gbs = gather_bytes / (stage_us[1] * 1e-6) / 1e9
     proj_flop = tokens_per_call * PROJ_FLOP_PER_TOKEN
     proj_tflops = proj_flop / (stage_us[2] * 1e-6) / 1e12
@@ -282,7 +309,7 @@ def main():
         roofline = {"kernel": "ple_gather_dequant (gather_kernel)", "bound": "hbm",
                     "achieved": round(gather_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(gather_gbs / HBM_PEAK_GBS, 4),
-                    "traffic": recorded_traffic("gather_kernel", name),
+                    "traffic": recorded_traffic("gather_heads_kernel" if heads else "gather_kernel", name),
                     "per_launch": {"bytes": gather_bytes, "avg_us": round(float(stage_us[1]), 2)}}
     else:
         k = ["ple_hash (hash_kernel)", "", "", "ple_gate_conv_fuse (fuse_kernel)"][dominant]
@@ -298,7 +325,8 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": describe(name, wl), "name": name, "tokens_per_step": tokens_per_step,
+        "config": {"workload": describe(name, wl, heads), "name": name, "layout": args.layout,
+                   "tokens_per_step": tokens_per_step,
                    "sequences": wl.S, "table_rows": wl.R, "table_bytes": wl.R * D},
         "roofline": roofline,
         "stages_us": {"hash": round(float(stage_us[0]), 2), "gather": round(float(stage_us[1]), 2),
@@ -309,7 +337,7 @@ def main():
                    "unit": "GB/s", "frac": round(gather_gbs / HBM_PEAK_GBS, 4),
                    "bytes_per_launch": gather_bytes, "lookups_per_launch": lookups,
                    "unique_rows_per_launch": unique_rows,
-                   "traffic": recorded_traffic("gather_kernel", name)},
+                   "traffic": recorded_traffic("gather_heads_kernel" if heads else "gather_kernel", name)},
         "proj": {"bound": "mfma", "achieved": round(proj_tflops, 2), "peak": BF16_PEAK_TFLOPS,
                  "unit": "TFLOP/s", "frac": round(proj_tflops / BF16_PEAK_TFLOPS, 4)},
         "fuse": {"bound": "hbm", "achieved": round(fuse_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -318,11 +346,11 @@ def main():
     }
     if not args.no_cpu_baseline and h0 is not None:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(wl, name, W, cw, h0, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(wl, name, W, cw, h0, args.cpu_budget, heads)
     elif not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         h0 = wl.hidden(0)
-        result["cpu_baseline"] = cpu_baseline(wl, name, W, cw, h0, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(wl, name, W, cw, h0, args.cpu_budget, heads)
     if args.copy_calibration:
         # a plain copy of known size: FETCH_SIZE / WRITE_SIZE of this dispatch
         # calibrate the per-kernel counters to bytes

@@ -158,6 +158,49 @@ int ple_forward_profiled(const ple_forward_args* args, void* stream, void* const
 /* Workspace bytes ple_forward needs for up to max_T tokens and max_S sequences. */
 size_t ple_forward_workspace_size(int64_t max_T, int32_t max_S);
 
+/* ---- The 16-lookup layout ------------------------------------------------
+ * The SSD-streaming page's model card ("技术细节") speaks of 16 lookups of
+ * 160-byte rows per token: the same 51,200,245,760-byte table read as 16
+ * head tables of R = 20,000,096 rows x 160 bytes. Reading fixed by this
+ * library where the pages are silent:
+ *  - heads 0..7 take the bigram key, heads 8..15 the trigram key (same keys
+ *    as above); head h's row = mix64(key + (h mod 8) * 0x9E3779B97F4A7C15)
+ *    mod R, the h-th output of a SplitMix64 stream started at the key (heads
+ *    0 and 8 equal ple_hash's two IDs); -1 when the n-gram is missing;
+ *  - one fp32 scale per (head, row), scales[h][r];
+ *  - x[t][160 h + j] = bf16_rne(fl32(dec(table[h][row_h][j]) * scales[h][row_h])),
+ *    +0 for a missing head row. The projection, gate, conv and fuse are the
+ *    same as above.
+ * Error bits, ownership and stream rules are those of the two-lookup calls. */
+
+/* a1, 16-lookup layout. As ple_hash, but
+ *   row_ids int32 [T][16] out  [t][h] row of head h, -1 if missing; 16-byte aligned */
+int ple_hash_heads(const int32_t* tokens, int64_t T, const int32_t* cu_seqlens, int32_t S,
+                   const int32_t* hist_ids, const int32_t* hist_len, int32_t vocab_size, int64_t R,
+                   int32_t* row_ids, int32_t* dev_err, void* stream);
+
+/* a2, 16-lookup layout.
+ *   row_ids int32 [T][16]             16-byte aligned
+ *   table   uint8 [16][R][160]        E4M3FN codes (the same bytes as [R][2560]); 16-byte aligned
+ *   scales  float [16][R]             one scale per head row
+ *   x_bf16  uint16 [T][2560]     out  x (formula above); 16-byte aligned
+ *   raw_opt uint8 [T][16][160]   out  optional: the 16 rows' bytes, zero for -1; 16-byte aligned
+ * Row ids outside [-1, R) are treated as -1 and flagged PLE_DEVERR_ROW_RANGE. */
+int ple_lookup_heads(const int32_t* row_ids, int64_t T, const uint8_t* table, const float* scales,
+                     int64_t R, uint16_t* x_bf16, uint8_t* raw_opt, int32_t* dev_err, void* stream);
+
+/* a1..a4 in the 16-lookup layout: ple_forward with `table` read as
+ * [16][R][160], `scales` as [16][R] (R = rows per head table), row_ids_out
+ * (optional) as int32 [T][16] (16-byte aligned), and a workspace of
+ * ple_forward_heads_workspace_size bytes. */
+int ple_forward_heads(const ple_forward_args* args, void* stream);
+
+/* ple_forward_heads with the five timing events of ple_forward_profiled. */
+int ple_forward_heads_profiled(const ple_forward_args* args, void* stream, void* const* events);
+
+/* Workspace bytes ple_forward_heads needs for up to max_T tokens and max_S sequences. */
+size_t ple_forward_heads_workspace_size(int64_t max_T, int32_t max_S);
+
 /* Static description of a status code. */
 const char* ple_status_string(int status);
 

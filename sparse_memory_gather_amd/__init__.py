@@ -61,7 +61,11 @@ class ForwardArgs(ctypes.Structure):
 _lib = None
 
 EXPORTS = ("ple_hash", "ple_lookup", "ple_proj", "ple_forward", "ple_forward_profiled",
-           "ple_forward_workspace_size", "ple_status_string", "ple_last_error")
+           "ple_forward_workspace_size", "ple_hash_heads", "ple_lookup_heads", "ple_forward_heads",
+           "ple_forward_heads_profiled", "ple_forward_heads_workspace_size", "ple_status_string",
+           "ple_last_error")
+HEADS = 16            # 16-lookup layout: head tables of 160-byte rows
+SLICE = D // HEADS
 
 
 def load_library(path: str = LIB_PATH):
@@ -74,18 +78,23 @@ def load_library(path: str = LIB_PATH):
         raise ImportError(f"libple is not built ({path} missing); run __graft_entry__.build()")
     lib = ctypes.CDLL(path)
     I32, I64 = ctypes.c_int32, ctypes.c_int64
-    lib.ple_hash.argtypes = [_P, I64, _P, I32, _P, _P, I32, I64, _P, _P, _P]
-    lib.ple_hash.restype = ctypes.c_int
-    lib.ple_lookup.argtypes = [_P, I64, _P, _P, I64, _P, _P, _P, _P]
-    lib.ple_lookup.restype = ctypes.c_int
+    for name in ("ple_hash", "ple_hash_heads"):
+        getattr(lib, name).argtypes = [_P, I64, _P, I32, _P, _P, I32, I64, _P, _P, _P]
+        getattr(lib, name).restype = ctypes.c_int
+    for name in ("ple_lookup", "ple_lookup_heads"):
+        getattr(lib, name).argtypes = [_P, I64, _P, _P, I64, _P, _P, _P, _P]
+        getattr(lib, name).restype = ctypes.c_int
     lib.ple_proj.argtypes = [_P, I64, _P, _P, _P]
     lib.ple_proj.restype = ctypes.c_int
-    lib.ple_forward.argtypes = [ctypes.POINTER(ForwardArgs), _P]
-    lib.ple_forward.restype = ctypes.c_int
-    lib.ple_forward_profiled.argtypes = [ctypes.POINTER(ForwardArgs), _P, ctypes.POINTER(_P)]
-    lib.ple_forward_profiled.restype = ctypes.c_int
-    lib.ple_forward_workspace_size.argtypes = [I64, I32]
-    lib.ple_forward_workspace_size.restype = ctypes.c_size_t
+    for name in ("ple_forward", "ple_forward_heads"):
+        getattr(lib, name).argtypes = [ctypes.POINTER(ForwardArgs), _P]
+        getattr(lib, name).restype = ctypes.c_int
+    for name in ("ple_forward_profiled", "ple_forward_heads_profiled"):
+        getattr(lib, name).argtypes = [ctypes.POINTER(ForwardArgs), _P, ctypes.POINTER(_P)]
+        getattr(lib, name).restype = ctypes.c_int
+    for name in ("ple_forward_workspace_size", "ple_forward_heads_workspace_size"):
+        getattr(lib, name).argtypes = [I64, I32]
+        getattr(lib, name).restype = ctypes.c_size_t
     lib.ple_status_string.argtypes = [ctypes.c_int]
     lib.ple_status_string.restype = ctypes.c_char_p
     lib.ple_last_error.argtypes = []
@@ -125,36 +134,62 @@ def _opt(t, name, dtype, shape):
     return None if t is None else _dev(t, name, dtype, shape)
 
 
-def workspace_size(max_T: int, max_S: int) -> int:
-    return int(load_library().ple_forward_workspace_size(max_T, max_S))
+def workspace_size(max_T: int, max_S: int, heads: bool = False) -> int:
+    lib = load_library()
+    f = lib.ple_forward_heads_workspace_size if heads else lib.ple_forward_workspace_size
+    return int(f(max_T, max_S))
+
+
+def _table(table, R: int):
+    """The table's bytes, [R][2560] or (16-lookup layout) [16][R][160]."""
+    if not isinstance(table, torch.Tensor) or table.numel() != R * D:
+        raise ValueError(f"table must hold R x 2560 = {R * D} bytes")
+    return _dev(table, "table", torch.uint8)
+
+
+def _rows_of(table, scales, heads: bool) -> int:
+    """R (rows, per head table in the 16-lookup layout) from the scales' shape."""
+    if heads:
+        if scales.dim() != 2 or scales.shape[0] != HEADS:
+            raise ValueError("scales must be float32 [16][R] in the 16-lookup layout")
+        return scales.shape[1]
+    return table.shape[0]
 
 
 def ple_hash(tokens, cu_seqlens, hist_ids, hist_len, R: int, vocab_size: int = DEFAULT_VOCAB,
-             row_ids=None, dev_err=None, stream=None):
-    """a1: row IDs int32 [T][2] (bigram, trigram; -1 when missing)."""
+             row_ids=None, dev_err=None, stream=None, heads: bool = False):
+    """a1: row IDs int32 [T][2] (bigram, trigram; -1 when missing), or
+    [T][16] in the 16-lookup layout (heads=True)."""
     T = tokens.numel()
     S = cu_seqlens.numel() - 1
+    n = HEADS if heads else 2
     if row_ids is None:
-        row_ids = torch.empty((T, 2), dtype=torch.int32, device=tokens.device)
-    _check(load_library().ple_hash(
+        row_ids = torch.empty((T, n), dtype=torch.int32, device=tokens.device)
+    lib = load_library()
+    _check((lib.ple_hash_heads if heads else lib.ple_hash)(
         _dev(tokens, "tokens", torch.int32, (T,)), T, _dev(cu_seqlens, "cu_seqlens", torch.int32, (S + 1,)),
         S, _dev(hist_ids, "hist_ids", torch.int32, (S, 2)), _dev(hist_len, "hist_len", torch.int32, (S,)),
-        vocab_size, R, _dev(row_ids, "row_ids", torch.int32, (T, 2)),
+        vocab_size, R, _dev(row_ids, "row_ids", torch.int32, (T, n)),
         _opt(dev_err, "dev_err", torch.int32, (1,)), _stream(stream)))
     return row_ids
 
 
-def ple_lookup(row_ids, table, scales, x=None, raw=None, dev_err=None, stream=None):
-    """a2: x bf16 [T][2560] = bf16(sum of the two dequantized rows)."""
+def ple_lookup(row_ids, table, scales, x=None, raw=None, dev_err=None, stream=None, heads: bool = False):
+    """a2: x bf16 [T][2560] = bf16(sum of the two dequantized rows); with
+    heads=True the 16-lookup layout (scales [16][R], row_ids [T][16], raw
+    [T][16][160])."""
     T = row_ids.shape[0]
-    R = table.shape[0]
+    R = _rows_of(table, scales, heads)
     if x is None:
         x = torch.empty((T, D), dtype=torch.bfloat16, device=row_ids.device)
-    _check(load_library().ple_lookup(
-        _dev(row_ids, "row_ids", torch.int32, (T, 2)), T, _dev(table, "table", torch.uint8, (R, D)),
-        _dev(scales, "scales", torch.float32, (R,)), R, _dev(x, "x", torch.bfloat16, (T, D)),
-        _opt(raw, "raw", torch.uint8, (T, 2, D)), _opt(dev_err, "dev_err", torch.int32, (1,)),
-        _stream(stream)))
+    lib = load_library()
+    n = HEADS if heads else 2
+    _check((lib.ple_lookup_heads if heads else lib.ple_lookup)(
+        _dev(row_ids, "row_ids", torch.int32, (T, n)), T, _table(table, R),
+        _dev(scales, "scales", torch.float32, (HEADS, R) if heads else (R,)), R,
+        _dev(x, "x", torch.bfloat16, (T, D)),
+        _opt(raw, "raw", torch.uint8, (T, HEADS, SLICE) if heads else (T, 2, D)),
+        _opt(dev_err, "dev_err", torch.int32, (1,)), _stream(stream)))
     return x
 
 
@@ -198,8 +233,8 @@ class Workspace:
         self.device = device
         self.buf = None
 
-    def get(self, T: int, S: int) -> torch.Tensor:
-        need = workspace_size(T, S)
+    def get(self, T: int, S: int, heads: bool = False) -> torch.Tensor:
+        need = workspace_size(T, S, heads)
         if self.buf is None or self.buf.numel() < need:
             self.buf = torch.empty((max(need, 256),), dtype=torch.uint8, device=self.device)
         return self.buf
@@ -207,23 +242,25 @@ class Workspace:
 
 def ple_forward(tokens, cu_seqlens, table, scales, W, conv_w, h, state: State, out=None,
                 workspace=None, vocab_size: int = DEFAULT_VOCAB, eps: float = DEFAULT_EPS,
-                dev_err=None, debug: bool = False, stream=None, events=None):
+                dev_err=None, debug: bool = False, stream=None, events=None, heads: bool = False):
     """a1..a4 for one chunk. Updates `state` in place; returns out (bf16
     [T][2560]) or, with debug=True, a dict with out, row_ids, x, e, gate, y.
     `events`: optional sequence of five hipEvent_t handles (ints) recorded
-    around the four kernels (ple_forward_profiled)."""
+    around the four kernels (ple_forward_profiled). heads=True: the 16-lookup
+    layout (scales [16][R], row_ids [T][16])."""
     T = tokens.numel()
     S = cu_seqlens.numel() - 1
-    R = table.shape[0]
+    R = _rows_of(table, scales, heads)
+    n = HEADS if heads else 2
     dev = tokens.device
     if out is None:
         out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
     if workspace is None:
         workspace = Workspace(dev)
-    ws = workspace.get(T, S) if isinstance(workspace, Workspace) else workspace
+    ws = workspace.get(T, S, heads) if isinstance(workspace, Workspace) else workspace
     dbg = {}
     if debug:
-        dbg = dict(row_ids=torch.empty((T, 2), dtype=torch.int32, device=dev),
+        dbg = dict(row_ids=torch.empty((T, n), dtype=torch.int32, device=dev),
                    x=torch.empty((T, D), dtype=torch.bfloat16, device=dev),
                    e=torch.empty((T, D), dtype=torch.float32, device=dev),
                    gate=torch.empty((T,), dtype=torch.float32, device=dev),
@@ -234,8 +271,8 @@ def ple_forward(tokens, cu_seqlens, table, scales, W, conv_w, h, state: State, o
     a.cu_seqlens = _dev(cu_seqlens, "cu_seqlens", torch.int32, (S + 1,))
     a.S = S
     a.vocab_size = vocab_size
-    a.table = _dev(table, "table", torch.uint8, (R, D))
-    a.scales = _dev(scales, "scales", torch.float32, (R,))
+    a.table = _table(table, R)
+    a.scales = _dev(scales, "scales", torch.float32, (HEADS, R) if heads else (R,))
     a.R = R
     a.W = _dev(W, "W", torch.bfloat16, (D, D))
     a.conv_w = _dev(conv_w, "conv_w", torch.bfloat16, (D, CONV_TAPS))
@@ -254,11 +291,13 @@ def ple_forward(tokens, cu_seqlens, table, scales, W, conv_w, h, state: State, o
         a.e_out = dbg["e"].data_ptr()
         a.gate_out = dbg["gate"].data_ptr()
         a.y_out = dbg["y"].data_ptr()
+    lib = load_library()
     if events is None:
-        _check(load_library().ple_forward(ctypes.byref(a), _stream(stream)))
+        _check((lib.ple_forward_heads if heads else lib.ple_forward)(ctypes.byref(a), _stream(stream)))
     else:
         ev = (_P * 5)(*[ctypes.c_void_p(int(e)) for e in events])
-        _check(load_library().ple_forward_profiled(ctypes.byref(a), _stream(stream), ev))
+        f = lib.ple_forward_heads_profiled if heads else lib.ple_forward_profiled
+        _check(f(ctypes.byref(a), _stream(stream), ev))
     if debug:
         dbg["out"] = out
         return dbg

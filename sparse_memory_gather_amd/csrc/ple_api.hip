@@ -73,10 +73,13 @@ struct WsLayout {
 
 size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
 
-WsLayout layout(int64_t T, int32_t S) {
+// row IDs per token: 2 (bigram, trigram) or 16 in the 16-lookup layout
+int ids_per_token(bool heads) { return heads ? 16 : 2; }
+
+WsLayout layout(int64_t T, int32_t S, bool heads) {
     WsLayout w{};
     size_t off = 0;
-    w.row_ids = off; off = up256(off + (size_t)T * 2 * sizeof(int32_t));
+    w.row_ids = off; off = up256(off + (size_t)T * ids_per_token(heads) * sizeof(int32_t));
     w.x = off;       off = up256(off + (size_t)T * kD * 2);
     w.e16 = off;     off = up256(off + (size_t)T * kD * 2);
     w.snap = off;    off = up256(off + (size_t)S * 3 * kD * sizeof(float));
@@ -116,12 +119,20 @@ const char* ple_last_error(void) { return g_last_error.c_str(); }
 
 size_t ple_forward_workspace_size(int64_t max_T, int32_t max_S) {
     if (max_T < 0 || max_S < 0) return 0;
-    return layout(max_T, max_S).total;
+    return layout(max_T, max_S, false).total;
 }
 
-int ple_hash(const int32_t* tokens, int64_t T, const int32_t* cu_seqlens, int32_t S,
-             const int32_t* hist_ids, const int32_t* hist_len, int32_t vocab_size, int64_t R,
-             int32_t* row_ids, int32_t* dev_err, void* stream) {
+size_t ple_forward_heads_workspace_size(int64_t max_T, int32_t max_S) {
+    if (max_T < 0 || max_S < 0) return 0;
+    return layout(max_T, max_S, true).total;
+}
+
+}  // extern "C"
+
+static int hash_impl(const int32_t* tokens, int64_t T, const int32_t* cu_seqlens, int32_t S,
+                     const int32_t* hist_ids, const int32_t* hist_len, int32_t vocab_size, int64_t R,
+                     int32_t* row_ids, int32_t* dev_err, void* stream, bool heads) {
+    const char* fn = heads ? "ple_hash_heads" : "ple_hash";
     if (T < 0) return fail(PLE_ERR_SHAPE, "T = %lld < 0", (long long)T);
     if (S < 1) return fail(PLE_ERR_SHAPE, "S = %d < 1", S);
     if (int st = check_R(R)) return st;
@@ -129,38 +140,71 @@ int ple_hash(const int32_t* tokens, int64_t T, const int32_t* cu_seqlens, int32_
         return fail(PLE_ERR_RANGE, "vocab_size = %d outside [1, 2^20]", vocab_size);
     if (T == 0) return ok();
     if (!tokens || !cu_seqlens || !hist_ids || !hist_len || !row_ids)
-        return fail(PLE_ERR_NULL, "ple_hash: a required pointer is NULL");
+        return fail(PLE_ERR_NULL, "%s: a required pointer is NULL", fn);
     if (!aligned(tokens, 4) || !aligned(cu_seqlens, 4) || !aligned(hist_ids, 4) ||
-        !aligned(hist_len, 4) || !aligned(row_ids, 8) || !aligned(dev_err, 4))
-        return fail(PLE_ERR_ALIGN, "ple_hash: misaligned pointer");
+        !aligned(hist_len, 4) || !aligned(row_ids, heads ? 16 : 8) || !aligned(dev_err, 4))
+        return fail(PLE_ERR_ALIGN, "%s: misaligned pointer", fn);
+    const size_t ids = (size_t)T * ids_per_token(heads) * 4;
     Range r[] = {rng("tokens", tokens, T * 4, false), rng("cu_seqlens", cu_seqlens, (S + 1) * 4ull, false),
                  rng("hist_ids", hist_ids, S * 8ull, false), rng("hist_len", hist_len, S * 4ull, false),
-                 rng("row_ids", row_ids, T * 8, true), rng("dev_err", dev_err, 4, true)};
+                 rng("row_ids", row_ids, ids, true), rng("dev_err", dev_err, 4, true)};
     if (int st = check_alias(r, 6)) return st;
     hipError_t e = launch_hash(tokens, T, cu_seqlens, S, hist_ids, hist_len, vocab_size, R, row_ids,
-                               dev_err, nullptr, nullptr, reinterpret_cast<hipStream_t>(stream));
-    if (int st = hip_status(e, "ple_hash launch")) return st;
+                               dev_err, nullptr, nullptr, heads, reinterpret_cast<hipStream_t>(stream));
+    if (int st = hip_status(e, heads ? "ple_hash_heads launch" : "ple_hash launch")) return st;
     return ok();
 }
 
-int ple_lookup(const int32_t* row_ids, int64_t T, const uint8_t* table, const float* scales,
-               int64_t R, uint16_t* x_bf16, uint8_t* raw_opt, int32_t* dev_err, void* stream) {
+static int lookup_impl(const int32_t* row_ids, int64_t T, const uint8_t* table, const float* scales,
+                       int64_t R, uint16_t* x_bf16, uint8_t* raw_opt, int32_t* dev_err, void* stream,
+                       bool heads) {
+    const char* fn = heads ? "ple_lookup_heads" : "ple_lookup";
     if (T < 0) return fail(PLE_ERR_SHAPE, "T = %lld < 0", (long long)T);
     if (int st = check_R(R)) return st;
     if (T == 0) return ok();
     if (!row_ids || !table || !scales || !x_bf16)
-        return fail(PLE_ERR_NULL, "ple_lookup: a required pointer is NULL");
-    if (!aligned(row_ids, 8) || !aligned(table, 16) || !aligned(scales, 4) || !aligned(x_bf16, 16) ||
-        !aligned(raw_opt, 16) || !aligned(dev_err, 4))
-        return fail(PLE_ERR_ALIGN, "ple_lookup: misaligned pointer");
-    Range r[] = {rng("row_ids", row_ids, T * 8, false), rng("table", table, (size_t)R * kD, false),
-                 rng("scales", scales, (size_t)R * 4, false), rng("x", x_bf16, (size_t)T * kD * 2, true),
-                 rng("raw", raw_opt, (size_t)T * 2 * kD, true), rng("dev_err", dev_err, 4, true)};
+        return fail(PLE_ERR_NULL, "%s: a required pointer is NULL", fn);
+    if (!aligned(row_ids, heads ? 16 : 8) || !aligned(table, 16) || !aligned(scales, 4) ||
+        !aligned(x_bf16, 16) || !aligned(raw_opt, 16) || !aligned(dev_err, 4))
+        return fail(PLE_ERR_ALIGN, "%s: misaligned pointer", fn);
+    // both layouts: R x 2560 table bytes (16 x R x 160), raw T x 2560 x (2 or 1) bytes
+    const size_t n_scales = (size_t)R * (heads ? 16 : 1);
+    Range r[] = {rng("row_ids", row_ids, (size_t)T * ids_per_token(heads) * 4, false),
+                 rng("table", table, (size_t)R * kD, false), rng("scales", scales, n_scales * 4, false),
+                 rng("x", x_bf16, (size_t)T * kD * 2, true),
+                 rng("raw", raw_opt, (size_t)T * kD * (heads ? 1 : 2), true), rng("dev_err", dev_err, 4, true)};
     if (int st = check_alias(r, 6)) return st;
-    hipError_t e = launch_gather(row_ids, T, table, scales, R, x_bf16, raw_opt, dev_err,
-                                 reinterpret_cast<hipStream_t>(stream));
-    if (int st = hip_status(e, "ple_lookup launch")) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = heads ? launch_gather_heads(row_ids, T, table, scales, R, x_bf16, raw_opt, dev_err, s)
+                         : launch_gather(row_ids, T, table, scales, R, x_bf16, raw_opt, dev_err, s);
+    if (int st = hip_status(e, heads ? "ple_lookup_heads launch" : "ple_lookup launch")) return st;
     return ok();
+}
+
+extern "C" {
+
+int ple_hash(const int32_t* tokens, int64_t T, const int32_t* cu_seqlens, int32_t S,
+             const int32_t* hist_ids, const int32_t* hist_len, int32_t vocab_size, int64_t R,
+             int32_t* row_ids, int32_t* dev_err, void* stream) {
+    return hash_impl(tokens, T, cu_seqlens, S, hist_ids, hist_len, vocab_size, R, row_ids, dev_err, stream,
+                     false);
+}
+
+int ple_hash_heads(const int32_t* tokens, int64_t T, const int32_t* cu_seqlens, int32_t S,
+                   const int32_t* hist_ids, const int32_t* hist_len, int32_t vocab_size, int64_t R,
+                   int32_t* row_ids, int32_t* dev_err, void* stream) {
+    return hash_impl(tokens, T, cu_seqlens, S, hist_ids, hist_len, vocab_size, R, row_ids, dev_err, stream,
+                     true);
+}
+
+int ple_lookup(const int32_t* row_ids, int64_t T, const uint8_t* table, const float* scales,
+               int64_t R, uint16_t* x_bf16, uint8_t* raw_opt, int32_t* dev_err, void* stream) {
+    return lookup_impl(row_ids, T, table, scales, R, x_bf16, raw_opt, dev_err, stream, false);
+}
+
+int ple_lookup_heads(const int32_t* row_ids, int64_t T, const uint8_t* table, const float* scales,
+                     int64_t R, uint16_t* x_bf16, uint8_t* raw_opt, int32_t* dev_err, void* stream) {
+    return lookup_impl(row_ids, T, table, scales, R, x_bf16, raw_opt, dev_err, stream, true);
 }
 
 int ple_proj(const uint16_t* x_bf16, int64_t T, const uint16_t* W_bf16, float* e, void* stream) {
@@ -178,7 +222,9 @@ int ple_proj(const uint16_t* x_bf16, int64_t T, const uint16_t* W_bf16, float* e
     return ok();
 }
 
-static int forward_impl(const ple_forward_args* a, void* stream, void* const* events) {
+}  // extern "C"
+
+static int forward_impl(const ple_forward_args* a, void* stream, void* const* events, bool heads) {
     if (!a) return fail(PLE_ERR_NULL, "ple_forward: args is NULL");
     const int64_t T = a->T;
     const int32_t S = a->S;
@@ -193,14 +239,14 @@ static int forward_impl(const ple_forward_args* a, void* stream, void* const* ev
         !a->out || !a->hist_ids || !a->hist_len || !a->conv_state)
         return fail(PLE_ERR_NULL, "ple_forward: a required pointer is NULL");
     if (!a->workspace) return fail(PLE_ERR_WORKSPACE, "ple_forward: workspace is NULL");
-    const WsLayout L = layout(T, S);
+    const WsLayout L = layout(T, S, heads);
     if (a->workspace_bytes < L.total)
         return fail(PLE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", a->workspace_bytes, L.total);
     if (!aligned(a->tokens, 4) || !aligned(a->cu_seqlens, 4) || !aligned(a->table, 16) ||
         !aligned(a->scales, 4) || !aligned(a->W, 16) || !aligned(a->conv_w, 16) || !aligned(a->h, 16) ||
         !aligned(a->out, 16) || !aligned(a->hist_ids, 4) || !aligned(a->hist_len, 4) ||
         !aligned(a->conv_state, 16) || !aligned(a->workspace, 256) || !aligned(a->dev_err, 4) ||
-        !aligned(a->row_ids_out, 8) || !aligned(a->x_out, 16) || !aligned(a->e_out, 16) ||
+        !aligned(a->row_ids_out, heads ? 16 : 8) || !aligned(a->x_out, 16) || !aligned(a->e_out, 16) ||
         !aligned(a->gate_out, 4) || !aligned(a->y_out, 16))
         return fail(PLE_ERR_ALIGN, "ple_forward: misaligned pointer");
     const size_t act = (size_t)T * kD * 2;
@@ -208,7 +254,7 @@ static int forward_impl(const ple_forward_args* a, void* stream, void* const* ev
         rng("tokens", a->tokens, T * 4, false),
         rng("cu_seqlens", a->cu_seqlens, (S + 1) * 4ull, false),
         rng("table", a->table, (size_t)a->R * kD, false),
-        rng("scales", a->scales, (size_t)a->R * 4, false),
+        rng("scales", a->scales, (size_t)a->R * (heads ? 16 : 1) * 4, false),
         rng("W", a->W, (size_t)kD * kD * 2, false),
         rng("conv_w", a->conv_w, (size_t)kD * kTaps * 2, false),
         rng("h", a->h, act, false),
@@ -218,7 +264,7 @@ static int forward_impl(const ple_forward_args* a, void* stream, void* const* ev
         rng("conv_state", a->conv_state, (size_t)S * 3 * kD * 4, true),
         rng("workspace", a->workspace, L.total, true),
         rng("dev_err", a->dev_err, 4, true),
-        rng("row_ids_out", a->row_ids_out, T * 8, true),
+        rng("row_ids_out", a->row_ids_out, (size_t)T * ids_per_token(heads) * 4, true),
         rng("x_out", a->x_out, act, true),
         rng("e_out", a->e_out, (size_t)T * kD * 4, true),
         rng("gate_out", a->gate_out, T * 4, true),
@@ -239,10 +285,11 @@ static int forward_impl(const ple_forward_args* a, void* stream, void* const* ev
     hipError_t e = mark(0);
     if (int st = hip_status(e, "ple_forward: event record")) return st;
     e = launch_hash(a->tokens, T, a->cu_seqlens, S, a->hist_ids, a->hist_len, a->vocab_size,
-                    a->R, row_ids, a->dev_err, a->conv_state, snap, s);
+                    a->R, row_ids, a->dev_err, a->conv_state, snap, heads, s);
     if (int st = hip_status(e, "ple_forward: hash launch")) return st;
     if (int st = hip_status(mark(1), "ple_forward: event record")) return st;
-    e = launch_gather(row_ids, T, a->table, a->scales, a->R, x, nullptr, a->dev_err, s);
+    e = heads ? launch_gather_heads(row_ids, T, a->table, a->scales, a->R, x, nullptr, a->dev_err, s)
+              : launch_gather(row_ids, T, a->table, a->scales, a->R, x, nullptr, a->dev_err, s);
     if (int st = hip_status(e, "ple_forward: gather launch")) return st;
     if (int st = hip_status(mark(2), "ple_forward: event record")) return st;
     e = launch_proj(x, T, a->W, a->e_out, e16, s);
@@ -255,13 +302,29 @@ static int forward_impl(const ple_forward_args* a, void* stream, void* const* ev
     return ok();
 }
 
-int ple_forward(const ple_forward_args* a, void* stream) { return forward_impl(a, stream, nullptr); }
+static int check_events(void* const* events) {
+    if (!events) return fail(PLE_ERR_NULL, "profiled forward: events is NULL");
+    for (int i = 0; i < 5; ++i)
+        if (!events[i]) return fail(PLE_ERR_NULL, "profiled forward: events[%d] is NULL", i);
+    return PLE_OK;
+}
+
+extern "C" {
+
+int ple_forward(const ple_forward_args* a, void* stream) { return forward_impl(a, stream, nullptr, false); }
 
 int ple_forward_profiled(const ple_forward_args* a, void* stream, void* const* events) {
-    if (!events) return fail(PLE_ERR_NULL, "ple_forward_profiled: events is NULL");
-    for (int i = 0; i < 5; ++i)
-        if (!events[i]) return fail(PLE_ERR_NULL, "ple_forward_profiled: events[%d] is NULL", i);
-    return forward_impl(a, stream, events);
+    if (int st = check_events(events)) return st;
+    return forward_impl(a, stream, events, false);
+}
+
+int ple_forward_heads(const ple_forward_args* a, void* stream) {
+    return forward_impl(a, stream, nullptr, true);
+}
+
+int ple_forward_heads_profiled(const ple_forward_args* a, void* stream, void* const* events) {
+    if (int st = check_events(events)) return st;
+    return forward_impl(a, stream, events, true);
 }
 
 }  // extern "C"

@@ -9,6 +9,12 @@
 //   bigram  key (2<<60)|(a<<20)|b,  trigram key (3<<60)|(a<<40)|(b<<20)|c
 // with the SplitMix64 finalizer, reduced mod R (unsigned 64-bit). Missing
 // history gives -1.
+//
+// The 16-lookup layout (the model card's 16 lookups of 160-byte rows, SSD
+// streaming page, "技术细节") writes 16 IDs per token: heads 0..7 on the
+// bigram key, heads 8..15 on the trigram key, head h finalizing
+// key + (h mod 8) * 0x9E3779B97F4A7C15 (the h-th SplitMix64 output from the
+// key), so heads 0 and 8 equal the two-lookup IDs.
 #include "ple_kernels.h"
 
 namespace ple {
@@ -21,7 +27,10 @@ __device__ __forceinline__ uint64_t splitmix_finalize(uint64_t z) {
 }
 
 constexpr int kHashBlock = 256;
+constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ULL;
 
+// kHeads = 0: two IDs per token (bigram, trigram); 16: the 16-lookup layout
+template <int kHeads>
 __global__ void __launch_bounds__(kHashBlock)
 hash_kernel(const int32_t* __restrict__ tokens, int64_t T, const int32_t* __restrict__ cu, int32_t S,
             const int32_t* __restrict__ hist_ids, const int32_t* __restrict__ hist_len,
@@ -68,17 +77,27 @@ hash_kernel(const int32_t* __restrict__ tokens, int64_t T, const int32_t* __rest
         return (uint32_t)v & 0xFFFFFu;
     };
     const uint32_t c = seq_at(j);
-    int32_t r2 = -1, r3 = -1;
+    uint64_t k2 = 0, k3 = 0;
     if (j >= 1) {
         const uint32_t b = seq_at(j - 1);
-        r2 = (int32_t)(splitmix_finalize((2ULL << 60) | ((uint64_t)b << 20) | c) % R);
-        if (j >= 2) {
-            const uint32_t a = seq_at(j - 2);
-            r3 = (int32_t)(splitmix_finalize((3ULL << 60) | ((uint64_t)a << 40) |
-                                             ((uint64_t)b << 20) | c) % R);
-        }
+        k2 = (2ULL << 60) | ((uint64_t)b << 20) | c;
+        if (j >= 2) k3 = (3ULL << 60) | ((uint64_t)seq_at(j - 2) << 40) | ((uint64_t)b << 20) | c;
     }
-    reinterpret_cast<int2*>(row_ids)[t] = make_int2(r2, r3);
+    if (kHeads == 0) {
+        const int32_t r2 = j >= 1 ? (int32_t)(splitmix_finalize(k2) % R) : -1;
+        const int32_t r3 = j >= 2 ? (int32_t)(splitmix_finalize(k3) % R) : -1;
+        reinterpret_cast<int2*>(row_ids)[t] = make_int2(r2, r3);
+    } else {
+        int32_t id[16];
+#pragma unroll
+        for (int h = 0; h < 8; ++h) {
+            id[h] = j >= 1 ? (int32_t)(splitmix_finalize(k2 + (uint64_t)h * kGamma) % R) : -1;
+            id[8 + h] = j >= 2 ? (int32_t)(splitmix_finalize(k3 + (uint64_t)h * kGamma) % R) : -1;
+        }
+        int4* dst = reinterpret_cast<int4*>(row_ids + t * 16);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dst[q] = make_int4(id[4 * q], id[4 * q + 1], id[4 * q + 2], id[4 * q + 3]);
+    }
 }
 
 }  // namespace
@@ -86,16 +105,21 @@ hash_kernel(const int32_t* __restrict__ tokens, int64_t T, const int32_t* __rest
 hipError_t launch_hash(const int32_t* tokens, int64_t T, const int32_t* cu, int32_t S,
                        const int32_t* hist_ids, const int32_t* hist_len, int32_t vocab, int64_t R,
                        int32_t* row_ids, int32_t* dev_err, const float* conv_state,
-                       float* state_snap, hipStream_t stream) {
+                       float* state_snap, bool heads, hipStream_t stream) {
     int64_t blocks = (T + kHashBlock - 1) / kHashBlock;
     if (blocks < 1) blocks = 1;
     int64_t snap_vec4 = state_snap ? (int64_t)S * 3 * kD / 4 : 0;
     int64_t snap_blocks = (snap_vec4 + kHashBlock - 1) / kHashBlock;
     if (snap_blocks > blocks) blocks = snap_blocks < 65536 ? snap_blocks : 65536;
     dim3 grid((unsigned)blocks, state_snap ? 2 : 1);
-    hipLaunchKernelGGL(hash_kernel, grid, dim3(kHashBlock), 0, stream, tokens, T, cu, S, hist_ids,
-                       hist_len, vocab, (uint64_t)R, row_ids, dev_err, conv_state, state_snap,
-                       snap_vec4);
+    if (heads)
+        hipLaunchKernelGGL(hash_kernel<16>, grid, dim3(kHashBlock), 0, stream, tokens, T, cu, S, hist_ids,
+                           hist_len, vocab, (uint64_t)R, row_ids, dev_err, conv_state, state_snap,
+                           snap_vec4);
+    else
+        hipLaunchKernelGGL(hash_kernel<0>, grid, dim3(kHashBlock), 0, stream, tokens, T, cu, S, hist_ids,
+                           hist_len, vocab, (uint64_t)R, row_ids, dev_err, conv_state, state_snap,
+                           snap_vec4);
     return hipGetLastError();
 }
 

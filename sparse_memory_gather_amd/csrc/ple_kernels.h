@@ -30,13 +30,19 @@ __device__ __forceinline__ void flag_error(int32_t* dev_err, int bit) {
 
 // ---- launchers (each returns hipGetLastError()) ----------------------------
 
-// n-gram IDs for T tokens; optionally also copies conv_state [S][3][kD] into
-// state_snap (the fused path reads the old state from the copy while it
-// rewrites conv_state in place).
+// n-gram IDs for T tokens (2 per token, or 16 with heads); optionally also
+// copies conv_state [S][3][kD] into state_snap (the fused path reads the old
+// state from the copy while it rewrites conv_state in place).
 hipError_t launch_hash(const int32_t* tokens, int64_t T, const int32_t* cu, int32_t S,
                        const int32_t* hist_ids, const int32_t* hist_len, int32_t vocab, int64_t R,
                        int32_t* row_ids, int32_t* dev_err, const float* conv_state,
-                       float* state_snap, hipStream_t stream);
+                       float* state_snap, bool heads, hipStream_t stream);
+
+// 16-lookup layout: table [16][R][160], scales [16][R], row_ids [T][16],
+// raw (optional) [T][16][160].
+hipError_t launch_gather_heads(const int32_t* row_ids, int64_t T, const uint8_t* table,
+                               const float* scales, int64_t R, uint16_t* x, uint8_t* raw,
+                               int32_t* dev_err, hipStream_t stream);
 
 hipError_t launch_gather(const int32_t* row_ids, int64_t T, const uint8_t* table,
                          const float* scales, int64_t R, uint16_t* x, uint8_t* raw,

@@ -79,7 +79,12 @@ def y_bound(ref: dict, cu, cw, state, W) -> np.ndarray:
     return ydv + Y_FP32 * yabs + 1e-7
 
 
-def oracle_samples(seqs, samples, W, cw, R, eps=1e-6):
+def head_rows(R: int):
+    """Row source of the 16-lookup layout for oracle.forward_heads."""
+    return lambda hs, rs: table.slices_cpu(hs, rs, R)
+
+
+def oracle_samples(seqs, samples, W, cw, R, eps=1e-6, heads: bool = False):
     """Reference outputs of sampled tokens.
 
     seqs: list of (tokens int32[n], h bf16 bits [n][D]) — whole sequences
@@ -103,9 +108,9 @@ def oracle_samples(seqs, samples, W, cw, R, eps=1e-6):
         hid.append(hist)
         hln.append(k)
     S = len(samples)
-    r = oracle.forward(np.concatenate(toks), np.array(cu, np.int32), np.concatenate(hs), W, cw, R,
-                       rows, np.array(hid, np.int32), np.array(hln, np.int32),
-                       np.zeros((S, 3, D)), eps)
+    fwd, src = (oracle.forward_heads, head_rows(R)) if heads else (oracle.forward, rows)
+    r = fwd(np.concatenate(toks), np.array(cu, np.int32), np.concatenate(hs), W, cw, R,
+            src, np.array(hid, np.int32), np.array(hln, np.int32), np.zeros((S, 3, D)), eps)
     last = np.array(cu[1:]) - 1
     # y tolerance from the (up to) four taps that feed each sample; taps
     # before a sequence start are zero on both sides

@@ -155,3 +155,29 @@ def test_decode_steps_after_history(dev, full_table, dev_weights, weights):
     ref = oracle_samples(seqs, samples, W, cw, wl.R)
     got = {key: np.concatenate([steps[k][2][key] for k in check_k]) for key in steps[0][2]}
     print("decode", check_samples(got, ref, W, "decode"))
+
+
+def test_prefill_heads_layout(dev, full_table, dev_weights, weights):
+    # the 16-lookup layout on the same 51.2 GB of table bytes: 16 head tables
+    # of 20,000,096 rows x 160 bytes, 16 x 20,000,096 scales
+    W, cw = weights
+    tab, _ = full_table
+    R = inputs.R_FULL
+    sc16 = table.head_scales_gpu(R, device=dev)
+    rng = np.random.default_rng(15)
+    hs, rs = rng.integers(0, 16, 500), rng.integers(0, R, 500)
+    _, want = table.slices_cpu(hs, rs, R)
+    assert np.array_equal(sc16[torch.as_tensor(hs, device=dev), torch.as_tensor(rs, device=dev)].cpu().numpy(),
+                          want)
+    wl = inputs.make_workload("prefill")
+    toks, cu = wl.chunks[0]
+    h = wl.hidden(0)
+    st = ple.State(1, dev)
+    res = ple.ple_forward(dev_i32(toks, dev), dev_i32(cu, dev), tab, sc16, dev_weights[0], dev_weights[1],
+                          dev_bf16(h, dev), st, debug=True, heads=True)
+    ref_ids = oracle.ngram_ids_heads(toks, cu, np.zeros((1, 2), np.int32), np.zeros(1, np.int32), R)
+    assert np.array_equal(res["row_ids"].cpu().numpy(), ref_ids)
+    pos = sorted(set([0, 1, 2, 3, len(toks) - 1] + _interior(rng, 4, len(toks) - 1, 8)))
+    ref = oracle_samples([(toks, h)], [(0, p) for p in pos], W, cw, R, heads=True)
+    print("prefill heads", check_samples(gather_debug(res, pos), ref, W, "prefill heads"))
+    del sc16

@@ -10,7 +10,7 @@ import oracle
 import sparse_memory_gather_amd as ple
 from gen import inputs, table
 
-from parity_util import (D, check_samples, dev_bf16, dev_i32, e_bound, gather_debug, host_bits,
+from parity_util import (D, check_samples, dev_bf16, dev_i32, e_bound, gather_debug, head_rows, host_bits,
                          oracle_samples, rows, y_bound, E_REL, OUT_ATOL, OUT_RTOL)
 
 pytestmark = pytest.mark.gpu
@@ -255,3 +255,93 @@ def test_save_restore_state_resumes_identically(dev, small_table, dev_weights):
     b = _forward(dev, tab, sc, dev_weights, toks[32:], cu, h[32:], saved)
     assert np.array_equal(host_bits(a["out"]), host_bits(b["out"]))
     assert torch.equal(st.conv_state, saved.conv_state)
+
+
+# ---------------------------------------------------------------------------
+# 16-lookup layout (16 head tables of 160-byte rows)
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def small_head_scales(dev):
+    return table.head_scales_gpu(R_SMALL, device=dev)
+
+
+def test_heads_scales_generator_gpu_matches_cpu(dev, small_head_scales):
+    rng = np.random.default_rng(50)
+    hs, rs = rng.integers(0, 16, 3000), rng.integers(0, R_SMALL, 3000)
+    _, want = table.slices_cpu(hs, rs, R_SMALL)
+    got = small_head_scales[torch.as_tensor(hs, device=dev), torch.as_tensor(rs, device=dev)].cpu().numpy()
+    assert np.array_equal(got, want)
+
+
+def test_heads_hash_lookup_bit_exact(dev, small_table, small_head_scales):
+    tab, _ = small_table
+    lengths = [0, 1, 2, 3, 5, 129, 1, 300]
+    hl = [2, 0, 1, 2, 0, 1, 2, 0]
+    toks, cu, hist, hlen, _ = _case(51, lengths, hl)
+    rid = ple.ple_hash(dev_i32(toks, dev), dev_i32(cu, dev), dev_i32(hist, dev), dev_i32(hlen, dev),
+                       R_SMALL, heads=True)
+    ref_ids = oracle.ngram_ids_heads(toks, cu, hist, hlen, R_SMALL)
+    assert np.array_equal(rid.cpu().numpy(), ref_ids)
+    T = len(toks)
+    raw = torch.empty((T, 16, 160), dtype=torch.uint8, device=dev)
+    x = ple.ple_lookup(rid, tab, small_head_scales, raw=raw, heads=True)
+    heads = np.broadcast_to(np.arange(16), ref_ids.shape)
+    valid = ref_ids >= 0
+    q = heads[valid] * R_SMALL + ref_ids[valid]
+    uniq, inv = np.unique(q, return_inverse=True)
+    codes, scales = head_rows(R_SMALL)(uniq // R_SMALL, uniq % R_SMALL)
+    compact = np.full(ref_ids.shape, -1, np.int32)
+    compact[valid] = inv
+    want_x, want_raw = oracle.gather_dequant_heads(compact, codes, scales, raw=True)
+    assert np.array_equal(raw.cpu().numpy(), want_raw)
+    assert np.array_equal(host_bits(x), want_x)
+
+
+def test_heads_lookup_out_of_range_ids_flagged_and_zero(dev, small_table, small_head_scales):
+    tab, _ = small_table
+    ids = np.full((4, 16), 7, np.int32)
+    ids[1, 3] = R_SMALL          # out of range -> treated as missing, flagged
+    ids[2, 15] = -5              # below -1 -> same
+    ids[3, :] = -1               # all missing -> x = +0
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    x = host_bits(ple.ple_lookup(dev_i32(ids, dev), tab, small_head_scales, dev_err=err, heads=True))
+    assert err.item() & 8
+    assert np.all(x[1, 480:640] == 0) and np.all(x[2, 2400:2560] == 0) and np.all(x[3] == 0)
+    assert np.any(x[1, :480] != 0)
+
+
+def test_heads_forward_parity_with_edge_cases(dev, small_table, small_head_scales, dev_weights, weights):
+    W, cw = weights
+    tab, _ = small_table
+    lengths = [1, 2, 3, 40, 300, 4]
+    hl = [0, 1, 2, 2, 0, 1]
+    toks, cu, hist, hlen, h = _case(52, lengths, hl)
+    S = len(lengths)
+    st = ple.State(S, dev)
+    st.hist_ids.copy_(dev_i32(hist, dev))
+    st.hist_len.copy_(dev_i32(hlen, dev))
+    res = ple.ple_forward(dev_i32(toks, dev), dev_i32(cu, dev), tab, small_head_scales, dev_weights[0],
+                          dev_weights[1], dev_bf16(h, dev), st, debug=True, heads=True)
+    ref = oracle.forward_heads(toks, cu, h, W, cw, R_SMALL, head_rows(R_SMALL), hist, hlen)
+    got = gather_debug(res, np.arange(len(toks)))
+    assert np.array_equal(got["row_ids"], ref["row_ids"])
+    assert np.array_equal(got["x"], ref["x"])
+    out = inputs.bf16_bits_to_f32(got["out"]).astype(np.float64)
+    assert np.all(np.abs(out - ref["out"]) <= OUT_ATOL + OUT_RTOL * np.abs(ref["out"]))
+    assert np.all(np.abs(got["g"] - ref["g"]) <= 1e-4)
+    assert np.all(np.abs(got["y"] - ref["y"]) <= y_bound(ref, cu, cw, np.zeros((S, 3, D)), W))
+    assert np.array_equal(st.hist_len.cpu().numpy(), ref["hist_len"])
+    np.testing.assert_allclose(st.conv_state.cpu().numpy(), ref["conv_state"], rtol=2e-2, atol=1e-4)
+    # tokens whose four conv taps lie in this chunk, through the shared checker
+    # (e, bf16 flips, g, y, out); each becomes its own short oracle segment
+    seqs, samples, idx = [], [], []
+    for s in range(S):
+        a, b = int(cu[s]), int(cu[s + 1])
+        full = np.concatenate([hist[s][2 - hl[s]:], toks[a:b]]).astype(np.int32)
+        hh = np.concatenate([np.zeros((hl[s], D), np.uint16), h[a:b]])
+        seqs.append((full, hh))
+        samples += [(s, hl[s] + p) for p in range(3, b - a)]
+        idx += [a + p for p in range(3, b - a)]
+    refs = oracle_samples(seqs, samples, W, cw, R_SMALL, heads=True)
+    check_samples(gather_debug(res, idx), refs, W, "heads")
