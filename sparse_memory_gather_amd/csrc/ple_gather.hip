@@ -95,60 +95,74 @@ gather_kernel(const int32_t* __restrict__ row_ids, int64_t T, const uint8_t* __r
 
 // 16-lookup layout: the table as 16 head tables of R rows x 160 bytes and
 // one scale per (head, row). Head h's row fills x columns 160h .. 160h+159;
-// a missing n-gram leaves its heads' columns +0. One wave per token, the
-// same five 512-element spans as above: lane l of span s covers elements
-// 512s + 8l .. +7, which lie in one head (160 is a multiple of 8); lanes
-// 0..15 load the token's 16 row IDs and scales and the others take theirs
-// with a lane shuffle.
+// a missing n-gram leaves its heads' columns +0. One wave per token (two
+// tokens per wave, all loads issued first, measured slower), the same five
+// 512-element spans as above: lane l of span s covers elements 512s + 8l .. +7, which
+// lie in one head (160 is a multiple of 8); lanes 0..15 load a token's 16 row
+// IDs and scales and the others take theirs with a lane shuffle.
+constexpr int kHeadTokPerWave = 1;
+
 __global__ void __launch_bounds__(64 * kTokPerBlock)
 gather_heads_kernel(const int32_t* __restrict__ row_ids, int64_t T, const uint8_t* __restrict__ table,
                     const float* __restrict__ scales, int64_t R, uint16_t* __restrict__ x,
                     uint8_t* __restrict__ raw, int32_t* dev_err) {
 #pragma clang fp contract(off)
     const int lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
-    if (t >= T) return;
-    int my_id = -1;
-    float my_scale = 0.0f;
-    if (lane < 16) {
-        int r = row_ids[t * 16 + lane];
-        if (r < -1 || (int64_t)r >= R) {
-            flag_error(dev_err, 8);
-            r = -1;
-        }
-        my_id = r;
-        if (r >= 0) my_scale = scales[(int64_t)lane * R + r];
-    }
-    u32x2 a[kSpans];
-    float sc[kSpans];
-    bool ok[kSpans];
+    const int64_t t0 = ((int64_t)blockIdx.x * kTokPerBlock + (threadIdx.x >> 6)) * kHeadTokPerWave;
+    if (t0 >= T) return;
+    u32x2 a[kHeadTokPerWave][kSpans];
+    float sc[kHeadTokPerWave][kSpans];
+    bool ok[kHeadTokPerWave][kSpans];
     int head[kSpans], off[kSpans];
 #pragma unroll
     for (int s = 0; s < kSpans; ++s) {
         const int e0 = 512 * s + 8 * lane;
         head[s] = e0 / 160;
         off[s] = e0 - 160 * head[s];
-        const int r = __shfl(my_id, head[s]);
-        sc[s] = __shfl(my_scale, head[s]);
-        ok[s] = r >= 0;
-        const u32x2 z = {0u, 0u};
-        a[s] = ok[s] ? *reinterpret_cast<const u32x2*>(table + ((int64_t)head[s] * R + r) * 160 + off[s]) : z;
     }
-    u32x4* xrow = reinterpret_cast<u32x4*>(x + t * kD) + lane;
 #pragma unroll
-    for (int s = 0; s < kSpans; ++s) {
-        float p[8];
-        decode8(a[s], sc[s], p);
-        u32x4 o;
+    for (int k = 0; k < kHeadTokPerWave; ++k) {
+        const int64_t t = t0 + k;
+        int my_id = -1;
+        float my_scale = 0.0f;
+        if (lane < 16 && t < T) {
+            int r = row_ids[t * 16 + lane];
+            if (r < -1 || (int64_t)r >= R) {
+                flag_error(dev_err, 8);
+                r = -1;
+            }
+            my_id = r;
+            if (r >= 0) my_scale = scales[(int64_t)lane * R + r];
+        }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            o[i] = ok[s] ? pack_bf16x2(p[2 * i], p[2 * i + 1]) : 0u;
-        __builtin_nontemporal_store(o, xrow + s * 64);
+        for (int s = 0; s < kSpans; ++s) {
+            const int r = __shfl(my_id, head[s]);
+            sc[k][s] = __shfl(my_scale, head[s]);
+            ok[k][s] = r >= 0;
+            const u32x2 z = {0u, 0u};
+            a[k][s] = ok[k][s] ? *reinterpret_cast<const u32x2*>(table + ((int64_t)head[s] * R + r) * 160 + off[s])
+                               : z;
+        }
     }
-    if (raw) {
 #pragma unroll
-        for (int s = 0; s < kSpans; ++s)
-            *reinterpret_cast<u32x2*>(raw + (t * 16 + head[s]) * 160 + off[s]) = a[s];
+    for (int k = 0; k < kHeadTokPerWave; ++k) {
+        const int64_t t = t0 + k;
+        if (t >= T) break;
+        u32x4* xrow = reinterpret_cast<u32x4*>(x + t * kD) + lane;
+#pragma unroll
+        for (int s = 0; s < kSpans; ++s) {
+            float p[8];
+            decode8(a[k][s], sc[k][s], p);
+            u32x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = ok[k][s] ? pack_bf16x2(p[2 * i], p[2 * i + 1]) : 0u;
+            __builtin_nontemporal_store(o, xrow + s * 64);
+        }
+        if (raw) {
+#pragma unroll
+            for (int s = 0; s < kSpans; ++s)
+                *reinterpret_cast<u32x2*>(raw + (t * 16 + head[s]) * 160 + off[s]) = a[k][s];
+        }
     }
 }
 
@@ -157,7 +171,8 @@ gather_heads_kernel(const int32_t* __restrict__ row_ids, int64_t T, const uint8_
 hipError_t launch_gather_heads(const int32_t* row_ids, int64_t T, const uint8_t* table,
                                const float* scales, int64_t R, uint16_t* x, uint8_t* raw,
                                int32_t* dev_err, hipStream_t stream) {
-    int64_t blocks = (T + kTokPerBlock - 1) / kTokPerBlock;
+    const int64_t per_block = (int64_t)kTokPerBlock * kHeadTokPerWave;
+    int64_t blocks = (T + per_block - 1) / per_block;
     hipLaunchKernelGGL(gather_heads_kernel, dim3((unsigned)blocks), dim3(64 * kTokPerBlock), 0, stream,
                        row_ids, T, table, scales, R, x, raw, dev_err);
     return hipGetLastError();
