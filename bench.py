@@ -165,6 +165,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill", choices=["tiny", "decode", "prefill", "ragged", "long"])
+    ap.add_argument("--overlap", action="store_true",
+                    help="long workload: IDs and rows of the next chunk on a second stream (ple_forward_x)")
     ap.add_argument("--layout", default="two", choices=["two", "heads"],
                     help="two: 2 lookups of 2560-byte rows per token; heads: 16 lookups of 160-byte rows")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -226,7 +228,45 @@ def main():
     for b in batches:
         ws.get(b[0].numel(), b[1].numel() - 1)
 
-    if name == "long":
+    if name == "long" and args.overlap:
+        # IDs and rows of chunk i+1 on a side stream while chunk i is
+        # projected and fused (ple_forward_x); each chunk's n-gram history
+        # comes from the token stream, two x buffers alternate
+        side = torch.cuda.Stream(device=dev)
+        n_ids = 16 if heads else 2
+        hists = []
+        for i, (t, c) in enumerate(wl.chunks):
+            prev = wl.chunks[i - 1][0]      # chunk 0 continues from chunk 15 of the previous step
+            hists.append(torch.from_numpy(prev[-2:].reshape(1, 2).astype(np.int32)).to(dev))
+        hl2 = torch.full((1,), 2, dtype=torch.int32, device=dev)
+        hl0 = torch.zeros((1,), dtype=torch.int32, device=dev)
+        T_chunk = batches[0][0].numel()
+        xbuf = [torch.empty((T_chunk, D), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+        rbuf = [torch.empty((T_chunk, n_ids), dtype=torch.int32, device=dev) for _ in range(2)]
+        free = [torch.cuda.Event() for _ in range(2)]
+        ready = [torch.cuda.Event() for _ in range(2)]
+        # both sides on streams of their own: the legacy default stream would
+        # serialize them
+        main = torch.cuda.Stream(device=dev)
+        main.wait_stream(torch.cuda.current_stream(dev))
+        for e in free:
+            e.record(main)
+
+        def step(k, events=None):
+            for i, ((t, c, h), o) in enumerate(zip(batches, outs)):
+                j = i % 2
+                with torch.cuda.stream(side):
+                    side.wait_event(free[j])
+                    hl = hl0 if (k == 0 and i == 0) else hl2
+                    ple.ple_hash(t, c, hists[i], hl, wl.R, row_ids=rbuf[j], heads=heads)
+                    ple.ple_lookup(rbuf[j], tab, sc, x=xbuf[j], heads=heads)
+                    ready[j].record(side)
+                with torch.cuda.stream(main):
+                    main.wait_event(ready[j])
+                    ple.ple_forward_x(xbuf[j], t, c, Wd, cwd, h, state, out=o, workspace=ws)
+                    free[j].record(main)
+        tokens_per_step = sum(b[0].numel() for b in batches)
+    elif name == "long":
         def step(k, events=None):
             for (t, c, h), o in zip(batches, outs):
                 ple.ple_forward(t, c, tab, sc, Wd, cwd, h, state, out=o, workspace=ws, events=events, heads=heads)
@@ -325,7 +365,9 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": describe(name, wl, heads), "name": name, "layout": args.layout,
+        "config": {"workload": describe(name, wl, heads) + (
+                       "; IDs and rows of the next chunk gathered on a second stream during the current one"
+                       if args.overlap and name == "long" else ""), "name": name, "layout": args.layout,
                    "tokens_per_step": tokens_per_step,
                    "sequences": wl.S, "table_rows": wl.R, "table_bytes": wl.R * D},
         "roofline": roofline,

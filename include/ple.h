@@ -155,8 +155,22 @@ int ple_forward(const ple_forward_args* args, void* stream);
  * gate/conv/fuse kernels. events may not be NULL. */
 int ple_forward_profiled(const ple_forward_args* args, void* stream, void* const* events);
 
-/* Workspace bytes ple_forward needs for up to max_T tokens and max_S sequences. */
+/* Workspace bytes ple_forward (and ple_forward_x) needs for up to max_T
+ * tokens and max_S sequences. */
 size_t ple_forward_workspace_size(int64_t max_T, int32_t max_S);
+
+/* a3..a4 from rows gathered ahead: the IDs depend only on the tokens, so the
+ * ID and table-read stages can run early, on another stream, before the
+ * layer that needs them (SSD-streaming page, "技术细节" and the Spark
+ * deployment page's scheduling section: rows are fetched ahead of the PLE
+ * layer). x_bf16 (bf16 [T][2560], 16-byte aligned, read only) is the output
+ * of ple_hash + ple_lookup (or their 16-lookup variants) for this chunk with
+ * the history it had; this call runs the projection, gate, conv and fuse
+ * exactly as ple_forward would and updates conv_state, hist_ids and
+ * hist_len the same way. table, scales, R and vocab_size are not used;
+ * row_ids_out and x_out must be NULL. Ordering x's producer before this call
+ * (an event between the streams) is the caller's. */
+int ple_forward_x(const ple_forward_args* args, const uint16_t* x_bf16, void* stream);
 
 /* ---- The 16-lookup layout ------------------------------------------------
  * The SSD-streaming page's model card ("技术细节") speaks of 16 lookups of

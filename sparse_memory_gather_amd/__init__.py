@@ -62,8 +62,8 @@ _lib = None
 
 EXPORTS = ("ple_hash", "ple_lookup", "ple_proj", "ple_forward", "ple_forward_profiled",
            "ple_forward_workspace_size", "ple_hash_heads", "ple_lookup_heads", "ple_forward_heads",
-           "ple_forward_heads_profiled", "ple_forward_heads_workspace_size", "ple_status_string",
-           "ple_last_error")
+           "ple_forward_heads_profiled", "ple_forward_heads_workspace_size", "ple_forward_x",
+           "ple_status_string", "ple_last_error")
 HEADS = 16            # 16-lookup layout: head tables of 160-byte rows
 SLICE = D // HEADS
 
@@ -92,6 +92,8 @@ def load_library(path: str = LIB_PATH):
     for name in ("ple_forward_profiled", "ple_forward_heads_profiled"):
         getattr(lib, name).argtypes = [ctypes.POINTER(ForwardArgs), _P, ctypes.POINTER(_P)]
         getattr(lib, name).restype = ctypes.c_int
+    lib.ple_forward_x.argtypes = [ctypes.POINTER(ForwardArgs), _P, _P]
+    lib.ple_forward_x.restype = ctypes.c_int
     for name in ("ple_forward_workspace_size", "ple_forward_heads_workspace_size"):
         getattr(lib, name).argtypes = [I64, I32]
         getattr(lib, name).restype = ctypes.c_size_t
@@ -298,6 +300,52 @@ def ple_forward(tokens, cu_seqlens, table, scales, W, conv_w, h, state: State, o
         ev = (_P * 5)(*[ctypes.c_void_p(int(e)) for e in events])
         f = lib.ple_forward_heads_profiled if heads else lib.ple_forward_profiled
         _check(f(ctypes.byref(a), _stream(stream), ev))
+    if debug:
+        dbg["out"] = out
+        return dbg
+    return out
+
+
+def ple_forward_x(x, tokens, cu_seqlens, W, conv_w, h, state: State, out=None, workspace=None,
+                  eps: float = DEFAULT_EPS, dev_err=None, debug: bool = False, stream=None):
+    """a3..a4 from x (bf16 [T][2560]) gathered ahead by ple_hash + ple_lookup
+    (e.g. on another stream, with the history the chunk starts from): the
+    same projection, gate, conv, fuse and state update as ple_forward. With
+    debug=True returns a dict with out, e, gate, y."""
+    T = tokens.numel()
+    S = cu_seqlens.numel() - 1
+    dev = tokens.device
+    if out is None:
+        out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    if workspace is None:
+        workspace = Workspace(dev)
+    ws = workspace.get(T, S) if isinstance(workspace, Workspace) else workspace
+    dbg = {}
+    if debug:
+        dbg = dict(e=torch.empty((T, D), dtype=torch.float32, device=dev),
+                   gate=torch.empty((T,), dtype=torch.float32, device=dev),
+                   y=torch.empty((T, D), dtype=torch.float32, device=dev))
+    a = ForwardArgs()
+    a.tokens = _dev(tokens, "tokens", torch.int32, (T,))
+    a.T = T
+    a.cu_seqlens = _dev(cu_seqlens, "cu_seqlens", torch.int32, (S + 1,))
+    a.S = S
+    a.W = _dev(W, "W", torch.bfloat16, (D, D))
+    a.conv_w = _dev(conv_w, "conv_w", torch.bfloat16, (D, CONV_TAPS))
+    a.h = _dev(h, "h", torch.bfloat16, (T, D))
+    a.out = _dev(out, "out", torch.bfloat16, (T, D))
+    a.hist_ids = _dev(state.hist_ids, "hist_ids", torch.int32, (S, 2))
+    a.hist_len = _dev(state.hist_len, "hist_len", torch.int32, (S,))
+    a.conv_state = _dev(state.conv_state, "conv_state", torch.float32, (S, 3, D))
+    a.workspace = _dev(ws, "workspace", torch.uint8)
+    a.workspace_bytes = ws.numel()
+    a.dev_err = _opt(dev_err, "dev_err", torch.int32, (1,))
+    a.eps = eps
+    if debug:
+        a.e_out = dbg["e"].data_ptr()
+        a.gate_out = dbg["gate"].data_ptr()
+        a.y_out = dbg["y"].data_ptr()
+    _check(load_library().ple_forward_x(ctypes.byref(a), _dev(x, "x", torch.bfloat16, (T, D)), _stream(stream)))
     if debug:
         dbg["out"] = out
         return dbg

@@ -224,20 +224,29 @@ int ple_proj(const uint16_t* x_bf16, int64_t T, const uint16_t* W_bf16, float* e
 
 }  // extern "C"
 
-static int forward_impl(const ple_forward_args* a, void* stream, void* const* events, bool heads) {
+// x_in != NULL: ple_forward_x (x given; no ID or gather kernel, table,
+// scales, R and vocab_size unused)
+static int forward_impl(const ple_forward_args* a, void* stream, void* const* events, bool heads,
+                        const uint16_t* x_in = nullptr) {
     if (!a) return fail(PLE_ERR_NULL, "ple_forward: args is NULL");
+    const bool from_x = x_in != nullptr;
     const int64_t T = a->T;
     const int32_t S = a->S;
     if (T < 0) return fail(PLE_ERR_SHAPE, "T = %lld < 0", (long long)T);
     if (S < 1) return fail(PLE_ERR_SHAPE, "S = %d < 1", S);
-    if (int st = check_R(a->R)) return st;
-    if (a->vocab_size < 1 || a->vocab_size > PLE_MAX_VOCAB)
-        return fail(PLE_ERR_RANGE, "vocab_size = %d outside [1, 2^20]", a->vocab_size);
+    if (!from_x) {
+        if (int st = check_R(a->R)) return st;
+        if (a->vocab_size < 1 || a->vocab_size > PLE_MAX_VOCAB)
+            return fail(PLE_ERR_RANGE, "vocab_size = %d outside [1, 2^20]", a->vocab_size);
+    }
     if (!(a->eps >= 0.0f) || !isfinite(a->eps)) return fail(PLE_ERR_RANGE, "eps must be finite and >= 0");
+    if (from_x && (a->row_ids_out || a->x_out))
+        return fail(PLE_ERR_SHAPE, "ple_forward_x: row_ids_out and x_out are not produced (x is an input)");
     if (T == 0) return ok();
-    if (!a->tokens || !a->cu_seqlens || !a->table || !a->scales || !a->W || !a->conv_w || !a->h ||
-        !a->out || !a->hist_ids || !a->hist_len || !a->conv_state)
+    if (!a->tokens || !a->cu_seqlens || (!from_x && (!a->table || !a->scales)) || !a->W || !a->conv_w ||
+        !a->h || !a->out || !a->hist_ids || !a->hist_len || !a->conv_state)
         return fail(PLE_ERR_NULL, "ple_forward: a required pointer is NULL");
+    if (from_x && !aligned(x_in, 16)) return fail(PLE_ERR_ALIGN, "ple_forward_x: x is not 16-byte aligned");
     if (!a->workspace) return fail(PLE_ERR_WORKSPACE, "ple_forward: workspace is NULL");
     const WsLayout L = layout(T, S, heads);
     if (a->workspace_bytes < L.total)
@@ -253,8 +262,9 @@ static int forward_impl(const ple_forward_args* a, void* stream, void* const* ev
     Range r[] = {
         rng("tokens", a->tokens, T * 4, false),
         rng("cu_seqlens", a->cu_seqlens, (S + 1) * 4ull, false),
-        rng("table", a->table, (size_t)a->R * kD, false),
-        rng("scales", a->scales, (size_t)a->R * (heads ? 16 : 1) * 4, false),
+        rng("table", from_x ? nullptr : a->table, (size_t)a->R * kD, false),
+        rng("scales", from_x ? nullptr : a->scales, (size_t)a->R * (heads ? 16 : 1) * 4, false),
+        rng("x", x_in, (size_t)T * kD * 2, false),
         rng("W", a->W, (size_t)kD * kD * 2, false),
         rng("conv_w", a->conv_w, (size_t)kD * kTaps * 2, false),
         rng("h", a->h, act, false),
@@ -284,13 +294,21 @@ static int forward_impl(const ple_forward_args* a, void* stream, void* const* ev
     };
     hipError_t e = mark(0);
     if (int st = hip_status(e, "ple_forward: event record")) return st;
-    e = launch_hash(a->tokens, T, a->cu_seqlens, S, a->hist_ids, a->hist_len, a->vocab_size,
-                    a->R, row_ids, a->dev_err, a->conv_state, snap, heads, s);
-    if (int st = hip_status(e, "ple_forward: hash launch")) return st;
+    if (from_x) {
+        x = const_cast<uint16_t*>(x_in);  // read only from here on
+        e = launch_state_copy(a->conv_state, snap, S, s);
+        if (int st = hip_status(e, "ple_forward_x: state copy launch")) return st;
+    } else {
+        e = launch_hash(a->tokens, T, a->cu_seqlens, S, a->hist_ids, a->hist_len, a->vocab_size,
+                        a->R, row_ids, a->dev_err, a->conv_state, snap, heads, s);
+        if (int st = hip_status(e, "ple_forward: hash launch")) return st;
+    }
     if (int st = hip_status(mark(1), "ple_forward: event record")) return st;
-    e = heads ? launch_gather_heads(row_ids, T, a->table, a->scales, a->R, x, nullptr, a->dev_err, s)
-              : launch_gather(row_ids, T, a->table, a->scales, a->R, x, nullptr, a->dev_err, s);
-    if (int st = hip_status(e, "ple_forward: gather launch")) return st;
+    if (!from_x) {
+        e = heads ? launch_gather_heads(row_ids, T, a->table, a->scales, a->R, x, nullptr, a->dev_err, s)
+                  : launch_gather(row_ids, T, a->table, a->scales, a->R, x, nullptr, a->dev_err, s);
+        if (int st = hip_status(e, "ple_forward: gather launch")) return st;
+    }
     if (int st = hip_status(mark(2), "ple_forward: event record")) return st;
     e = launch_proj(x, T, a->W, a->e_out, e16, s);
     if (int st = hip_status(e, "ple_forward: projection launch")) return st;
@@ -325,6 +343,11 @@ int ple_forward_heads(const ple_forward_args* a, void* stream) {
 int ple_forward_heads_profiled(const ple_forward_args* a, void* stream, void* const* events) {
     if (int st = check_events(events)) return st;
     return forward_impl(a, stream, events, true);
+}
+
+int ple_forward_x(const ple_forward_args* a, const uint16_t* x_bf16, void* stream) {
+    if (!x_bf16) return fail(PLE_ERR_NULL, "ple_forward_x: x is NULL");
+    return forward_impl(a, stream, nullptr, false, x_bf16);
 }
 
 }  // extern "C"

@@ -100,7 +100,23 @@ hash_kernel(const int32_t* __restrict__ tokens, int64_t T, const int32_t* __rest
     }
 }
 
+// the carried conv state alone (ple_forward_x: no ID kernel in the launch)
+__global__ void __launch_bounds__(kHashBlock)
+state_copy_kernel(const f32x4* __restrict__ src, f32x4* __restrict__ dst, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * kHashBlock + threadIdx.x; i < n; i += (int64_t)gridDim.x * kHashBlock)
+        dst[i] = src[i];
+}
+
 }  // namespace
+
+hipError_t launch_state_copy(const float* conv_state, float* state_snap, int32_t S, hipStream_t stream) {
+    const int64_t n = (int64_t)S * 3 * kD / 4;
+    int64_t blocks = (n + kHashBlock - 1) / kHashBlock;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)blocks), dim3(kHashBlock), 0, stream,
+                       reinterpret_cast<const f32x4*>(conv_state), reinterpret_cast<f32x4*>(state_snap), n);
+    return hipGetLastError();
+}
 
 hipError_t launch_hash(const int32_t* tokens, int64_t T, const int32_t* cu, int32_t S,
                        const int32_t* hist_ids, const int32_t* hist_len, int32_t vocab, int64_t R,

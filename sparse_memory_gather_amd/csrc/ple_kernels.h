@@ -38,6 +38,9 @@ hipError_t launch_hash(const int32_t* tokens, int64_t T, const int32_t* cu, int3
                        int32_t* row_ids, int32_t* dev_err, const float* conv_state,
                        float* state_snap, bool heads, hipStream_t stream);
 
+// copy of conv_state [S][3][kD] into state_snap
+hipError_t launch_state_copy(const float* conv_state, float* state_snap, int32_t S, hipStream_t stream);
+
 // 16-lookup layout: table [16][R][160], scales [16][R], row_ids [T][16],
 // raw (optional) [T][16][160].
 hipError_t launch_gather_heads(const int32_t* row_ids, int64_t T, const uint8_t* table,

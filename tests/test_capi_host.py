@@ -124,3 +124,22 @@ def test_hash_lookup_proj_reject_bad_arguments():
                           None) == -5
     assert lib.ple_proj(FAKE, 4, FAKE + 0x100000, FAKE + 0x100000, None) == -5
     assert lib.ple_proj(FAKE, -1, FAKE + 0x100000, FAKE + 0x10000000, None) == -2
+
+
+@cpu_only
+def test_forward_x_and_heads_reject_bad_arguments():
+    lib = ple.load_library()
+    X = FAKE + 0x8000000
+    # x NULL; debug outputs that ple_forward_x does not produce; x misaligned;
+    # x overlapping a written buffer
+    assert lib.ple_forward_x(ctypes.byref(_fwd_args()), None, None) == -1
+    assert lib.ple_forward_x(ctypes.byref(_fwd_args(x_out=FAKE + 0x9000000)), X, None) == -2
+    assert lib.ple_forward_x(ctypes.byref(_fwd_args()), X + 8, None) == -4
+    assert lib.ple_forward_x(ctypes.byref(_fwd_args()), FAKE + 0x3000000, None) == -5    # x inside out
+    # table, scales, R and vocab_size are not used by ple_forward_x
+    assert lib.ple_forward_x(ctypes.byref(_fwd_args(T=0, table=None, R=0)), X, None) == 0
+    # 16-lookup layout: row_ids must be 16-byte aligned; scales span 16 R
+    assert lib.ple_hash_heads(FAKE, 10, FAKE + 0x100, 1, FAKE, FAKE, 100, 10, FAKE + 0x1008, None, None) == -4
+    # x placed 320 bytes after the scales: outside 10 scales, inside 16 x 10
+    assert lib.ple_lookup_heads(FAKE, 4, FAKE + 0x10000, FAKE + 0x90000, 10, FAKE + 0x90140, None, None,
+                                None) == -5

@@ -345,3 +345,76 @@ def test_heads_forward_parity_with_edge_cases(dev, small_table, small_head_scale
         idx += [a + p for p in range(3, b - a)]
     refs = oracle_samples(seqs, samples, W, cw, R_SMALL, heads=True)
     check_samples(gather_debug(res, idx), refs, W, "heads")
+
+
+# ---------------------------------------------------------------------------
+# ID-ahead form: rows gathered on another stream, ple_forward_x consumes x
+# ---------------------------------------------------------------------------
+
+def test_forward_x_pipelined_equals_forward(dev, small_table, dev_weights):
+    # chunk i+1's IDs and rows are computed on a side stream while chunk i
+    # runs; the history each chunk starts from comes from the token stream
+    tab, sc = small_table
+    rng = np.random.default_rng(60)
+    cuts = [1, 300, 2, 517, 64]
+    n = sum(cuts)
+    toks = inputs.uniform_tokens(rng, n)
+    h = inputs.normal_bf16(rng, (n, D))
+
+    st_ref = ple.State(1, dev)
+    ref, pos = [], 0
+    for L in cuts:
+        ref.append(host_bits(ple.ple_forward(dev_i32(toks[pos:pos + L], dev), dev_i32([0, L], dev), tab, sc,
+                                             dev_weights[0], dev_weights[1], dev_bf16(h[pos:pos + L], dev),
+                                             st_ref)))
+        pos += L
+
+    side = torch.cuda.Stream(device=dev)
+    main = torch.cuda.current_stream(dev)
+    st = ple.State(1, dev)
+    chunks, pos = [], 0
+    for L in cuts:
+        k = min(2, pos)
+        hist = np.zeros((1, 2), np.int32)
+        hist[0, 2 - k:] = toks[pos - k:pos]
+        chunks.append(dict(t=dev_i32(toks[pos:pos + L], dev), cu=dev_i32([0, L], dev),
+                           hist=dev_i32(hist, dev), hl=dev_i32([k], dev), h=dev_bf16(h[pos:pos + L], dev)))
+        pos += L
+    torch.cuda.synchronize()
+    xs, ready = [], []
+    for c in chunks:   # all rows ahead, on the side stream
+        with torch.cuda.stream(side):
+            rid = ple.ple_hash(c["t"], c["cu"], c["hist"], c["hl"], R_SMALL)
+            xs.append(ple.ple_lookup(rid, tab, sc))
+            ev = torch.cuda.Event()
+            ev.record(side)
+            ready.append(ev)
+    outs = []
+    for c, x, ev in zip(chunks, xs, ready):
+        main.wait_event(ev)
+        outs.append(ple.ple_forward_x(x, c["t"], c["cu"], dev_weights[0], dev_weights[1], c["h"], st))
+    torch.cuda.synchronize()
+    for a, b in zip(outs, ref):
+        assert np.array_equal(host_bits(a), b)
+    assert torch.equal(st.conv_state, st_ref.conv_state)
+    assert torch.equal(st.hist_ids, st_ref.hist_ids) and torch.equal(st.hist_len, st_ref.hist_len)
+
+
+def test_forward_x_with_several_sequences_and_debug_outputs(dev, small_table, dev_weights):
+    tab, sc = small_table
+    lengths = [0, 3, 40, 1, 290]
+    toks, cu, hist, hlen, h = _case(61, lengths, [2, 1, 0, 2, 1])
+    S = len(lengths)
+    st_a, st_b = ple.State(S, dev), ple.State(S, dev)
+    for st in (st_a, st_b):
+        st.hist_ids.copy_(dev_i32(hist, dev))
+        st.hist_len.copy_(dev_i32(hlen, dev))
+    a = ple.ple_forward(dev_i32(toks, dev), dev_i32(cu, dev), tab, sc, dev_weights[0], dev_weights[1],
+                        dev_bf16(h, dev), st_a, debug=True)
+    rid = ple.ple_hash(dev_i32(toks, dev), dev_i32(cu, dev), st_b.hist_ids, st_b.hist_len, R_SMALL)
+    x = ple.ple_lookup(rid, tab, sc)
+    b = ple.ple_forward_x(x, dev_i32(toks, dev), dev_i32(cu, dev), dev_weights[0], dev_weights[1],
+                          dev_bf16(h, dev), st_b, debug=True)
+    for k in ("out", "e", "gate", "y"):
+        assert torch.equal(a[k], b[k]), k
+    assert torch.equal(st_a.conv_state, st_b.conv_state) and torch.equal(st_a.hist_ids, st_b.hist_ids)
