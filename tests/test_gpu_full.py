@@ -181,3 +181,44 @@ def test_prefill_heads_layout(dev, full_table, dev_weights, weights):
     ref = oracle_samples([(toks, h)], [(0, p) for p in pos], W, cw, R, heads=True)
     print("prefill heads", check_samples(gather_debug(res, pos), ref, W, "prefill heads"))
     del sc16
+
+
+def test_max_size_single_call(dev, dev_weights, weights):
+    # one call of 2^20 tokens in four uneven sequences: byte offsets of the
+    # bf16 rows pass 2^31, so any 32-bit index arithmetic would show here
+    W, cw = weights
+    R = 65_536
+    tab, sc = table.table_gpu(R, device=dev)
+    T = 1 << 20
+    lengths = [1, (1 << 19) - 1, (1 << 19) - 3, 3]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    rng = np.random.default_rng(17)
+    toks = inputs.uniform_tokens(rng, T)
+    g = torch.Generator(device=dev)
+    g.manual_seed(1717)
+    h = torch.randn((T, D), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    st = ple.State(len(lengths), dev)
+    res = ple.ple_forward(dev_i32(toks, dev), dev_i32(cu, dev), tab, sc, dev_weights[0], dev_weights[1], h,
+                          st, debug=True)
+    ids = res["row_ids"]
+    probe = np.array([0, 1, 2, 3, 4, cu[2] - 1, cu[2], cu[2] + 3, cu[3] - 1, cu[3], T - 3, T - 1,
+                      (1 << 19) + 12345, 900_001])
+    ref_ids = oracle.ngram_ids(toks, cu, np.zeros((4, 2), np.int32), np.zeros(4, np.int32), R)
+    assert np.array_equal(ids[torch.as_tensor(probe, device=dev)].cpu().numpy(), ref_ids[probe])
+    assert int((ids.cpu().numpy() != ref_ids).sum()) == 0
+    # sampled outputs, each recomputed from its own sequence
+    seqs, samples, idx = [], [], []
+    for s in range(4):
+        a, b = int(cu[s]), int(cu[s + 1])
+        pos = sorted(set(p for p in (0, 1, 2, 3, b - a - 1, (b - a) // 2) if 0 <= p < b - a))
+        # only the hidden rows the samples read (each sample and the three before it)
+        need = sorted(set(q for p in pos for q in range(max(0, p - 3), p + 1)))
+        hh = np.zeros((b - a, D), np.uint16)
+        hh[need] = host_bits(h[torch.as_tensor(np.array(need) + a, device=dev)])
+        seqs.append((toks[a:b], hh))
+        samples += [(s, p) for p in pos]
+        idx += [a + p for p in pos]
+    ref = oracle_samples(seqs, samples, W, cw, R)
+    print("max size", check_samples(gather_debug(res, idx), ref, W, "max size"))
+    del res, h
+    torch.cuda.empty_cache()
