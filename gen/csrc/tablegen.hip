@@ -101,3 +101,54 @@ extern "C" int gen_fill_scales(float* scales, int64_t n, uint64_t seed, uint32_t
                        scale_span);
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }
+
+// NVFP4 table (see tablegen_host.c): codes [R][1280], block scales [R][160]
+__global__ void __launch_bounds__(256) fill_nvfp4_codes(uint8_t* __restrict__ codes, uint64_t n_calls,
+                                                        uint64_t seed, const uint32_t* __restrict__ thr7) {
+    uint32_t thr[7];
+#pragma unroll
+    for (int k = 0; k < 7; ++k) thr[k] = thr7[k];
+    uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t n = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; n < n_calls; n += stride) {
+        uint64_t c[4] = {n, 0, 0, 0};
+        philox4x64_10(c, seed, 1);
+        uint32_t packed = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            uint64_t word = c[j / 2];
+            uint32_t w = (j & 1) ? (uint32_t)(word >> 32) : (uint32_t)word;
+            uint32_t u = w & 0x7FFFFFFFu, m = 0;
+#pragma unroll
+            for (int k = 0; k < 7; ++k) m += thr[k] <= u ? 1u : 0u;
+            packed |= (((w >> 31) << 3) | m) << (4 * j);
+        }
+        reinterpret_cast<uint32_t*>(codes)[n] = packed;
+    }
+}
+
+__global__ void __launch_bounds__(256) fill_nvfp4_blocks(uint8_t* __restrict__ blocks, uint64_t n_blocks,
+                                                         uint64_t seed, uint32_t lo, uint32_t span) {
+    uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t q = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; q < n_blocks; q += stride) {
+        uint64_t c[4] = {q, 2, 0, 0};
+        philox4x64_10(c, seed, 1);
+        blocks[q] = (uint8_t)(lo + (uint32_t)(c[0] >> 32) % span);
+    }
+}
+
+extern "C" int gen_fill_nvfp4(uint8_t* codes, uint8_t* blocks, int64_t R, uint64_t seed, const uint32_t* thr7_dev,
+                              uint32_t block_lo, uint32_t block_span, void* stream) {
+    if (!codes || !blocks || !thr7_dev || R <= 0) return -1;
+    if (reinterpret_cast<uintptr_t>(codes) % 4) return -2;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    uint64_t n_calls = (uint64_t)R * kRow / 8;
+    uint64_t want = (n_calls + 255) / 256;
+    unsigned grid = (unsigned)(want < 65536 * 8 ? want : 65536 * 8);
+    hipLaunchKernelGGL(fill_nvfp4_codes, dim3(grid), dim3(256), 0, s, codes, n_calls, seed, thr7_dev);
+    uint64_t n_blocks = (uint64_t)R * (kRow / 16);
+    uint64_t want_b = (n_blocks + 255) / 256;
+    unsigned grid_b = (unsigned)(want_b < 65536 * 8 ? want_b : 65536 * 8);
+    hipLaunchKernelGGL(fill_nvfp4_blocks, dim3(grid_b), dim3(256), 0, s, blocks, n_blocks, seed, block_lo,
+                       block_span);
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+}

@@ -12,6 +12,12 @@
  *          magnitude code is the number of thresholds <= u.
  *   scale: counter = (r, 1, 0, 0); m = lo + (hi32(out[0]) % span);
  *          scale = m * 2^-23 (an exact fp32 with at most 20 significant bits).
+ * NVFP4 table (a second table, key = (seed, 1)): element g = r * 2560 + c
+ *   takes word g % 8 of Philox(counter (g / 8, 0, 0, 0)); bit 31 is the sign,
+ *   the E2M1 magnitude is the number of the 7 thresholds <= bits 0..30;
+ *   element 2k is the low nibble of byte k of the row. Block b (elements
+ *   16b .. 16b+15) of row r: q = r * 160 + b, Philox(counter (q, 2, 0, 0)),
+ *   E4M3 code = lo + hi32(out[0]) % span. The row scale is the FP8 table's.
  * The same bytes, read as 16 head tables of R rows x 160 bytes, give row r of
  * head h at element g = (h R + r) 160; its scale is scale number h R + r of
  * the same recipe (the first R being the 2560-wide rows' scales).
@@ -106,5 +112,36 @@ void gen_scales(uint64_t seed, const int64_t* ids, int64_t n, uint32_t scale_lo,
         gen_philox4x64_10(sc, key, so);
         uint32_t m = scale_lo + (uint32_t)(so[0] >> 32) % scale_span;
         out[i] = (float)m * (1.0f / 8388608.0f);
+    }
+}
+
+/* NVFP4 rows ids[0..n): codes_out[n][1280], blocks_out[n][160] (the fp32 row
+ * scales are the FP8 table's, gen_table_rows). */
+void gen_nvfp4_rows(uint64_t seed, const int64_t* ids, int64_t n, const uint32_t* thr7,
+                    uint32_t block_lo, uint32_t block_span, uint8_t* codes_out, uint8_t* blocks_out) {
+    const uint64_t key[2] = {seed, 1};
+    for (int64_t i = 0; i < n; ++i) {
+        uint64_t r = (uint64_t)ids[i];
+        uint8_t* codes = codes_out + i * (ROW / 2);
+        for (int c8 = 0; c8 < ROW / 8; ++c8) {
+            uint64_t ctr[4] = {(r * ROW) / 8 + (uint64_t)c8, 0, 0, 0}, o[4];
+            gen_philox4x64_10(ctr, key, o);
+            for (int j = 0; j < 8; j += 2) {
+                uint8_t nib[2];
+                for (int k = 0; k < 2; ++k) {
+                    uint64_t word = o[(j + k) / 2];
+                    uint32_t w = ((j + k) & 1) ? (uint32_t)(word >> 32) : (uint32_t)word;
+                    uint32_t u = w & 0x7FFFFFFFu, m = 0;
+                    while (m < 7 && thr7[m] <= u) ++m;
+                    nib[k] = (uint8_t)(((w >> 31) << 3) | m);
+                }
+                codes[c8 * 4 + j / 2] = (uint8_t)(nib[0] | (nib[1] << 4));
+            }
+        }
+        for (int b = 0; b < ROW / 16; ++b) {
+            uint64_t ctr[4] = {r * (ROW / 16) + (uint64_t)b, 2, 0, 0}, o[4];
+            gen_philox4x64_10(ctr, key, o);
+            blocks_out[i * (ROW / 16) + b] = (uint8_t)(block_lo + (uint32_t)(o[0] >> 32) % block_span);
+        }
     }
 }

@@ -143,6 +143,26 @@ def e4m3_magnitude_thresholds() -> np.ndarray:
     return thr
 
 
+# NVFP4 table (E2M1 codes, one E4M3 scale per 16 elements, the fp32 row scale):
+# the E2M1 magnitude grid of the OCP Microscaling formats (v1.0, FP4 E2M1),
+# codes drawn for |Z| * 2, Z ~ N(0,1); block scales uniform over the E4M3
+# codes 0x28 .. 0x47 (0.25 .. 3.75)
+E2M1_GRID = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+NVFP4_BLOCK_CODE_LO = 0x28
+NVFP4_BLOCK_CODES = 32
+
+
+def e2m1_magnitude_thresholds() -> np.ndarray:
+    """7 31-bit thresholds mapping a uniform u in [0, 2^31) to the E2M1
+    magnitude code of |Z| * 2 rounded to nearest (the number of thresholds
+    <= u); threshold k sits at the midpoint of grid values k, k+1."""
+    mids = [0.5 * (E2M1_GRID[k] + E2M1_GRID[k + 1]) / 2.0 for k in range(7)]   # in units of |Z|
+    thr = np.array([math.floor(math.erf(m / math.sqrt(2.0)) * 2.0 ** 31 + 0.5) for m in mids], dtype=np.uint64)
+    thr = np.minimum(thr, 2 ** 31).astype(np.uint32)
+    assert np.all(np.diff(thr.astype(np.int64)) > 0)
+    return thr
+
+
 SCALE_M_LO = 83_887      # scale = m * 2^-23, m in [83887, 838861): [0.0100001, 0.0999999]
 SCALE_M_SPAN = 838_861 - 83_887
 

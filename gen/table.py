@@ -47,6 +47,9 @@ def _host_lib():
         lib.gen_scales.argtypes = [ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32,
                                    ctypes.c_uint32, ctypes.c_void_p]
         lib.gen_scales.restype = None
+        lib.gen_nvfp4_rows.argtypes = [ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                       ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]
+        lib.gen_nvfp4_rows.restype = None
         _host = lib
     return _host
 
@@ -96,6 +99,25 @@ def slices_cpu(heads, ids, R: int, seed: int = inputs.TABLE_SEED):
     return codes, scales
 
 
+def nvfp4_rows_cpu(ids, seed: int = inputs.TABLE_SEED):
+    """Rows `ids` of the NVFP4 table: (codes uint8[n][1280] packed E2M1, low
+    nibble first; blocks uint8[n][160] E4M3 scale per 16 elements; scales
+    float32[n], the fp32 row scales)."""
+    ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int64).reshape(-1))
+    n = len(ids)
+    codes = np.empty((n, inputs.D // 2), dtype=np.uint8)
+    blocks = np.empty((n, inputs.D // 16), dtype=np.uint8)
+    thr = np.ascontiguousarray(inputs.e2m1_magnitude_thresholds())
+    lib = _host_lib()
+    if n:
+        lib.gen_nvfp4_rows(seed, ids.ctypes.data, n, thr.ctypes.data, inputs.NVFP4_BLOCK_CODE_LO,
+                           inputs.NVFP4_BLOCK_CODES, codes.ctypes.data, blocks.ctypes.data)
+    scales = np.empty(n, dtype=np.float32)
+    if n:
+        lib.gen_scales(seed, ids.ctypes.data, n, inputs.SCALE_M_LO, inputs.SCALE_M_SPAN, scales.ctypes.data)
+    return codes, blocks, scales
+
+
 def _hip_lib():
     global _hip
     if _hip is None:
@@ -110,6 +132,9 @@ def _hip_lib():
         lib.gen_fill_scales.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32,
                                         ctypes.c_uint32, ctypes.c_void_p]
         lib.gen_fill_scales.restype = ctypes.c_int
+        lib.gen_fill_nvfp4.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64,
+                                       ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p]
+        lib.gen_fill_nvfp4.restype = ctypes.c_int
         _hip = lib
     return _hip
 
@@ -141,3 +166,24 @@ def head_scales_gpu(R: int, seed: int = inputs.TABLE_SEED, device="cuda"):
         raise RuntimeError(f"gen_fill_scales failed: {rc}")
     torch.cuda.current_stream(scales.device).synchronize()
     return scales
+
+
+def nvfp4_gpu(R: int, seed: int = inputs.TABLE_SEED, device="cuda"):
+    """The NVFP4 table on the GPU: codes uint8 [R][1280], blocks uint8
+    [R][160], row scales float32 [R]."""
+    import torch
+    codes = torch.empty((R, inputs.D // 2), dtype=torch.uint8, device=device)
+    blocks = torch.empty((R, inputs.D // 16), dtype=torch.uint8, device=device)
+    scales = torch.empty((R,), dtype=torch.float32, device=device)
+    thr = torch.from_numpy(inputs.e2m1_magnitude_thresholds().astype(np.int64)).to(torch.int32).to(device)
+    stream = torch.cuda.current_stream(codes.device).cuda_stream
+    rc = _hip_lib().gen_fill_nvfp4(codes.data_ptr(), blocks.data_ptr(), R, seed, thr.data_ptr(),
+                                   inputs.NVFP4_BLOCK_CODE_LO, inputs.NVFP4_BLOCK_CODES, stream)
+    if rc != 0:
+        raise RuntimeError(f"gen_fill_nvfp4 failed: {rc}")
+    rc = _hip_lib().gen_fill_scales(scales.data_ptr(), R, seed, inputs.SCALE_M_LO, inputs.SCALE_M_SPAN, stream)
+    if rc != 0:
+        raise RuntimeError(f"gen_fill_scales failed: {rc}")
+    torch.cuda.current_stream(codes.device).synchronize()
+    del thr
+    return codes, blocks, scales

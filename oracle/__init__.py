@@ -17,6 +17,9 @@ Parity status of each step (see the pins under tests/):
   e4m3_value              pinned (all 256 codes vs torch.float8_e4m3fn)
   gather_dequant          pinned (raw bytes vs generator rows; rounding
                           properties against the exact rational sum)
+  e2m1_value,             pinned (OCP MX v1.0 E2M1 table; the E2M1 grid
+  gather_dequant_nvfp4    of the generator); x vs torch fp32 with nibble
+                          order and block placement checked
   ngram_ids_heads,        pinned (SplitMix64 published stream for the head
   gather_dequant_heads    offsets; heads 0/8 equal the 2-lookup IDs; raw
                           bytes vs generator; torch fp32 product; placement)
@@ -60,6 +63,8 @@ def _load():
             "oracle_head_mix": ([ctypes.c_uint64, ctypes.c_int32], ctypes.c_uint64),
             "oracle_ngram_ids_heads": ([_P, _P, _I32, _P, _P, _I64, _P], None),
             "oracle_gather_dequant_heads": ([_P, _I64, _P, _P, _P, _P], None),
+            "oracle_e2m1_value": ([ctypes.c_uint8], ctypes.c_double),
+            "oracle_gather_dequant_nvfp4": ([_P, _I64, _P, _P, _P, _P, _P], None),
             "oracle_hist_update": ([_P, _P, _I32, _P, _P, _P, _P], None),
             "oracle_e4m3_value": ([ctypes.c_uint8], ctypes.c_double),
             "oracle_bf16_rne": ([ctypes.c_float], ctypes.c_uint16),
@@ -166,6 +171,25 @@ def gather_dequant(row_ids, table, scales, raw: bool = False):
     return (x, r) if raw else x
 
 
+def e2m1_value(code: int) -> float:
+    return float(_load().oracle_e2m1_value(code))
+
+
+def gather_dequant_nvfp4(row_ids, codes, blocks, scales, raw: bool = False):
+    """x (bf16 bits [T][2560]) from NVFP4 rows: codes uint8[n][1280] (packed
+    E2M1, low nibble first), blocks uint8[n][160] (E4M3 per 16 elements),
+    scales float32[n]; row_ids [T][2] index them (-1 = missing)."""
+    row_ids = _c(row_ids, np.int32).reshape(-1, 2)
+    codes = _c(codes, np.uint8)
+    blocks = _c(blocks, np.uint8)
+    scales = _c(scales, np.float32)
+    T = row_ids.shape[0]
+    x = np.empty((T, D), dtype=np.uint16)
+    r = np.empty((T, 2, D // 2), dtype=np.uint8) if raw else None
+    _load().oracle_gather_dequant_nvfp4(_ptr(row_ids), T, _ptr(codes), _ptr(blocks), _ptr(scales), _ptr(x), _ptr(r))
+    return (x, r) if raw else x
+
+
 def gather_dequant_heads(idx, slices, scales, raw: bool = False):
     """x (bf16 bits [T][2560]) of the 16-lookup layout from 160-byte rows
     `slices` (uint8[n][160]) and `scales` (float32[n]); idx[t][h] indexes
@@ -247,6 +271,36 @@ def forward(tokens, cu_seqlens, h_bf16, W_bf16, conv_w_bf16, R: int, row_source,
     compact = np.full(row_ids.shape, -1, dtype=np.int32)
     compact[row_ids >= 0] = inv.astype(np.int32)
     x = gather_dequant(compact, codes, scales)
+    e = project(x, W_bf16)
+    e_b = round_bf16(e)
+    g = gate(h_bf16, e_b, eps)
+    y, out, st = conv_fuse(h_bf16, e_b, g, cu, conv_w_bf16, conv_state)
+    hid, hln = hist_update(tokens, cu, hist_ids, hist_len)
+    return dict(row_ids=row_ids, x=x, e=e, e_b=e_b, g=g, y=y, out=out,
+                hist_ids=hid, hist_len=hln, conv_state=st)
+
+
+def forward_nvfp4(tokens, cu_seqlens, h_bf16, W_bf16, conv_w_bf16, R: int, row_source,
+                  hist_ids=None, hist_len=None, conv_state=None, eps: float = 1e-6):
+    """forward() over the NVFP4 table: rows from row_source(ids) -> (codes
+    uint8[n][1280], blocks uint8[n][160], scales float32[n]); IDs, projection,
+    gate, conv and fuse as in forward()."""
+    tokens = _c(tokens, np.int32)
+    cu = _c(cu_seqlens, np.int32)
+    S = len(cu) - 1
+    if hist_ids is None:
+        hist_ids = np.zeros((S, 2), np.int32)
+    if hist_len is None:
+        hist_len = np.zeros(S, np.int32)
+    if conv_state is None:
+        conv_state = np.zeros((S, 3, D), np.float64)
+    row_ids = ngram_ids(tokens, cu, hist_ids, hist_len, R)
+    valid = row_ids[row_ids >= 0]
+    uniq, inv = np.unique(valid, return_inverse=True)
+    codes, blocks, scales = row_source(uniq)
+    compact = np.full(row_ids.shape, -1, dtype=np.int32)
+    compact[row_ids >= 0] = inv.astype(np.int32)
+    x = gather_dequant_nvfp4(compact, codes, blocks, scales)
     e = project(x, W_bf16)
     e_b = round_bf16(e)
     g = gate(h_bf16, e_b, eps)

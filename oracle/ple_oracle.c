@@ -225,6 +225,52 @@ void oracle_gather_dequant(const int32_t* row_ids, int64_t T, const uint8_t* tab
     }
 }
 
+/* OCP Microscaling formats (v1.0), FP4 E2M1: sign S, exponent E (2 bits,
+ * bias 1), mantissa M (1 bit); E = 0 is subnormal 0.5 * M, otherwise
+ * 2^(E-1) * (1 + M/2); no infinities or NaN. */
+double oracle_e2m1_value(uint8_t code) {
+    int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+    double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -v : v;
+}
+
+/* NVFP4 table (the Spark deployment's packed PLE table: 4-bit codes with an
+ * FP8 scale per group of 16): row r = 1280 bytes of E2M1 codes (element 2k
+ * in the low nibble of byte k), 160 E4M3FN block scales (block b covers
+ * elements 16b .. 16b+15) and the fp32 row scale. Per element
+ *   p = fl32( fl32( e2m1(code) * e4m3(block) ) * scale ),
+ * the inner product being exact (at most 2 x 4 significant bits); the two
+ * rows combine as in the FP8 table: x = bf16(fl32(p_bi + p_tri)), a missing
+ * row skipped. raw (optional) gets the rows' code bytes [T][2][1280]. */
+void oracle_gather_dequant_nvfp4(const int32_t* row_ids, int64_t T, const uint8_t* codes,
+                                 const uint8_t* blocks, const float* scales, uint16_t* x, uint8_t* raw) {
+    for (int64_t t = 0; t < T; ++t) {
+        int32_t rr[2] = {row_ids[2 * t], row_ids[2 * t + 1]};
+        for (int c = 0; c < D; ++c) {
+            float acc = 0.0f;
+            int have = 0;
+            for (int k = 0; k < 2; ++k) {
+                int32_t r = rr[k];
+                if (r < 0) continue;
+                uint8_t byte = codes[(int64_t)r * (D / 2) + c / 2];
+                uint8_t nib = (c & 1) ? (byte >> 4) : (byte & 15);
+                float q = (float)(oracle_e2m1_value(nib) * oracle_e4m3_value(blocks[(int64_t)r * (D / 16) + c / 16]));
+                float p = q * scales[r];
+                acc = have ? acc + p : p;
+                have = 1;
+            }
+            x[t * D + c] = oracle_bf16_rne(acc);
+        }
+        if (raw) {
+            for (int k = 0; k < 2; ++k) {
+                uint8_t* dst = raw + (t * 2 + k) * (D / 2);
+                if (rr[k] >= 0) memcpy(dst, codes + (int64_t)rr[k] * (D / 2), D / 2);
+                else memset(dst, 0, D / 2);
+            }
+        }
+    }
+}
+
 /* 16-lookup layout: x[t][160 h + j] = bf16( fl32(dec(code_h[j]) * scale_h) )
  * for a present head row, +0 for a missing one; `slices` holds the rows
  * referenced by idx[t][h] (uint8 [n][160]) with their scales. raw (optional)

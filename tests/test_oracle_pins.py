@@ -443,6 +443,90 @@ def test_conv_short_segments_carry_state():
 
 
 # ---------------------------------------------------------------------------
+# NVFP4 table (E2M1 codes, E4M3 scale per 16 elements, fp32 row scale)
+# ---------------------------------------------------------------------------
+
+def _e2m1_golden():
+    return {int(c, 16): float(v) for c, v in _golden("e2m1_ocp.txt")}
+
+
+def test_e2m1_values_match_ocp_table_and_generator_grid():
+    gold = _e2m1_golden()
+    assert len(gold) == 16
+    for c, v in gold.items():
+        got = oracle.e2m1_value(c)
+        assert got == v and math.copysign(1, got) == math.copysign(1, v), c
+    assert tuple(gold[c] for c in range(8)) == inputs.E2M1_GRID
+
+
+def _nvfp4_torch(ids, codes, blocks, scales):
+    """x by torch fp32 ops: E2M1 by table lookup, E4M3 by torch's float8."""
+    gold = _e2m1_golden()
+    lut = torch.tensor([gold[c] for c in range(16)], dtype=torch.float32)
+    c = torch.from_numpy(codes).to(torch.int64)
+    nib = torch.stack([c & 15, c >> 4], dim=-1).reshape(codes.shape[0], -1)   # element 2k = low nibble
+    q = lut[nib] * torch.from_numpy(blocks).view(torch.float8_e4m3fn).to(torch.float32).repeat_interleave(16, 1)
+    p = q * torch.from_numpy(scales)[:, None]
+    out = []
+    for r0, r1 in ids:
+        acc = None
+        for r in (r0, r1):
+            if r >= 0:
+                acc = p[r] if acc is None else acc + p[r]
+        acc = torch.zeros(D) if acc is None else acc
+        out.append(acc.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+    return np.stack(out)
+
+
+def test_gather_dequant_nvfp4_matches_torch_fp32():
+    rng = np.random.default_rng(70)
+    n = 40
+    codes = rng.integers(0, 256, (n, 1280), dtype=np.uint8)
+    blocks = rng.integers(0, 0x7F, (n, 160), dtype=np.uint8)          # positive, no NaN
+    blocks[:, ::7] |= 0x80                                              # and some negative
+    scales = rng.uniform(0.01, 0.1, n).astype(np.float32)
+    ids = rng.integers(-1, n, (30, 2)).astype(np.int32)
+    x, raw = oracle.gather_dequant_nvfp4(ids, codes, blocks, scales, raw=True)
+    assert np.array_equal(x, _nvfp4_torch(ids, codes, blocks, scales))
+    for t, (r0, r1) in enumerate(ids):
+        for k, r in enumerate((r0, r1)):
+            assert np.array_equal(raw[t, k], codes[r] if r >= 0 else np.zeros(1280, np.uint8))
+
+
+def test_gather_dequant_nvfp4_element_and_block_placement():
+    codes = np.zeros((1, 1280), np.uint8)
+    blocks = np.zeros((1, 160), np.uint8)
+    codes[0, 8] = 0x20            # element 17 (high nibble of byte 8) = E2M1 1.0
+    blocks[0, 1] = 0x38           # block 1 (elements 16..31) = E4M3 1.0
+    x = oracle.gather_dequant_nvfp4(np.array([[0, -1]], np.int32), codes, blocks, np.array([0.5], np.float32))
+    nz = np.flatnonzero(x[0] & 0x7FFF)
+    assert list(nz) == [17] and x[0, 17] == 0x3F00          # bf16 0.5
+
+
+def test_nvfp4_generator_codes_follow_the_e2m1_half_normal():
+    codes, blocks, scales = table.nvfp4_rows_cpu(np.arange(64))
+    nib = np.concatenate([(codes & 15).ravel(), (codes >> 4).ravel()])
+    freq = np.bincount(nib & 7, minlength=8) / nib.size
+    edges = [0.0] + [0.5 * (inputs.E2M1_GRID[k] + inputs.E2M1_GRID[k + 1]) / 2 for k in range(7)] + [math.inf]
+    want = [math.erf(edges[k + 1] / math.sqrt(2)) - math.erf(edges[k] / math.sqrt(2)) for k in range(8)]
+    assert np.allclose(freq, want, atol=0.01)
+    assert 0.45 < np.mean(nib >= 8) < 0.55
+    assert blocks.min() >= inputs.NVFP4_BLOCK_CODE_LO
+    assert blocks.max() < inputs.NVFP4_BLOCK_CODE_LO + inputs.NVFP4_BLOCK_CODES
+    _, sc = table.rows_cpu(np.arange(64))
+    assert np.array_equal(scales, sc)                         # the FP8 table's row scales
+
+
+def test_forward_nvfp4_fresh_sequence(weights):
+    W, cw = weights
+    toks, h = _small_stream(4, seed=71)
+    r = oracle.forward_nvfp4(toks, np.array([0, 4], np.int32), h, W, cw, 65_536, table.nvfp4_rows_cpu)
+    assert np.all(r["x"][0] == 0) and r["g"][0] == 0.5
+    assert np.array_equal(r["out"][0], inputs.bf16_bits_to_f32(h[0]).astype(np.float64))
+    assert np.any(r["x"][1] != 0)
+
+
+# ---------------------------------------------------------------------------
 # 16-lookup layout (16 head tables of 160-byte rows)
 # ---------------------------------------------------------------------------
 
