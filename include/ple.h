@@ -215,6 +215,39 @@ int ple_forward_heads_profiled(const ple_forward_args* args, void* stream, void*
 /* Workspace bytes ple_forward_heads needs for up to max_T tokens and max_S sequences. */
 size_t ple_forward_heads_workspace_size(int64_t max_T, int32_t max_S);
 
+/* ---- NVFP4 table ------------------------------------------------------------
+ * The Spark deployment's packed PLE table keeps 4-bit codes with an FP8
+ * scale per group of 16 elements (26.82 GiB for the 51.2 G elements).
+ * Reading fixed by this library: row r of R is
+ *   codes  uint8 [R][1280]  OCP E2M1 codes, element 2k in the low nibble of byte k
+ *   blocks uint8 [R][160]   E4M3FN scale of elements 16b .. 16b+15
+ *   scales float [R]        one fp32 scale per row (as for the FP8 table)
+ * and p = fl32(fl32(e2m1(code) * e4m3(block)) * scale) (the inner product is
+ * exact); the bigram and trigram rows combine as in the FP8 table:
+ * x = bf16_rne(fl32(p_bi + p_tri)), a missing row skipped. Row IDs, the
+ * projection, gate, conv and fuse are those of ple_forward. */
+
+/* a2 over the NVFP4 table.
+ *   row_ids int32 [T][2]             8-byte aligned
+ *   codes   uint8 [R][1280]          16-byte aligned
+ *   blocks  uint8 [R][160]           4-byte aligned
+ *   scales  float [R]
+ *   x_bf16  uint16 [T][2560]    out  16-byte aligned
+ *   raw_opt uint8 [T][2][1280]  out  optional: the two rows' code bytes, zero for -1
+ * Row ids outside [-1, R) are treated as -1 and flagged PLE_DEVERR_ROW_RANGE. */
+int ple_lookup_nvfp4(const int32_t* row_ids, int64_t T, const uint8_t* codes, const uint8_t* blocks,
+                     const float* scales, int64_t R, uint16_t* x_bf16, uint8_t* raw_opt, int32_t* dev_err,
+                     void* stream);
+
+/* a1..a4 over the NVFP4 table: ple_forward with args->table = codes
+ * [R][1280], args->scales = the row scales and `blocks` [R][160]; workspace
+ * of ple_forward_workspace_size bytes. */
+int ple_forward_nvfp4(const ple_forward_args* args, const uint8_t* blocks, void* stream);
+
+/* ple_forward_nvfp4 with the five timing events of ple_forward_profiled. */
+int ple_forward_nvfp4_profiled(const ple_forward_args* args, const uint8_t* blocks, void* stream,
+                               void* const* events);
+
 /* Static description of a status code. */
 const char* ple_status_string(int status);
 

@@ -63,6 +63,7 @@ _lib = None
 EXPORTS = ("ple_hash", "ple_lookup", "ple_proj", "ple_forward", "ple_forward_profiled",
            "ple_forward_workspace_size", "ple_hash_heads", "ple_lookup_heads", "ple_forward_heads",
            "ple_forward_heads_profiled", "ple_forward_heads_workspace_size", "ple_forward_x",
+           "ple_lookup_nvfp4", "ple_forward_nvfp4", "ple_forward_nvfp4_profiled",
            "ple_status_string", "ple_last_error")
 HEADS = 16            # 16-lookup layout: head tables of 160-byte rows
 SLICE = D // HEADS
@@ -94,6 +95,12 @@ def load_library(path: str = LIB_PATH):
         getattr(lib, name).restype = ctypes.c_int
     lib.ple_forward_x.argtypes = [ctypes.POINTER(ForwardArgs), _P, _P]
     lib.ple_forward_x.restype = ctypes.c_int
+    lib.ple_lookup_nvfp4.argtypes = [_P, I64, _P, _P, _P, I64, _P, _P, _P, _P]
+    lib.ple_lookup_nvfp4.restype = ctypes.c_int
+    lib.ple_forward_nvfp4.argtypes = [ctypes.POINTER(ForwardArgs), _P, _P]
+    lib.ple_forward_nvfp4.restype = ctypes.c_int
+    lib.ple_forward_nvfp4_profiled.argtypes = [ctypes.POINTER(ForwardArgs), _P, _P, ctypes.POINTER(_P)]
+    lib.ple_forward_nvfp4_profiled.restype = ctypes.c_int
     for name in ("ple_forward_workspace_size", "ple_forward_heads_workspace_size"):
         getattr(lib, name).argtypes = [I64, I32]
         getattr(lib, name).restype = ctypes.c_size_t
@@ -195,6 +202,21 @@ def ple_lookup(row_ids, table, scales, x=None, raw=None, dev_err=None, stream=No
     return x
 
 
+def ple_lookup_nvfp4(row_ids, codes, blocks, scales, x=None, raw=None, dev_err=None, stream=None):
+    """a2 over the NVFP4 table: codes uint8 [R][1280], blocks uint8 [R][160],
+    scales float32 [R]; raw (optional) uint8 [T][2][1280]."""
+    T = row_ids.shape[0]
+    R = scales.shape[0]
+    if x is None:
+        x = torch.empty((T, D), dtype=torch.bfloat16, device=row_ids.device)
+    _check(load_library().ple_lookup_nvfp4(
+        _dev(row_ids, "row_ids", torch.int32, (T, 2)), T, _dev(codes, "codes", torch.uint8, (R, D // 2)),
+        _dev(blocks, "blocks", torch.uint8, (R, D // 16)), _dev(scales, "scales", torch.float32, (R,)), R,
+        _dev(x, "x", torch.bfloat16, (T, D)), _opt(raw, "raw", torch.uint8, (T, 2, D // 2)),
+        _opt(dev_err, "dev_err", torch.int32, (1,)), _stream(stream)))
+    return x
+
+
 def ple_proj(x, W, e=None, stream=None):
     """a3: e fp32 [T][2560] = x W^T."""
     T = x.shape[0]
@@ -244,15 +266,20 @@ class Workspace:
 
 def ple_forward(tokens, cu_seqlens, table, scales, W, conv_w, h, state: State, out=None,
                 workspace=None, vocab_size: int = DEFAULT_VOCAB, eps: float = DEFAULT_EPS,
-                dev_err=None, debug: bool = False, stream=None, events=None, heads: bool = False):
+                dev_err=None, debug: bool = False, stream=None, events=None, heads: bool = False,
+                nvfp4_blocks=None):
     """a1..a4 for one chunk. Updates `state` in place; returns out (bf16
     [T][2560]) or, with debug=True, a dict with out, row_ids, x, e, gate, y.
     `events`: optional sequence of five hipEvent_t handles (ints) recorded
     around the four kernels (ple_forward_profiled). heads=True: the 16-lookup
-    layout (scales [16][R], row_ids [T][16])."""
+    layout (scales [16][R], row_ids [T][16]). nvfp4_blocks (uint8 [R][160]):
+    the NVFP4 table, `table` then being the packed codes uint8 [R][1280]."""
     T = tokens.numel()
     S = cu_seqlens.numel() - 1
-    R = _rows_of(table, scales, heads)
+    nv = nvfp4_blocks is not None
+    if nv and heads:
+        raise ValueError("the NVFP4 table is read with two lookups per token")
+    R = scales.shape[0] if nv else _rows_of(table, scales, heads)
     n = HEADS if heads else 2
     dev = tokens.device
     if out is None:
@@ -273,7 +300,7 @@ def ple_forward(tokens, cu_seqlens, table, scales, W, conv_w, h, state: State, o
     a.cu_seqlens = _dev(cu_seqlens, "cu_seqlens", torch.int32, (S + 1,))
     a.S = S
     a.vocab_size = vocab_size
-    a.table = _table(table, R)
+    a.table = _dev(table, "table", torch.uint8, (R, D // 2)) if nv else _table(table, R)
     a.scales = _dev(scales, "scales", torch.float32, (HEADS, R) if heads else (R,))
     a.R = R
     a.W = _dev(W, "W", torch.bfloat16, (D, D))
@@ -294,10 +321,16 @@ def ple_forward(tokens, cu_seqlens, table, scales, W, conv_w, h, state: State, o
         a.gate_out = dbg["gate"].data_ptr()
         a.y_out = dbg["y"].data_ptr()
     lib = load_library()
-    if events is None:
+    ev = None if events is None else (_P * 5)(*[ctypes.c_void_p(int(e)) for e in events])
+    if nv:
+        blk = _dev(nvfp4_blocks, "nvfp4_blocks", torch.uint8, (R, D // 16))
+        if ev is None:
+            _check(lib.ple_forward_nvfp4(ctypes.byref(a), blk, _stream(stream)))
+        else:
+            _check(lib.ple_forward_nvfp4_profiled(ctypes.byref(a), blk, _stream(stream), ev))
+    elif ev is None:
         _check((lib.ple_forward_heads if heads else lib.ple_forward)(ctypes.byref(a), _stream(stream)))
     else:
-        ev = (_P * 5)(*[ctypes.c_void_p(int(e)) for e in events])
         f = lib.ple_forward_heads_profiled if heads else lib.ple_forward_profiled
         _check(f(ctypes.byref(a), _stream(stream), ev))
     if debug:

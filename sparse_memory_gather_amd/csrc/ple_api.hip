@@ -207,6 +207,28 @@ int ple_lookup_heads(const int32_t* row_ids, int64_t T, const uint8_t* table, co
     return lookup_impl(row_ids, T, table, scales, R, x_bf16, raw_opt, dev_err, stream, true);
 }
 
+int ple_lookup_nvfp4(const int32_t* row_ids, int64_t T, const uint8_t* codes, const uint8_t* blocks,
+                     const float* scales, int64_t R, uint16_t* x_bf16, uint8_t* raw_opt, int32_t* dev_err,
+                     void* stream) {
+    if (T < 0) return fail(PLE_ERR_SHAPE, "T = %lld < 0", (long long)T);
+    if (int st = check_R(R)) return st;
+    if (T == 0) return ok();
+    if (!row_ids || !codes || !blocks || !scales || !x_bf16)
+        return fail(PLE_ERR_NULL, "ple_lookup_nvfp4: a required pointer is NULL");
+    if (!aligned(row_ids, 8) || !aligned(codes, 16) || !aligned(blocks, 4) || !aligned(scales, 4) ||
+        !aligned(x_bf16, 16) || !aligned(raw_opt, 16) || !aligned(dev_err, 4))
+        return fail(PLE_ERR_ALIGN, "ple_lookup_nvfp4: misaligned pointer");
+    Range r[] = {rng("row_ids", row_ids, (size_t)T * 8, false), rng("codes", codes, (size_t)R * (kD / 2), false),
+                 rng("blocks", blocks, (size_t)R * (kD / 16), false), rng("scales", scales, (size_t)R * 4, false),
+                 rng("x", x_bf16, (size_t)T * kD * 2, true), rng("raw", raw_opt, (size_t)T * kD, true),
+                 rng("dev_err", dev_err, 4, true)};
+    if (int st = check_alias(r, 7)) return st;
+    hipError_t e = launch_gather_nvfp4(row_ids, T, codes, blocks, scales, R, x_bf16, raw_opt, dev_err,
+                                       reinterpret_cast<hipStream_t>(stream));
+    if (int st = hip_status(e, "ple_lookup_nvfp4 launch")) return st;
+    return ok();
+}
+
 int ple_proj(const uint16_t* x_bf16, int64_t T, const uint16_t* W_bf16, float* e, void* stream) {
     if (T < 0) return fail(PLE_ERR_SHAPE, "T = %lld < 0", (long long)T);
     if (T == 0) return ok();
@@ -226,8 +248,9 @@ int ple_proj(const uint16_t* x_bf16, int64_t T, const uint16_t* W_bf16, float* e
 
 // x_in != NULL: ple_forward_x (x given; no ID or gather kernel, table,
 // scales, R and vocab_size unused)
+// nv_blocks != NULL: NVFP4 table (table = codes [R][1280], nv_blocks [R][160])
 static int forward_impl(const ple_forward_args* a, void* stream, void* const* events, bool heads,
-                        const uint16_t* x_in = nullptr) {
+                        const uint16_t* x_in = nullptr, const uint8_t* nv_blocks = nullptr) {
     if (!a) return fail(PLE_ERR_NULL, "ple_forward: args is NULL");
     const bool from_x = x_in != nullptr;
     const int64_t T = a->T;
@@ -262,7 +285,8 @@ static int forward_impl(const ple_forward_args* a, void* stream, void* const* ev
     Range r[] = {
         rng("tokens", a->tokens, T * 4, false),
         rng("cu_seqlens", a->cu_seqlens, (S + 1) * 4ull, false),
-        rng("table", from_x ? nullptr : a->table, (size_t)a->R * kD, false),
+        rng("table", from_x ? nullptr : a->table, (size_t)a->R * (nv_blocks ? kD / 2 : kD), false),
+        rng("nvfp4_blocks", nv_blocks, (size_t)a->R * (kD / 16), false),
         rng("scales", from_x ? nullptr : a->scales, (size_t)a->R * (heads ? 16 : 1) * 4, false),
         rng("x", x_in, (size_t)T * kD * 2, false),
         rng("W", a->W, (size_t)kD * kD * 2, false),
@@ -305,8 +329,10 @@ static int forward_impl(const ple_forward_args* a, void* stream, void* const* ev
     }
     if (int st = hip_status(mark(1), "ple_forward: event record")) return st;
     if (!from_x) {
-        e = heads ? launch_gather_heads(row_ids, T, a->table, a->scales, a->R, x, nullptr, a->dev_err, s)
-                  : launch_gather(row_ids, T, a->table, a->scales, a->R, x, nullptr, a->dev_err, s);
+        e = nv_blocks ? launch_gather_nvfp4(row_ids, T, a->table, nv_blocks, a->scales, a->R, x, nullptr,
+                                            a->dev_err, s)
+            : heads   ? launch_gather_heads(row_ids, T, a->table, a->scales, a->R, x, nullptr, a->dev_err, s)
+                      : launch_gather(row_ids, T, a->table, a->scales, a->R, x, nullptr, a->dev_err, s);
         if (int st = hip_status(e, "ple_forward: gather launch")) return st;
     }
     if (int st = hip_status(mark(2), "ple_forward: event record")) return st;
@@ -343,6 +369,20 @@ int ple_forward_heads(const ple_forward_args* a, void* stream) {
 int ple_forward_heads_profiled(const ple_forward_args* a, void* stream, void* const* events) {
     if (int st = check_events(events)) return st;
     return forward_impl(a, stream, events, true);
+}
+
+int ple_forward_nvfp4(const ple_forward_args* a, const uint8_t* blocks, void* stream) {
+    if (!blocks) return fail(PLE_ERR_NULL, "ple_forward_nvfp4: blocks is NULL");
+    if (!aligned(blocks, 4)) return fail(PLE_ERR_ALIGN, "ple_forward_nvfp4: blocks is not 4-byte aligned");
+    return forward_impl(a, stream, nullptr, false, nullptr, blocks);
+}
+
+int ple_forward_nvfp4_profiled(const ple_forward_args* a, const uint8_t* blocks, void* stream,
+                               void* const* events) {
+    if (int st = check_events(events)) return st;
+    if (!blocks) return fail(PLE_ERR_NULL, "ple_forward_nvfp4: blocks is NULL");
+    if (!aligned(blocks, 4)) return fail(PLE_ERR_ALIGN, "ple_forward_nvfp4: blocks is not 4-byte aligned");
+    return forward_impl(a, stream, events, false, nullptr, blocks);
 }
 
 int ple_forward_x(const ple_forward_args* a, const uint16_t* x_bf16, void* stream) {

@@ -166,7 +166,99 @@ gather_heads_kernel(const int32_t* __restrict__ row_ids, int64_t T, const uint8_
     }
 }
 
+// NVFP4 table (the Spark deployment's packed PLE table: 4-bit codes with an
+// FP8 scale per group of 16): row r = 1280 bytes of OCP E2M1 codes (element
+// 2k in the low nibble of byte k), 160 E4M3 block scales (block b covers
+// elements 16b .. 16b+15) and the fp32 row scale;
+//   p = fl32(fl32(e2m1 * e4m3) * scale)   (the inner product exact),
+// the two rows combined as in the FP8 table. Same wave-per-token plan: lane
+// l of span s covers elements 512s + 8l .. +7, i.e. code word 64s + l and
+// block 32s + l/2 of each row. E2M1 pairs are decoded by
+// v_cvt_scalef32_pk_f32_fp4 with scale 1.0 (exact; low nibble first).
+__device__ __forceinline__ void decode_nvfp4(uint32_t w, float block, float s, float out[8]) {
+#pragma clang fp contract(off)
+    const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    const float e[8] = {v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float q = e[i] * block;
+        out[i] = q * s;
+    }
+}
+
+__global__ void __launch_bounds__(64 * kTokPerBlock)
+gather_nvfp4_kernel(const int32_t* __restrict__ row_ids, int64_t T, const uint8_t* __restrict__ codes,
+                    const uint8_t* __restrict__ blocks, const float* __restrict__ scales, int64_t R,
+                    uint16_t* __restrict__ x, uint8_t* __restrict__ raw, int32_t* dev_err) {
+#pragma clang fp contract(off)
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
+    if (t >= T) return;
+    int2 ids = reinterpret_cast<const int2*>(row_ids)[t];
+    int r0 = __builtin_amdgcn_readfirstlane(ids.x);
+    int r1 = __builtin_amdgcn_readfirstlane(ids.y);
+    if (r0 < -1 || (int64_t)r0 >= R) {
+        if (lane == 0) flag_error(dev_err, 8);
+        r0 = -1;
+    }
+    if (r1 < -1 || (int64_t)r1 >= R) {
+        if (lane == 0) flag_error(dev_err, 8);
+        r1 = -1;
+    }
+    const bool v0 = r0 >= 0, v1 = r1 >= 0;
+    const uint32_t* c0 = reinterpret_cast<const uint32_t*>(codes + (int64_t)(v0 ? r0 : 0) * (kD / 2)) + lane;
+    const uint32_t* c1 = reinterpret_cast<const uint32_t*>(codes + (int64_t)(v1 ? r1 : 0) * (kD / 2)) + lane;
+    const uint8_t* b0 = blocks + (int64_t)(v0 ? r0 : 0) * (kD / 16) + lane / 2;
+    const uint8_t* b1 = blocks + (int64_t)(v1 ? r1 : 0) * (kD / 16) + lane / 2;
+    uint32_t a[kSpans], b[kSpans], ba[kSpans], bb[kSpans];
+#pragma unroll
+    for (int s = 0; s < kSpans; ++s) {
+        a[s] = v0 ? c0[s * 64] : 0u;
+        b[s] = v1 ? c1[s * 64] : 0u;
+        ba[s] = v0 ? b0[s * 32] : 0u;
+        bb[s] = v1 ? b1[s * 32] : 0u;
+    }
+    const float s0 = v0 ? scales[r0] : 0.0f;
+    const float s1 = v1 ? scales[r1] : 0.0f;
+    u32x4* xrow = reinterpret_cast<u32x4*>(x + t * kD) + lane;
+#pragma unroll
+    for (int s = 0; s < kSpans; ++s) {
+        const float blk0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)ba[s], false)[0];
+        const float blk1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)bb[s], false)[0];
+        float pa[8], pb[8], acc[8];
+        decode_nvfp4(a[s], blk0, s0, pa);
+        decode_nvfp4(b[s], blk1, s1, pb);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = v0 ? (v1 ? pa[i] + pb[i] : pa[i]) : (v1 ? pb[i] : 0.0f);
+        u32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+        __builtin_nontemporal_store(o, xrow + s * 64);
+    }
+    if (raw) {
+        uint32_t* d0 = reinterpret_cast<uint32_t*>(raw + (t * 2 + 0) * (kD / 2)) + lane;
+        uint32_t* d1 = reinterpret_cast<uint32_t*>(raw + (t * 2 + 1) * (kD / 2)) + lane;
+#pragma unroll
+        for (int s = 0; s < kSpans; ++s) {
+            d0[s * 64] = a[s];
+            d1[s * 64] = b[s];
+        }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_gather_nvfp4(const int32_t* row_ids, int64_t T, const uint8_t* codes, const uint8_t* blocks,
+                               const float* scales, int64_t R, uint16_t* x, uint8_t* raw, int32_t* dev_err,
+                               hipStream_t stream) {
+    int64_t blocks_n = (T + kTokPerBlock - 1) / kTokPerBlock;
+    hipLaunchKernelGGL(gather_nvfp4_kernel, dim3((unsigned)blocks_n), dim3(64 * kTokPerBlock), 0, stream, row_ids,
+                       T, codes, blocks, scales, R, x, raw, dev_err);
+    return hipGetLastError();
+}
 
 hipError_t launch_gather_heads(const int32_t* row_ids, int64_t T, const uint8_t* table,
                                const float* scales, int64_t R, uint16_t* x, uint8_t* raw,

@@ -38,6 +38,12 @@ hipError_t launch_hash(const int32_t* tokens, int64_t T, const int32_t* cu, int3
                        int32_t* row_ids, int32_t* dev_err, const float* conv_state,
                        float* state_snap, bool heads, hipStream_t stream);
 
+// NVFP4 table: codes [R][1280] (E2M1, low nibble first), blocks [R][160]
+// (E4M3 per 16 elements), scales [R]; raw (optional) [T][2][1280]
+hipError_t launch_gather_nvfp4(const int32_t* row_ids, int64_t T, const uint8_t* codes, const uint8_t* blocks,
+                               const float* scales, int64_t R, uint16_t* x, uint8_t* raw, int32_t* dev_err,
+                               hipStream_t stream);
+
 // copy of conv_state [S][3][kD] into state_snap
 hipError_t launch_state_copy(const float* conv_state, float* state_snap, int32_t S, hipStream_t stream);
 

@@ -22,7 +22,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(ple.LIB_PATH), reason="libple
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(ple_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(ple_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_declarations_are_exported():
