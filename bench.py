@@ -44,6 +44,9 @@ GATHER_BYTES_PER_TOKEN = 8 + 2 * D
 # token 64 B of row ids and 5120 B of bf16 x
 HEADS_BYTES_PER_LOOKUP = 160 + 4
 HEADS_BYTES_PER_TOKEN = 64 + 2 * D
+# NVFP4 table: per valid lookup 1280 B of E2M1 codes + 160 B of E4M3 block
+# scales + 4 B row scale; per token as the FP8 table
+NVFP4_BYTES_PER_LOOKUP = D // 2 + D // 16 + 4
 PROJ_FLOP_PER_TOKEN = 2 * D * D
 FUSE_BYTES_PER_TOKEN = 3 * 2 * D
 
@@ -52,6 +55,8 @@ KERNEL_SOURCES = {
     "proj_kernel": ["sparse_memory_gather_amd/csrc/ple_proj.hip", "sparse_memory_gather_amd/csrc/ple_kernels.h"],
     "gather_kernel": ["sparse_memory_gather_amd/csrc/ple_gather.hip", "sparse_memory_gather_amd/csrc/ple_kernels.h"],
     "gather_heads_kernel": ["sparse_memory_gather_amd/csrc/ple_gather.hip",
+                            "sparse_memory_gather_amd/csrc/ple_kernels.h"],
+    "gather_nvfp4_kernel": ["sparse_memory_gather_amd/csrc/ple_gather.hip",
                             "sparse_memory_gather_amd/csrc/ple_kernels.h"],
     "fuse_kernel": ["sparse_memory_gather_amd/csrc/ple_fuse.hip", "sparse_memory_gather_amd/csrc/ple_kernels.h"],
 }
@@ -109,9 +114,13 @@ class HipEvents:
         return float(ms.value)
 
 
-def describe(name, wl, heads=False):
-    if heads:
+def describe(name, wl, layout="two"):
+    if layout == "heads":
         return describe(name, wl) + ", read as 16 head tables of 160-byte rows (16 lookups per token)"
+    if layout == "nvfp4":
+        return (describe(name, wl).replace("FP8 E4M3 table (51.2 GB)", "NVFP4 table (28.9 GB)")
+                .replace("FP8 table", "NVFP4 table")
+                + "; NVFP4 rows: 1280 B of E2M1 codes, 160 E4M3 scales per 16 elements, fp32 row scale")
     T = len(wl.chunks[0][0])
     if name == "prefill":
         return f"prefill: 1 sequence x 32768 Zipf(1.1) tokens, {wl.R:,}-row x 2560 FP8 E4M3 table (51.2 GB) in HBM"
@@ -124,7 +133,7 @@ def describe(name, wl, heads=False):
     return f"tiny: 1 x {T} uniform tokens, {wl.R:,}-row FP8 table"
 
 
-def cpu_baseline(wl, name, W, cw, h0, budget_s=12.0, heads=False):
+def cpu_baseline(wl, name, W, cw, h0, budget_s=12.0, layout="two"):
     """The CPU oracle (as it stands) on the first N tokens of the workload's
     first chunk, N sized so that the run takes about `budget_s` seconds."""
     import numpy as np
@@ -139,7 +148,10 @@ def cpu_baseline(wl, name, W, cw, h0, budget_s=12.0, heads=False):
         # the first n tokens, cut at the same sequence boundaries
         cut = np.minimum(cu, n).astype(np.int32)
         t0 = time.perf_counter()
-        if heads:
+        if layout == "nvfp4":
+            oracle.forward_nvfp4(toks[:n], cut, h0[:n], W, cw, wl.R, table.nvfp4_rows_cpu,
+                                 np.zeros((S, 2), np.int32), np.zeros(S, np.int32), np.zeros((S, 3, D)))
+        elif layout == "heads":
             oracle.forward_heads(toks[:n], cut, h0[:n], W, cw, wl.R,
                                  lambda hs, rs: table.slices_cpu(hs, rs, wl.R),
                                  np.zeros((S, 2), np.int32), np.zeros(S, np.int32), np.zeros((S, 3, D)))
@@ -167,8 +179,9 @@ def main():
     ap.add_argument("--workload", default="prefill", choices=["tiny", "decode", "prefill", "ragged", "long"])
     ap.add_argument("--overlap", action="store_true",
                     help="long workload: IDs and rows of the next chunk on a second stream (ple_forward_x)")
-    ap.add_argument("--layout", default="two", choices=["two", "heads"],
-                    help="two: 2 lookups of 2560-byte rows per token; heads: 16 lookups of 160-byte rows")
+    ap.add_argument("--layout", default="two", choices=["two", "heads", "nvfp4"],
+                    help="two: 2 lookups of 2560-byte FP8 rows per token; heads: 16 lookups of 160-byte "
+                         "rows; nvfp4: 2 lookups of NVFP4 rows (E2M1 codes, E4M3 scale per 16 elements)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -196,8 +209,13 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
     print(f"[bench] {name}: generating the {wl.R:,}-row table", file=sys.stderr, flush=True)
-    tab, sc = table.table_gpu(wl.R, device=dev)
     heads = args.layout == "heads"
+    nvfp4 = args.layout == "nvfp4"
+    blocks = None
+    if nvfp4:
+        tab, blocks, sc = table.nvfp4_gpu(wl.R, device=dev)
+    else:
+        tab, sc = table.table_gpu(wl.R, device=dev)
     if heads:
         sc = table.head_scales_gpu(wl.R, device=dev)
     Wd, cwd = bf16(W), bf16(cw)
@@ -221,7 +239,7 @@ def main():
         hh = bf16(wl.history_hidden(hist.size))
         cu_h = torch.arange(0, hist.size + 1, hist.shape[1], dtype=torch.int32, device=dev)
         ple.ple_forward(torch.from_numpy(hist.reshape(-1)).to(dev), cu_h, tab, sc, Wd, cwd, hh, state,
-                        workspace=ws, heads=heads)
+                        workspace=ws, heads=heads, nvfp4_blocks=blocks)
         del hh
     outs = [torch.empty_like(b[2]) for b in batches] if name in ("long", "decode") else \
         [torch.empty_like(batches[0][2])]
@@ -259,7 +277,10 @@ def main():
                     side.wait_event(free[j])
                     hl = hl0 if (k == 0 and i == 0) else hl2
                     ple.ple_hash(t, c, hists[i], hl, wl.R, row_ids=rbuf[j], heads=heads)
-                    ple.ple_lookup(rbuf[j], tab, sc, x=xbuf[j], heads=heads)
+                    if nvfp4:
+                        ple.ple_lookup_nvfp4(rbuf[j], tab, blocks, sc, x=xbuf[j])
+                    else:
+                        ple.ple_lookup(rbuf[j], tab, sc, x=xbuf[j], heads=heads)
                     ready[j].record(side)
                 with torch.cuda.stream(main):
                     main.wait_event(ready[j])
@@ -269,18 +290,20 @@ def main():
     elif name == "long":
         def step(k, events=None):
             for (t, c, h), o in zip(batches, outs):
-                ple.ple_forward(t, c, tab, sc, Wd, cwd, h, state, out=o, workspace=ws, events=events, heads=heads)
+                ple.ple_forward(t, c, tab, sc, Wd, cwd, h, state, out=o, workspace=ws, events=events, heads=heads,
+                                nvfp4_blocks=blocks)
         tokens_per_step = sum(b[0].numel() for b in batches)
     elif name == "decode":
         def step(k, events=None):
             t, c, h = batches[k % len(batches)]
             ple.ple_forward(t, c, tab, sc, Wd, cwd, h, state, out=outs[k % len(outs)], workspace=ws,
-                            events=events, heads=heads)
+                            events=events, heads=heads, nvfp4_blocks=blocks)
         tokens_per_step = batches[0][0].numel()
     else:
         def step(k, events=None):
             t, c, h = batches[0]
-            ple.ple_forward(t, c, tab, sc, Wd, cwd, h, state, out=outs[0], workspace=ws, events=events, heads=heads)
+            ple.ple_forward(t, c, tab, sc, Wd, cwd, h, state, out=outs[0], workspace=ws, events=events, heads=heads,
+                            nvfp4_blocks=blocks)
         tokens_per_step = batches[0][0].numel()
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
@@ -308,7 +331,8 @@ def main():
         if name == "long":
             for j, ((t, c, h), o) in enumerate(zip(batches, outs)):
                 ple.ple_forward(t, c, tab, sc, Wd, cwd, h, state, out=o, workspace=ws,
-                                events=ev[k * n_calls + j], heads=heads)
+                                events=ev[k * n_calls + j], heads=heads,
+                                nvfp4_blocks=blocks)
         else:
             step(k, events=ev[k])
     torch.cuda.synchronize()
@@ -330,6 +354,8 @@ def main():
         unique_rows = int(torch.unique(rid[rid >= 0]).numel()) if name != "decode" else None
     if heads:
         gather_bytes = lookups * HEADS_BYTES_PER_LOOKUP + tokens_per_call * HEADS_BYTES_PER_TOKEN
+    elif nvfp4:
+        gather_bytes = lookups * NVFP4_BYTES_PER_LOOKUP + tokens_per_call * GATHER_BYTES_PER_TOKEN
     else:
         gather_bytes = lookups * GATHER_BYTES_PER_LOOKUP + tokens_per_call * GATHER_BYTES_PER_TOKEN
     gather_gbs = gather_bytes / (stage_us[1] * 1e-6) / 1e9
@@ -338,6 +364,7 @@ def main():
     fuse_bytes = tokens_per_call * FUSE_BYTES_PER_TOKEN
     fuse_gbs = fuse_bytes / (stage_us[3] * 1e-6) / 1e9
 
+    gather_name = "gather_heads_kernel" if heads else "gather_nvfp4_kernel" if nvfp4 else "gather_kernel"
     dominant = int(np.argmax(stage_us))
     if dominant == 2:
         roofline = {"kernel": "ple_proj (proj_kernel, forward variant)", "bound": "mfma",
@@ -346,10 +373,10 @@ def main():
                     "traffic": recorded_traffic("proj_kernel", name),
                     "per_launch": {"flop": proj_flop, "avg_us": round(float(stage_us[2]), 2)}}
     elif dominant == 1:
-        roofline = {"kernel": "ple_gather_dequant (gather_kernel)", "bound": "hbm",
+        roofline = {"kernel": f"ple_gather_dequant ({gather_name})", "bound": "hbm",
                     "achieved": round(gather_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(gather_gbs / HBM_PEAK_GBS, 4),
-                    "traffic": recorded_traffic("gather_heads_kernel" if heads else "gather_kernel", name),
+                    "traffic": recorded_traffic(gather_name, name),
                     "per_launch": {"bytes": gather_bytes, "avg_us": round(float(stage_us[1]), 2)}}
     else:
         k = ["ple_hash (hash_kernel)", "", "", "ple_gate_conv_fuse (fuse_kernel)"][dominant]
@@ -365,11 +392,12 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": describe(name, wl, heads) + (
+        "config": {"workload": describe(name, wl, args.layout) + (
                        "; IDs and rows of the next chunk gathered on a second stream during the current one"
                        if args.overlap and name == "long" else ""), "name": name, "layout": args.layout,
                    "tokens_per_step": tokens_per_step,
-                   "sequences": wl.S, "table_rows": wl.R, "table_bytes": wl.R * D},
+                   "sequences": wl.S, "table_rows": wl.R,
+                   "table_bytes": wl.R * (NVFP4_BYTES_PER_LOOKUP if nvfp4 else D + (64 if heads else 4))},
         "roofline": roofline,
         "stages_us": {"hash": round(float(stage_us[0]), 2), "gather": round(float(stage_us[1]), 2),
                       "proj": round(float(stage_us[2]), 2), "fuse": round(float(stage_us[3]), 2)},
@@ -379,7 +407,7 @@ def main():
                    "unit": "GB/s", "frac": round(gather_gbs / HBM_PEAK_GBS, 4),
                    "bytes_per_launch": gather_bytes, "lookups_per_launch": lookups,
                    "unique_rows_per_launch": unique_rows,
-                   "traffic": recorded_traffic("gather_heads_kernel" if heads else "gather_kernel", name)},
+                   "traffic": recorded_traffic(gather_name, name)},
         "proj": {"bound": "mfma", "achieved": round(proj_tflops, 2), "peak": BF16_PEAK_TFLOPS,
                  "unit": "TFLOP/s", "frac": round(proj_tflops / BF16_PEAK_TFLOPS, 4)},
         "fuse": {"bound": "hbm", "achieved": round(fuse_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -388,11 +416,11 @@ def main():
     }
     if not args.no_cpu_baseline and h0 is not None:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(wl, name, W, cw, h0, args.cpu_budget, heads)
+        result["cpu_baseline"] = cpu_baseline(wl, name, W, cw, h0, args.cpu_budget, args.layout)
     elif not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         h0 = wl.hidden(0)
-        result["cpu_baseline"] = cpu_baseline(wl, name, W, cw, h0, args.cpu_budget, heads)
+        result["cpu_baseline"] = cpu_baseline(wl, name, W, cw, h0, args.cpu_budget, args.layout)
     if args.copy_calibration:
         # a plain copy of known size: FETCH_SIZE / WRITE_SIZE of this dispatch
         # calibrate the per-kernel counters to bytes

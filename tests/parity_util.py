@@ -115,7 +115,7 @@ def head_rows(R: int):
     return lambda hs, rs: table.slices_cpu(hs, rs, R)
 
 
-def oracle_samples(seqs, samples, W, cw, R, eps=1e-6, heads: bool = False):
+def oracle_samples(seqs, samples, W, cw, R, eps=1e-6, heads: bool = False, nvfp4: bool = False):
     """Reference outputs of sampled tokens.
 
     seqs: list of (tokens int32[n], h bf16 bits [n][D]) — whole sequences
@@ -139,7 +139,12 @@ def oracle_samples(seqs, samples, W, cw, R, eps=1e-6, heads: bool = False):
         hid.append(hist)
         hln.append(k)
     S = len(samples)
-    fwd, src = (oracle.forward_heads, head_rows(R)) if heads else (oracle.forward, rows)
+    if nvfp4:
+        fwd, src = oracle.forward_nvfp4, table.nvfp4_rows_cpu
+    elif heads:
+        fwd, src = oracle.forward_heads, head_rows(R)
+    else:
+        fwd, src = oracle.forward, rows
     r = fwd(np.concatenate(toks), np.array(cu, np.int32), np.concatenate(hs), W, cw, R,
             src, np.array(hid, np.int32), np.array(hln, np.int32), np.zeros((S, 3, D)), eps)
     last = np.array(cu[1:]) - 1

@@ -183,6 +183,34 @@ def test_prefill_heads_layout(dev, full_table, dev_weights, weights):
     del sc16
 
 
+def test_prefill_nvfp4_table(dev, dev_weights, weights):
+    # the NVFP4 table at the full row count: 20,000,096 rows x (1280 code
+    # bytes + 160 block scales + 4-byte row scale) = 28.9 GB in HBM
+    W, cw = weights
+    R = inputs.R_FULL
+    codes, blocks, scales = table.nvfp4_gpu(R, device=dev)
+    rng = np.random.default_rng(19)
+    ids = np.concatenate([rng.integers(0, R, 2000), [0, R - 1]])
+    c, b, s = table.nvfp4_rows_cpu(ids)
+    it = torch.as_tensor(ids, device=dev)
+    assert np.array_equal(codes[it].cpu().numpy(), c)
+    assert np.array_equal(blocks[it].cpu().numpy(), b)
+    assert np.array_equal(scales[it].cpu().numpy(), s)
+    wl = inputs.make_workload("prefill")
+    toks, cu = wl.chunks[0]
+    h = wl.hidden(0)
+    st = ple.State(1, dev)
+    res = ple.ple_forward(dev_i32(toks, dev), dev_i32(cu, dev), codes, scales, dev_weights[0], dev_weights[1],
+                          dev_bf16(h, dev), st, debug=True, nvfp4_blocks=blocks)
+    ref_ids = oracle.ngram_ids(toks, cu, np.zeros((1, 2), np.int32), np.zeros(1, np.int32), R)
+    assert np.array_equal(res["row_ids"].cpu().numpy(), ref_ids)
+    pos = sorted(set([0, 1, 2, 3, len(toks) - 1] + _interior(rng, 4, len(toks) - 1, 8)))
+    ref = oracle_samples([(toks, h)], [(0, p) for p in pos], W, cw, R, nvfp4=True)
+    print("prefill nvfp4", check_samples(gather_debug(res, pos), ref, W, "prefill nvfp4"))
+    del res, codes, blocks, scales
+    torch.cuda.empty_cache()
+
+
 def test_max_size_single_call(dev, dev_weights, weights):
     # one call of 2^20 tokens in four uneven sequences: byte offsets of the
     # bf16 rows pass 2^31, so any 32-bit index arithmetic would show here
