@@ -340,7 +340,8 @@ static int forward_impl(const ple_forward_args* a, void* stream, void* const* ev
     if (int st = hip_status(e, "ple_forward: projection launch")) return st;
     if (int st = hip_status(mark(3), "ple_forward: event record")) return st;
     e = launch_fuse(a->h, e16, T, a->cu_seqlens, S, a->tokens, a->conv_w, snap, a->conv_state,
-                    a->hist_ids, a->hist_len, a->out, a->eps, a->gate_out, a->y_out, s);
+                    a->hist_ids, a->hist_len, a->out, a->eps, a->gate_out, a->y_out,
+                    reinterpret_cast<uint16_t*>(ws + L.x), s);
     if (int st = hip_status(e, "ple_forward: fuse launch")) return st;
     if (int st = hip_status(mark(4), "ple_forward: event record")) return st;
     return ok();

@@ -9,25 +9,27 @@
 //   v = g e,  y[t][c] = sum_k w[c][k] v[t-3+k][c],  out = bf16(h + y),
 // with v before a sequence's first token taken from the carried state.
 //
-// One block of 640 threads owns BT consecutive tokens; thread i owns
-// features 4i .. 4i+3 and loads, up front, e and h of the block's tokens and
-// of the three before them (packed bf16, 8 bytes a row). BT is 16 for long
-// calls and 1 for short ones (decode steps), whose tokens then run side by
-// side; a token's result does not depend on BT. The kernel is bound
-// by vector ALU issue (no packed fp32 here), so the arithmetic is kept lean:
+// Two kernels compute this, with the same arithmetic in the same order, so
+// that a token's result does not depend on which one runs it. In both, a
+// block has 640 threads and thread i owns features 4i .. 4i+3 (packed bf16,
+// 8 bytes of a row):
 //   - gate sums e^2, h.e, h^2 straight from the packed pairs with the bf16
 //     dot-product instruction (products of bf16 values are exact in fp32);
-//     each wave reduces its lanes to four row sums with DPP, and after a
-//     barrier one thread per token adds the 40 row sums of the block, always
-//     in the same order, so a token's gate does not depend on which block or
-//     chunk computes it;
-//   - v = g e is formed once per window position; an output whose four taps
-//     lie in its own sequence (all but a sequence's first three tokens)
-//     convolves straight from those registers, the others take the taps
-//     before the sequence start from the carried state (a scalar test:
-//     sequence bounds are wave-uniform).
-// The block holding a sequence's last token writes the new conv state and
-// n-gram history; the old state is read from a copy taken before this
+//     each row of 16 lanes reduces to one sum with DPP, and one thread per
+//     token adds the block's 40 row sums in row order;
+//   - v = g e; y = the four taps in one fixed FMA order, taps before a
+//     sequence's first token taken from the carried state; out = bf16(h + y).
+// fuse_kernel (short calls: decode steps, and calls of many short
+// sequences): one token per block, loading e and h of the token and of the
+// three before it, so the tokens of a call run side by side.
+// fuse_stream_kernel (long calls): one block per CU walks a contiguous range
+// of tokens, kStep at a time. The e and h rows of the next step are loaded
+// while the current step is computed, and the v of the last three tokens
+// stay in registers (a ring reset from the carried state at each sequence
+// start), so every row of e and h is read once; a block first runs the three
+// tokens before its range (without output) to fill the ring.
+// Whichever block holds a sequence's last token writes the new conv state
+// and n-gram history; the old state is read from a copy taken before this
 // kernel, so the in-place update cannot race with readers.
 #include "ple_kernels.h"
 
@@ -37,7 +39,12 @@ namespace {
 constexpr int FPT = 4;                 // features per thread
 constexpr int kThreads = kD / FPT;     // 640
 constexpr int kWaves = kThreads / 64;  // 10
+constexpr int kRows = kWaves * 4;      // rows of 16 lanes in a block
 constexpr int kSmallT = 1024;          // calls up to this many tokens run one token per block
+constexpr int kStep = 8;               // fuse_stream_kernel: tokens per step
+constexpr int kDepth = 1;              // fuse_stream_kernel: steps loaded ahead
+constexpr int kStreamBlocks = 256;     // fuse_stream_kernel: one block per CU
+constexpr int kMinRange = 32;          // fuse_stream_kernel: fewest tokens per block
 
 __device__ __forceinline__ void unpack4(const u32x2& q, float v[4]) {
     v[0] = bf16_to_f32(q[0] & 0xFFFFu);
@@ -84,8 +91,54 @@ __device__ __forceinline__ int seq_of(const int32_t* cu, int32_t S, int64_t t) {
     return lo;
 }
 
-// BT tokens per block (16 for long calls; 1 for short ones, so that decode
-// steps, whose tokens each start a sequence, run side by side)
+// the gate from a token's three sums (fixed operation order, no contraction)
+__device__ __forceinline__ float gate_of(float ee, float he, float hh, float eps) {
+#pragma clang fp contract(off)
+    const float rh = sqrtf(hh * (1.0f / kD) + eps);
+    const float re = sqrtf(ee * (1.0f / kD) + eps);
+    const float z = he / (rh * re) * (1.0f / 50.596443f);  // 1/sqrt(2560)
+    return 1.0f / (1.0f + expf(-z));
+}
+
+// gate sums of one token over this thread's four features, reduced over the
+// row of 16 lanes; lane 15 of each row stores them in red[row]
+__device__ __forceinline__ void gate_rows(const u32x2& qe, const u32x2& qh, int lane, int wave,
+                                          float (*red)[3]) {
+    float ee = dot2(qe[1], qe[1], dot2(qe[0], qe[0], 0.0f));
+    float he = dot2(qh[1], qe[1], dot2(qh[0], qe[0], 0.0f));
+    float hh = dot2(qh[1], qh[1], dot2(qh[0], qh[0], 0.0f));
+    ee = row_sum(ee);
+    he = row_sum(he);
+    hh = row_sum(hh);
+    if ((lane & 15) == 15) {
+        float* r = red[wave * 4 + (lane >> 4)];
+        r[0] = ee;
+        r[1] = he;
+        r[2] = hh;
+    }
+}
+
+// n-gram history of sequence s after its last token en-1 (sequence start st)
+__device__ __forceinline__ void update_history(const int32_t* tokens, int32_t* hist_ids, int32_t* hist_len,
+                                               int s, int64_t st, int64_t en) {
+    int hl = hist_len[s];
+    if (hl < 0 || hl > 2) hl = 0;
+    const int64_t L = en - st;
+    if (L >= 2) {
+        hist_ids[2 * s] = tokens[en - 2];
+        hist_ids[2 * s + 1] = tokens[en - 1];
+        hist_len[s] = 2;
+    } else if (hl >= 1) {
+        hist_ids[2 * s] = hist_ids[2 * s + 1];
+        hist_ids[2 * s + 1] = tokens[en - 1];
+        hist_len[s] = 2;
+    } else {
+        hist_ids[2 * s + 1] = tokens[en - 1];
+        hist_len[s] = 1;
+    }
+}
+
+// BT tokens per block (1 in use: short calls, whose tokens then run side by side)
 template <int BT>
 __global__ void __launch_bounds__(kThreads)
 fuse_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ e16, int64_t T,
@@ -93,28 +146,31 @@ fuse_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ e16, in
             const uint16_t* __restrict__ conv_w, const float* __restrict__ snap,
             float* __restrict__ conv_state, int32_t* __restrict__ hist_ids,
             int32_t* __restrict__ hist_len, uint16_t* out, float eps, float* __restrict__ gate_out,
-            float* __restrict__ y_out) {
+            float* __restrict__ y_out, const uint16_t* __restrict__ hw) {
     constexpr int kWin = BT + 3;       // tokens whose v the block needs
-    constexpr int kRows = kWaves * 4;  // rows of 16 lanes in the block
-    __shared__ float red_s[kRows][kWin][3];
+    __shared__ float red_s[kWin][kRows][3];
     __shared__ float g_s[kWin];
     __shared__ int seg_s[kWin], start_s[kWin], end_s[kWin];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t t0 = (int64_t)blockIdx.x * BT;
     const uint32_t cb = (uint32_t)tid * FPT * 2;  // byte offset of this thread's features in a row
 
-    // this thread's e and h of the 19-token window
+    // this thread's e and h of the window; the h rows of the three tokens
+    // before the block's own come from hw (a copy taken before this kernel)
+    // when out is h, since other blocks overwrite them
     const u32x2 zero = {0u, 0u};
     u32x2 ep[kWin], hp[kWin];
+    const uint16_t* hwin = hw ? hw : h;
     if (t0 >= 3 && t0 + BT <= T) {
         // interior block: one uniform base, 32-bit per-lane offsets
         const char* eb = reinterpret_cast<const char*>(e16) + (t0 - 3) * (kD * 2);
         const char* hb = reinterpret_cast<const char*>(h) + (t0 - 3) * (kD * 2);
+        const char* wb = reinterpret_cast<const char*>(hwin) + (t0 - 3) * (kD * 2);
 #pragma unroll
         for (int i = 0; i < kWin; ++i) {
             const uint32_t off = cb + (uint32_t)(i * kD * 2);
             ep[i] = *reinterpret_cast<const u32x2*>(eb + off);
-            hp[i] = *reinterpret_cast<const u32x2*>(hb + off);
+            hp[i] = *reinterpret_cast<const u32x2*>((i < 3 ? wb : hb) + off);
         }
     } else {
         // first and last blocks: unconditional loads from a clamped (in-bounds)
@@ -125,7 +181,8 @@ fuse_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ e16, in
             const bool in = t >= 0 && t < T;
             const int64_t tc = t < 0 ? 0 : (t >= T ? T - 1 : t);
             const u32x2 qe = *reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(e16) + tc * (kD * 2) + cb);
-            const u32x2 qh = *reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(h) + tc * (kD * 2) + cb);
+            const u32x2 qh = *reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(i < 3 ? hwin : h) +
+                                                             tc * (kD * 2) + cb);
             ep[i] = in ? qe : zero;
             hp[i] = in ? qh : zero;
         }
@@ -134,21 +191,7 @@ fuse_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ e16, in
     // gate sums: four features per thread (bf16 dot products), then the rows
     // of 16 lanes; lane 15 of each row keeps the row's sums
 #pragma unroll
-    for (int i = 0; i < kWin; ++i) {
-        const u32x2 qe = ep[i], qh = hp[i];
-        float ee = dot2(qe[1], qe[1], dot2(qe[0], qe[0], 0.0f));
-        float he = dot2(qh[1], qe[1], dot2(qh[0], qe[0], 0.0f));
-        float hh = dot2(qh[1], qh[1], dot2(qh[0], qh[0], 0.0f));
-        ee = row_sum(ee);
-        he = row_sum(he);
-        hh = row_sum(hh);
-        if ((lane & 15) == 15) {
-            const int r = wave * 4 + (lane >> 4);
-            red_s[r][i][0] = ee;
-            red_s[r][i][1] = he;
-            red_s[r][i][2] = hh;
-        }
-    }
+    for (int i = 0; i < kWin; ++i) gate_rows(ep[i], hp[i], lane, wave, red_s[i]);
     __syncthreads();
     if (tid < kWin) {
         const int64_t t = t0 - 3 + tid;
@@ -156,14 +199,11 @@ fuse_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ e16, in
             float ee = 0.0f, he = 0.0f, hh = 0.0f;
 #pragma unroll 8
             for (int r = 0; r < kRows; ++r) {
-                ee += red_s[r][tid][0];
-                he += red_s[r][tid][1];
-                hh += red_s[r][tid][2];
+                ee += red_s[tid][r][0];
+                he += red_s[tid][r][1];
+                hh += red_s[tid][r][2];
             }
-            const float rh = sqrtf(hh * (1.0f / kD) + eps);
-            const float re = sqrtf(ee * (1.0f / kD) + eps);
-            const float z = he / (rh * re) * (1.0f / 50.596443f);  // 1/sqrt(2560)
-            const float g = 1.0f / (1.0f + expf(-z));
+            const float g = gate_of(ee, he, hh, eps);
             g_s[tid] = g;
             if (gate_out && tid >= 3) gate_out[t] = g;
             const int s = seq_of(cu, S, t);
@@ -257,24 +297,215 @@ fuse_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ e16, in
                 *reinterpret_cast<f32x4*>(conv_state + ((int64_t)s * 3 + r) * kD + tid * FPT) =
                     f32x4{a[0], a[1], a[2], a[3]};
             }
-            if (tid == 0) {
-                int hl = hist_len[s];
-                if (hl < 0 || hl > 2) hl = 0;
-                const int L = en - st;
-                if (L >= 2) {
-                    hist_ids[2 * s] = tokens[en - 2];
-                    hist_ids[2 * s + 1] = tokens[en - 1];
-                    hist_len[s] = 2;
-                } else if (hl >= 1) {
-                    hist_ids[2 * s] = hist_ids[2 * s + 1];
-                    hist_ids[2 * s + 1] = tokens[en - 1];
-                    hist_len[s] = 2;
-                } else {
-                    hist_ids[2 * s + 1] = tokens[en - 1];
-                    hist_len[s] = 1;
-                }
+            if (tid == 0) update_history(tokens, hist_ids, hist_len, s, st, en);
+        }
+    }
+}
+
+// e and h of tokens t .. t+kStep-1 for this thread; tokens past `last` read
+// row `last` (in bounds; their results are never used). The row clamp is
+// scalar and no branch surrounds the loads, so the compiler can count them
+// and wait only for the step a computation needs.
+template <int kN>
+__device__ __forceinline__ void load_step(const uint16_t* __restrict__ e16, const uint16_t* __restrict__ h,
+                                          int64_t t, int64_t last, uint32_t cb, u32x2 (&pe)[kN],
+                                          u32x2 (&ph)[kN]) {
+#pragma unroll
+    for (int j = 0; j < kN; ++j) {
+        const int64_t r = t + j < last ? t + j : last;
+        pe[j] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(e16 + r * kD) + cb);
+        ph[j] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(h + r * kD) + cb);
+    }
+}
+
+template <int kN, int kAhead>
+__global__ void __launch_bounds__(kThreads)
+fuse_stream_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ e16, int64_t T,
+                   const int32_t* __restrict__ cu, int32_t S, const int32_t* __restrict__ tokens,
+                   const uint16_t* __restrict__ conv_w, const float* __restrict__ snap,
+                   float* __restrict__ conv_state, int32_t* __restrict__ hist_ids,
+                   int32_t* __restrict__ hist_len, uint16_t* out, float eps, float* __restrict__ gate_out,
+                   float* __restrict__ y_out, int64_t per_block, const uint16_t* __restrict__ halo) {
+    static_assert(kN >= 3, "the three tokens before a range must fit in the first step");
+    __shared__ float red_s[kN][kRows][3];
+    __shared__ float g_s[kN];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint32_t cb = (uint32_t)tid * FPT * 2;
+    const int64_t a = (int64_t)blockIdx.x * per_block;  // this block's tokens: a .. b-1
+    if (a >= T) return;
+    const int64_t b = a + per_block < T ? a + per_block : T;
+
+    // sequence of token a, and the first token to run: up to three before a
+    // in the same sequence, so that the ring holds v of a-3 .. a-1
+    int s = seq_of(cu, S, a);
+    int64_t st = cu[s], en = cu[s + 1];
+    if (st < 0 || st > a) st = a;  // malformed cu_seqlens (flagged by the ID kernel): stay in bounds
+    if (en <= a || en > T) en = a + 1;
+    const int64_t a0 = a - 3 > st ? a - 3 : st;
+
+    float w[FPT][kTaps];
+    {
+        const u32x4* wp = reinterpret_cast<const u32x4*>(conv_w + tid * FPT * kTaps);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            u32x4 q = wp[i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int idx = i * 8 + 2 * j;
+                w[idx / 4][idx % 4] = bf16_to_f32(q[j] & 0xFFFFu);
+                w[(idx + 1) / 4][(idx + 1) % 4] = bf16_to_f32(q[j] >> 16);
             }
         }
+    }
+    // v of the three tokens before the current one (oldest first)
+    float r0[FPT] = {}, r1[FPT] = {}, r2[FPT] = {};
+
+    // one step: tokens tb .. tb+kN-1 from (ce, ch), while the rows of the
+    // step kAhead later load into (ne, nh)
+    auto step = [&](int64_t tb, u32x2 (&ce)[kN], u32x2 (&ch)[kN], u32x2 (&ne)[kN], u32x2 (&nh)[kN]) {
+        load_step<kN>(e16, h, tb + kAhead * kN, b - 1, cb, ne, nh);  // past b: row b-1 again, unused
+#pragma unroll
+        for (int j = 0; j < kN; ++j) gate_rows(ce[j], ch[j], lane, wave, red_s[j]);
+        __syncthreads();
+        if (tid < kN) {
+            float ee = 0.0f, he = 0.0f, hh = 0.0f;
+#pragma unroll 8
+            for (int r = 0; r < kRows; ++r) {
+                ee += red_s[tid][r][0];
+                he += red_s[tid][r][1];
+                hh += red_s[tid][r][2];
+            }
+            const float g = gate_of(ee, he, hh, eps);
+            g_s[tid] = g;
+            const int64_t t = tb + tid;
+            if (gate_out && t >= a && t < b) gate_out[t] = g;
+        }
+        __syncthreads();
+        char* ob = reinterpret_cast<char*>(out) + tb * (kD * 2);
+        if (tb >= a && tb + kN <= b && st < tb && en > tb + kN && !y_out) {
+            // common case: every token of the step is in the range and in
+            // sequence s, none starts or ends it. v of the step and the three
+            // tokens before it in one statically indexed window
+            float vw[kN + 3][FPT];
+#pragma unroll
+            for (int q = 0; q < FPT; ++q) {
+                vw[0][q] = r0[q];
+                vw[1][q] = r1[q];
+                vw[2][q] = r2[q];
+            }
+#pragma unroll
+            for (int j = 0; j < kN; ++j) {
+                float e[FPT];
+                unpack4(ce[j], e);
+                const float g = g_s[j];
+#pragma unroll
+                for (int q = 0; q < FPT; ++q) vw[j + 3][q] = g * e[q];
+            }
+#pragma unroll
+            for (int j = 0; j < kN; ++j) {
+                float y[FPT], hv[FPT];
+#pragma unroll
+                for (int q = 0; q < FPT; ++q) y[q] = conv4(w[q], vw[j][q], vw[j + 1][q], vw[j + 2][q], vw[j + 3][q]);
+                unpack4(ch[j], hv);
+                const u32x2 o = {pack_bf16x2(hv[0] + y[0], hv[1] + y[1]), pack_bf16x2(hv[2] + y[2], hv[3] + y[3])};
+                __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(ob + (cb + (uint32_t)(j * kD * 2))));
+            }
+#pragma unroll
+            for (int q = 0; q < FPT; ++q) {
+                r0[q] = vw[kN][q];
+                r1[q] = vw[kN + 1][q];
+                r2[q] = vw[kN + 2][q];
+            }
+            return;
+        }
+#pragma unroll
+        for (int j = 0; j < kN; ++j) {
+            const int64_t t = tb + j;
+            if (t >= b) break;
+            // sequence bounds are the same in every lane
+            while (t >= en && s + 1 < S) {
+                ++s;
+                st = en;
+                en = cu[s + 1];
+            }
+            if (en <= t || en > T) en = t + 1;  // malformed cu_seqlens: stay in bounds
+            if (t == st) {
+                // a sequence starts: its three earlier taps are the carried state
+                const float* sp = snap + (int64_t)s * 3 * kD + tid * FPT;
+                const f32x4 c0 = *reinterpret_cast<const f32x4*>(sp);
+                const f32x4 c1 = *reinterpret_cast<const f32x4*>(sp + kD);
+                const f32x4 c2 = *reinterpret_cast<const f32x4*>(sp + 2 * kD);
+#pragma unroll
+                for (int q = 0; q < FPT; ++q) {
+                    r0[q] = c0[q];
+                    r1[q] = c1[q];
+                    r2[q] = c2[q];
+                }
+            }
+            float e[FPT], v[FPT], y[FPT];
+            unpack4(ce[j], e);
+            const float g = g_s[j];
+#pragma unroll
+            for (int q = 0; q < FPT; ++q) {
+                v[q] = g * e[q];
+                y[q] = conv4(w[q], r0[q], r1[q], r2[q], v[q]);
+                r0[q] = r1[q];
+                r1[q] = r2[q];
+                r2[q] = v[q];
+            }
+            if (t < a) continue;  // a token before the range: ring only
+            float hv[FPT];
+            unpack4(ch[j], hv);
+            const u32x2 o = {pack_bf16x2(hv[0] + y[0], hv[1] + y[1]), pack_bf16x2(hv[2] + y[2], hv[3] + y[3])};
+            __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(ob + (cb + (uint32_t)(j * kD * 2))));
+            if (y_out) *reinterpret_cast<f32x4*>(y_out + t * kD + tid * FPT) = f32x4{y[0], y[1], y[2], y[3]};
+            if (t == en - 1) {
+                // last token of sequence s: new conv state = v at t-2, t-1, t
+                float* dp = conv_state + (int64_t)s * 3 * kD + tid * FPT;
+                *reinterpret_cast<f32x4*>(dp) = f32x4{r0[0], r0[1], r0[2], r0[3]};
+                *reinterpret_cast<f32x4*>(dp + kD) = f32x4{r1[0], r1[1], r1[2], r1[3]};
+                *reinterpret_cast<f32x4*>(dp + 2 * kD) = f32x4{r2[0], r2[1], r2[2], r2[3]};
+                if (tid == 0) update_history(tokens, hist_ids, hist_len, s, st, en);
+            }
+        }
+    };
+
+    // kAhead + 1 buffers in rotation, the loop unrolled so that each is named
+    // statically: step u computes from buffer u and loads into the one that
+    // step u-1 used
+    u32x2 be[kAhead + 1][kN], bh[kAhead + 1][kN];
+#pragma unroll
+    for (int d = 0; d < kAhead; ++d) load_step<kN>(e16, h, a0 + d * kN, b - 1, cb, be[d], bh[d]);
+    if (halo) {
+        // out is h: the rows before a belong to the previous block, which
+        // overwrites them; take them from the copy made before this kernel
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+            if (a0 + j < a)
+                bh[0][j] = *reinterpret_cast<const u32x2*>(
+                    reinterpret_cast<const char*>(halo) +
+                    ((int64_t)blockIdx.x * 3 + 3 - (a - (a0 + j))) * (kD * 2) + cb);
+    }
+    for (int64_t tb = a0; tb < b; tb += (kAhead + 1) * kN) {
+#pragma unroll
+        for (int u = 0; u <= kAhead; ++u) {
+            if (tb + u * kN >= b) break;
+            step(tb + u * kN, be[u], bh[u], be[(u + kAhead) % (kAhead + 1)], bh[(u + kAhead) % (kAhead + 1)]);
+        }
+    }
+}
+
+// out is h: the three h rows before each streaming block's range, copied to
+// halo [blocks][3][kD] before the fuse kernel overwrites them
+__global__ void __launch_bounds__(kThreads)
+halo_copy_kernel(const uint16_t* __restrict__ h, int64_t per_block, uint16_t* __restrict__ halo) {
+    const int64_t a = (int64_t)blockIdx.x * per_block;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        const int64_t t = a - 3 + k;
+        if (t < 0) continue;
+        const u32x2 q = *reinterpret_cast<const u32x2*>(h + t * kD + threadIdx.x * FPT);
+        *reinterpret_cast<u32x2*>(halo + ((int64_t)blockIdx.x * 3 + k) * kD + threadIdx.x * FPT) = q;
     }
 }
 
@@ -284,16 +515,32 @@ hipError_t launch_fuse(const uint16_t* h, const uint16_t* e16, int64_t T, const 
                        int32_t S, const int32_t* tokens, const uint16_t* conv_w,
                        const float* state_snap, float* conv_state, int32_t* hist_ids,
                        int32_t* hist_len, uint16_t* out, float eps, float* gate_out, float* y_out,
-                       hipStream_t stream) {
-    if (T <= kSmallT) {
+                       uint16_t* h_copy, hipStream_t stream) {
+    const bool in_place = out == h;
+    if (T <= kSmallT || T < (int64_t)kMinRange * S) {
+        // short calls, or many short sequences (each start would stall a
+        // streaming block on its carried state): one token per block
+        if (in_place) {
+            hipError_t e = hipMemcpyAsync(h_copy, h, (size_t)T * kD * 2, hipMemcpyDeviceToDevice, stream);
+            if (e != hipSuccess) return e;
+        }
         hipLaunchKernelGGL(fuse_kernel<1>, dim3((unsigned)T), dim3(kThreads), 0, stream, h, e16, T, cu,
                            S, tokens, conv_w, state_snap, conv_state, hist_ids, hist_len, out, eps,
-                           gate_out, y_out);
+                           gate_out, y_out, in_place ? h_copy : nullptr);
     } else {
-        const int64_t blocks = (T + 15) / 16;
-        hipLaunchKernelGGL(fuse_kernel<16>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, h, e16, T,
+        int64_t blocks = (T + kMinRange - 1) / kMinRange;
+        if (blocks > kStreamBlocks) blocks = kStreamBlocks;
+        const int64_t per_block = (T + blocks - 1) / blocks;
+        blocks = (T + per_block - 1) / per_block;
+        if (in_place) {
+            hipLaunchKernelGGL(halo_copy_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, h, per_block,
+                               h_copy);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        hipLaunchKernelGGL((fuse_stream_kernel<kStep, kDepth>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, h, e16, T,
                            cu, S, tokens, conv_w, state_snap, conv_state, hist_ids, hist_len, out, eps,
-                           gate_out, y_out);
+                           gate_out, y_out, per_block, in_place ? h_copy : nullptr);
     }
     return hipGetLastError();
 }

@@ -68,6 +68,6 @@ hipError_t launch_fuse(const uint16_t* h, const uint16_t* e16, int64_t T, const 
                        int32_t S, const int32_t* tokens, const uint16_t* conv_w,
                        const float* state_snap, float* conv_state, int32_t* hist_ids,
                        int32_t* hist_len, uint16_t* out, float eps, float* gate_out, float* y_out,
-                       hipStream_t stream);
+                       uint16_t* h_copy, hipStream_t stream);  // h_copy: T x 2560 bf16 scratch, used when out == h
 
 }  // namespace ple

@@ -228,6 +228,61 @@ def test_kernel_variants_agree_bit_exactly(dev, small_table, dev_weights):
             assert np.array_equal(a, b), cuts
 
 
+def test_streaming_fuse_equals_per_sequence_calls(dev, small_table, dev_weights):
+    # one 1380-token call of eleven sequences with carried state runs the
+    # streaming fuse (block ranges of ~32 tokens cross sequence starts and
+    # ends); each sequence alone (<= 1024 tokens) runs the one-token fuse and
+    # the small-T projection: outputs, gates and the new state must be equal
+    tab, sc = small_table
+    lengths = [1, 2, 3, 5, 40, 33, 700, 31, 500, 1, 64]
+    hl = [0, 1, 2, 2, 0, 2, 1, 2, 2, 2, 0]
+    toks, cu, hist, hlen, h = _case(91, lengths, hl)
+    S = len(lengths)
+    rng = np.random.default_rng(92)
+    state0 = (rng.standard_normal((S, 3, D)) * 0.5).astype(np.float32)
+    state0[np.array(hl) == 0] = 0.0
+
+    def fresh(sl):
+        st = ple.State(len(range(*sl.indices(S))), dev)
+        st.hist_ids.copy_(dev_i32(hist[sl], dev))
+        st.hist_len.copy_(dev_i32(hlen[sl], dev))
+        st.conv_state.copy_(torch.from_numpy(state0[sl]).to(dev))
+        return st
+
+    st = fresh(slice(0, S))
+    whole = _forward(dev, tab, sc, dev_weights, toks, cu, h, st)
+    for i in range(S):
+        a, b = int(cu[i]), int(cu[i + 1])
+        si = fresh(slice(i, i + 1))
+        one = _forward(dev, tab, sc, dev_weights, toks[a:b], np.array([0, b - a], np.int32), h[a:b], si)
+        assert np.array_equal(host_bits(one["out"]), host_bits(whole["out"][a:b])), i
+        assert torch.equal(one["gate"], whole["gate"][a:b]), i
+        assert torch.equal(one["y"], whole["y"][a:b]), i
+        assert torch.equal(si.conv_state[0], st.conv_state[i]), i
+        assert torch.equal(si.hist_ids[0], st.hist_ids[i]) and torch.equal(si.hist_len[0], st.hist_len[i]), i
+
+
+@pytest.mark.parametrize("T,lengths", [(1000, [1000]), (4000, [1500, 1, 2499]), (9000, [9000])])
+def test_in_place_equals_out_of_place_both_fuse_kernels(dev, small_table, dev_weights, T, lengths):
+    # out == h: the h rows a block reads but does not own come from a copy
+    # taken before the fuse (1000 tokens: one-token fuse, all of h; longer:
+    # streaming fuse, three rows per block range)
+    tab, sc = small_table
+    rng = np.random.default_rng(T)
+    toks = inputs.uniform_tokens(rng, T)
+    h = inputs.normal_bf16(rng, (T, D))
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    S = len(lengths)
+    ref = ple.ple_forward(dev_i32(toks, dev), dev_i32(cu, dev), tab, sc, dev_weights[0], dev_weights[1],
+                          dev_bf16(h, dev), ple.State(S, dev))
+    hd = dev_bf16(h, dev)
+    st = ple.State(S, dev)
+    out = ple.ple_forward(dev_i32(toks, dev), dev_i32(cu, dev), tab, sc, dev_weights[0], dev_weights[1],
+                          hd, st, out=hd)
+    assert out.data_ptr() == hd.data_ptr()
+    assert np.array_equal(host_bits(hd), host_bits(ref))
+
+
 def test_in_place_out_equals_h(dev, small_table, dev_weights):
     tab, sc = small_table
     rng = np.random.default_rng(7)
