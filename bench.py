@@ -58,7 +58,8 @@ KERNEL_SOURCES = {
                             "sparse_memory_gather_amd/csrc/ple_kernels.h"],
     "gather_nvfp4_kernel": ["sparse_memory_gather_amd/csrc/ple_gather.hip",
                             "sparse_memory_gather_amd/csrc/ple_kernels.h"],
-    "fuse_kernel": ["sparse_memory_gather_amd/csrc/ple_fuse.hip", "sparse_memory_gather_amd/csrc/ple_kernels.h"],
+    "fuse_stream_kernel": ["sparse_memory_gather_amd/csrc/ple_fuse.hip",
+                           "sparse_memory_gather_amd/csrc/ple_kernels.h"],
 }
 
 
@@ -379,12 +380,12 @@ def main():
                     "traffic": recorded_traffic(gather_name, name),
                     "per_launch": {"bytes": gather_bytes, "avg_us": round(float(stage_us[1]), 2)}}
     else:
-        k = ["ple_hash (hash_kernel)", "", "", "ple_gate_conv_fuse (fuse_kernel)"][dominant]
+        k = ["ple_hash (hash_kernel)", "", "", "ple_gate_conv_fuse (fuse_stream_kernel / fuse_kernel)"][dominant]
         nb = fuse_bytes if dominant == 3 else tokens_per_call * 12
         gbs = nb / (stage_us[dominant] * 1e-6) / 1e9
         roofline = {"kernel": k, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                    "traffic": recorded_traffic("fuse_kernel", name) if dominant == 3 else None,
+                    "traffic": recorded_traffic("fuse_stream_kernel", name) if dominant == 3 else None,
                     "per_launch": {"bytes": nb, "avg_us": round(float(stage_us[dominant]), 2)}}
 
     result = {
