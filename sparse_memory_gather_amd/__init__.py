@@ -264,6 +264,92 @@ class Workspace:
         return self.buf
 
 
+class Forward:
+    """One ple_forward call prepared once: every tensor is checked and the C
+    argument struct built at construction; each call passes the struct
+    straight to the library. For loops that run the same buffers again (a
+    decode loop copying each step's tokens and hidden states into fixed
+    device buffers). The tensors given must keep their storage while the
+    object is in use; arguments as for ple_forward."""
+
+    def __init__(self, tokens, cu_seqlens, table, scales, W, conv_w, h, state: State, out=None,
+                 workspace=None, vocab_size: int = DEFAULT_VOCAB, eps: float = DEFAULT_EPS,
+                 dev_err=None, debug: bool = False, heads: bool = False, nvfp4_blocks=None):
+        T = tokens.numel()
+        S = cu_seqlens.numel() - 1
+        nv = nvfp4_blocks is not None
+        if nv and heads:
+            raise ValueError("the NVFP4 table is read with two lookups per token")
+        R = scales.shape[0] if nv else _rows_of(table, scales, heads)
+        n = HEADS if heads else 2
+        dev = tokens.device
+        if out is None:
+            out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+        if workspace is None:
+            workspace = Workspace(dev)
+        ws = workspace.get(T, S, heads) if isinstance(workspace, Workspace) else workspace
+        dbg = {}
+        if debug:
+            dbg = dict(row_ids=torch.empty((T, n), dtype=torch.int32, device=dev),
+                       x=torch.empty((T, D), dtype=torch.bfloat16, device=dev),
+                       e=torch.empty((T, D), dtype=torch.float32, device=dev),
+                       gate=torch.empty((T,), dtype=torch.float32, device=dev),
+                       y=torch.empty((T, D), dtype=torch.float32, device=dev))
+        a = ForwardArgs()
+        a.tokens = _dev(tokens, "tokens", torch.int32, (T,))
+        a.T = T
+        a.cu_seqlens = _dev(cu_seqlens, "cu_seqlens", torch.int32, (S + 1,))
+        a.S = S
+        a.vocab_size = vocab_size
+        a.table = _dev(table, "table", torch.uint8, (R, D // 2)) if nv else _table(table, R)
+        a.scales = _dev(scales, "scales", torch.float32, (HEADS, R) if heads else (R,))
+        a.R = R
+        a.W = _dev(W, "W", torch.bfloat16, (D, D))
+        a.conv_w = _dev(conv_w, "conv_w", torch.bfloat16, (D, CONV_TAPS))
+        a.h = _dev(h, "h", torch.bfloat16, (T, D))
+        a.out = _dev(out, "out", torch.bfloat16, (T, D))
+        a.hist_ids = _dev(state.hist_ids, "hist_ids", torch.int32, (S, 2))
+        a.hist_len = _dev(state.hist_len, "hist_len", torch.int32, (S,))
+        a.conv_state = _dev(state.conv_state, "conv_state", torch.float32, (S, 3, D))
+        a.workspace = _dev(ws, "workspace", torch.uint8)
+        a.workspace_bytes = ws.numel()
+        a.dev_err = _opt(dev_err, "dev_err", torch.int32, (1,))
+        a.eps = eps
+        if debug:
+            a.row_ids_out = dbg["row_ids"].data_ptr()
+            a.x_out = dbg["x"].data_ptr()
+            a.e_out = dbg["e"].data_ptr()
+            a.gate_out = dbg["gate"].data_ptr()
+            a.y_out = dbg["y"].data_ptr()
+        lib = load_library()
+        self.args, self.out, self.debug = a, out, dbg if debug else None
+        byref = ctypes.byref(a)
+        # the tensors whose addresses the struct holds stay referenced here
+        self._keep = (tokens, cu_seqlens, table, scales, W, conv_w, h, state, ws, dev_err, nvfp4_blocks)
+        if nv:
+            blk = _dev(nvfp4_blocks, "nvfp4_blocks", torch.uint8, (R, D // 16))
+            self._run = lambda st: lib.ple_forward_nvfp4(byref, blk, st)
+            self._run_ev = lambda st, ev: lib.ple_forward_nvfp4_profiled(byref, blk, st, ev)
+        elif heads:
+            self._run = lambda st: lib.ple_forward_heads(byref, st)
+            self._run_ev = lambda st, ev: lib.ple_forward_heads_profiled(byref, st, ev)
+        else:
+            self._run = lambda st: lib.ple_forward(byref, st)
+            self._run_ev = lambda st, ev: lib.ple_forward_profiled(byref, st, ev)
+
+    def __call__(self, stream=None, events=None):
+        """Enqueue the call on `stream` (default: torch's current stream);
+        returns out, or the debug dict. `events` as for ple_forward."""
+        if events is None:
+            _check(self._run(_stream(stream)))
+        else:
+            _check(self._run_ev(_stream(stream), (_P * 5)(*[ctypes.c_void_p(int(e)) for e in events])))
+        if self.debug is not None:
+            self.debug["out"] = self.out
+            return self.debug
+        return self.out
+
+
 def ple_forward(tokens, cu_seqlens, table, scales, W, conv_w, h, state: State, out=None,
                 workspace=None, vocab_size: int = DEFAULT_VOCAB, eps: float = DEFAULT_EPS,
                 dev_err=None, debug: bool = False, stream=None, events=None, heads: bool = False,
@@ -271,72 +357,12 @@ def ple_forward(tokens, cu_seqlens, table, scales, W, conv_w, h, state: State, o
     """a1..a4 for one chunk. Updates `state` in place; returns out (bf16
     [T][2560]) or, with debug=True, a dict with out, row_ids, x, e, gate, y.
     `events`: optional sequence of five hipEvent_t handles (ints) recorded
-    around the four kernels (ple_forward_profiled). heads=True: the 16-lookup
+    around the four stages (ple_forward_profiled). heads=True: the 16-lookup
     layout (scales [16][R], row_ids [T][16]). nvfp4_blocks (uint8 [R][160]):
     the NVFP4 table, `table` then being the packed codes uint8 [R][1280]."""
-    T = tokens.numel()
-    S = cu_seqlens.numel() - 1
-    nv = nvfp4_blocks is not None
-    if nv and heads:
-        raise ValueError("the NVFP4 table is read with two lookups per token")
-    R = scales.shape[0] if nv else _rows_of(table, scales, heads)
-    n = HEADS if heads else 2
-    dev = tokens.device
-    if out is None:
-        out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
-    if workspace is None:
-        workspace = Workspace(dev)
-    ws = workspace.get(T, S, heads) if isinstance(workspace, Workspace) else workspace
-    dbg = {}
-    if debug:
-        dbg = dict(row_ids=torch.empty((T, n), dtype=torch.int32, device=dev),
-                   x=torch.empty((T, D), dtype=torch.bfloat16, device=dev),
-                   e=torch.empty((T, D), dtype=torch.float32, device=dev),
-                   gate=torch.empty((T,), dtype=torch.float32, device=dev),
-                   y=torch.empty((T, D), dtype=torch.float32, device=dev))
-    a = ForwardArgs()
-    a.tokens = _dev(tokens, "tokens", torch.int32, (T,))
-    a.T = T
-    a.cu_seqlens = _dev(cu_seqlens, "cu_seqlens", torch.int32, (S + 1,))
-    a.S = S
-    a.vocab_size = vocab_size
-    a.table = _dev(table, "table", torch.uint8, (R, D // 2)) if nv else _table(table, R)
-    a.scales = _dev(scales, "scales", torch.float32, (HEADS, R) if heads else (R,))
-    a.R = R
-    a.W = _dev(W, "W", torch.bfloat16, (D, D))
-    a.conv_w = _dev(conv_w, "conv_w", torch.bfloat16, (D, CONV_TAPS))
-    a.h = _dev(h, "h", torch.bfloat16, (T, D))
-    a.out = _dev(out, "out", torch.bfloat16, (T, D))
-    a.hist_ids = _dev(state.hist_ids, "hist_ids", torch.int32, (S, 2))
-    a.hist_len = _dev(state.hist_len, "hist_len", torch.int32, (S,))
-    a.conv_state = _dev(state.conv_state, "conv_state", torch.float32, (S, 3, D))
-    a.workspace = _dev(ws, "workspace", torch.uint8)
-    a.workspace_bytes = ws.numel()
-    a.dev_err = _opt(dev_err, "dev_err", torch.int32, (1,))
-    a.eps = eps
-    if debug:
-        a.row_ids_out = dbg["row_ids"].data_ptr()
-        a.x_out = dbg["x"].data_ptr()
-        a.e_out = dbg["e"].data_ptr()
-        a.gate_out = dbg["gate"].data_ptr()
-        a.y_out = dbg["y"].data_ptr()
-    lib = load_library()
-    ev = None if events is None else (_P * 5)(*[ctypes.c_void_p(int(e)) for e in events])
-    if nv:
-        blk = _dev(nvfp4_blocks, "nvfp4_blocks", torch.uint8, (R, D // 16))
-        if ev is None:
-            _check(lib.ple_forward_nvfp4(ctypes.byref(a), blk, _stream(stream)))
-        else:
-            _check(lib.ple_forward_nvfp4_profiled(ctypes.byref(a), blk, _stream(stream), ev))
-    elif ev is None:
-        _check((lib.ple_forward_heads if heads else lib.ple_forward)(ctypes.byref(a), _stream(stream)))
-    else:
-        f = lib.ple_forward_heads_profiled if heads else lib.ple_forward_profiled
-        _check(f(ctypes.byref(a), _stream(stream), ev))
-    if debug:
-        dbg["out"] = out
-        return dbg
-    return out
+    return Forward(tokens, cu_seqlens, table, scales, W, conv_w, h, state, out=out, workspace=workspace,
+                   vocab_size=vocab_size, eps=eps, dev_err=dev_err, debug=debug, heads=heads,
+                   nvfp4_blocks=nvfp4_blocks)(stream=stream, events=events)
 
 
 def ple_forward_x(x, tokens, cu_seqlens, W, conv_w, h, state: State, out=None, workspace=None,

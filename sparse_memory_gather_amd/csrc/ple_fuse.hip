@@ -19,9 +19,8 @@
 //     token adds the block's 40 row sums in row order;
 //   - v = g e; y = the four taps in one fixed FMA order, taps before a
 //     sequence's first token taken from the carried state; out = bf16(h + y).
-// fuse_kernel (short calls: decode steps, and calls of many short
-// sequences): one token per block, loading e and h of the token and of the
-// three before it, so the tokens of a call run side by side.
+// fuse_token_kernel (short calls: decode steps, and calls of many short
+// sequences): one token per block, so the tokens of a call run side by side.
 // fuse_stream_kernel (long calls): one block per CU walks a contiguous range
 // of tokens, kStep at a time. The e and h rows of the next step are loaded
 // while the current step is computed, and the v of the last three tokens
@@ -31,7 +30,7 @@
 // Whichever block holds a sequence's last token writes the new conv state
 // and n-gram history; the old state is read from a copy taken before this
 // kernel, so the in-place update cannot race with readers.
-#include "ple_kernels.h"
+#include "ple_ngram.h"
 
 namespace ple {
 namespace {
@@ -82,15 +81,6 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                            false);
 }
 
-__device__ __forceinline__ int seq_of(const int32_t* cu, int32_t S, int64_t t) {
-    int lo = 0, hi = S - 1;
-    while (lo < hi) {
-        int mid = (lo + hi + 1) >> 1;
-        if ((int64_t)cu[mid] <= t) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-}
-
 // the gate from a token's three sums (fixed operation order, no contraction)
 __device__ __forceinline__ float gate_of(float ee, float he, float hh, float eps) {
 #pragma clang fp contract(off)
@@ -138,90 +128,48 @@ __device__ __forceinline__ void update_history(const int32_t* tokens, int32_t* h
     }
 }
 
-// BT tokens per block (1 in use: short calls, whose tokens then run side by side)
-template <int BT>
+// One token per block (short calls). The token's sequence is found first, so
+// that the carried-state taps load beside e and h; window rows before the
+// sequence start are neither loaded nor gated (a decode step, whose tokens
+// each start a sequence, reads only its own row). hw: where the h rows of the
+// three earlier tokens are read (a copy when out is h), or NULL for h.
 __global__ void __launch_bounds__(kThreads)
-fuse_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ e16, int64_t T,
-            const int32_t* __restrict__ cu, int32_t S, const int32_t* __restrict__ tokens,
-            const uint16_t* __restrict__ conv_w, const float* __restrict__ snap,
-            float* __restrict__ conv_state, int32_t* __restrict__ hist_ids,
-            int32_t* __restrict__ hist_len, uint16_t* out, float eps, float* __restrict__ gate_out,
-            float* __restrict__ y_out, const uint16_t* __restrict__ hw) {
-    constexpr int kWin = BT + 3;       // tokens whose v the block needs
-    __shared__ float red_s[kWin][kRows][3];
-    __shared__ float g_s[kWin];
-    __shared__ int seg_s[kWin], start_s[kWin], end_s[kWin];
+fuse_token_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ e16, int64_t T,
+                  const int32_t* __restrict__ cu, int32_t S, const int32_t* __restrict__ tokens,
+                  const uint16_t* __restrict__ conv_w, const float* __restrict__ snap,
+                  float* __restrict__ conv_state, int32_t* __restrict__ hist_ids,
+                  int32_t* __restrict__ hist_len, uint16_t* out, float eps, float* __restrict__ gate_out,
+                  float* __restrict__ y_out, const uint16_t* __restrict__ hw) {
+    __shared__ float red_s[4][kRows][3];
+    __shared__ float g_s[4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t t0 = (int64_t)blockIdx.x * BT;
-    const uint32_t cb = (uint32_t)tid * FPT * 2;  // byte offset of this thread's features in a row
+    const int64_t t = blockIdx.x;
+    const uint32_t cb = (uint32_t)tid * FPT * 2;
 
-    // this thread's e and h of the window; the h rows of the three tokens
-    // before the block's own come from hw (a copy taken before this kernel)
-    // when out is h, since other blocks overwrite them
-    const u32x2 zero = {0u, 0u};
-    u32x2 ep[kWin], hp[kWin];
+    const int s = seq_of(cu, S, t);
+    int64_t st = cu[s], en = cu[s + 1];
+    if (st < 0 || st > t) st = t;  // malformed cu_seqlens (flagged by the ID kernel): stay in bounds
+    if (en <= t || en > T) en = t + 1;
+    // window slot k is token t-3+k; slots below `first` lie before the start
+    const int first = st > t - 3 ? (int)(st - (t - 3)) : 0;
+    f32x4 c[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+        c[k] = k < first ? *reinterpret_cast<const f32x4*>(snap + ((int64_t)s * 3 + 3 - (first - k)) * kD + tid * FPT)
+                         : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     const uint16_t* hwin = hw ? hw : h;
-    if (t0 >= 3 && t0 + BT <= T) {
-        // interior block: one uniform base, 32-bit per-lane offsets
-        const char* eb = reinterpret_cast<const char*>(e16) + (t0 - 3) * (kD * 2);
-        const char* hb = reinterpret_cast<const char*>(h) + (t0 - 3) * (kD * 2);
-        const char* wb = reinterpret_cast<const char*>(hwin) + (t0 - 3) * (kD * 2);
+    u32x2 ep[4], hp[4];
 #pragma unroll
-        for (int i = 0; i < kWin; ++i) {
-            const uint32_t off = cb + (uint32_t)(i * kD * 2);
-            ep[i] = *reinterpret_cast<const u32x2*>(eb + off);
-            hp[i] = *reinterpret_cast<const u32x2*>((i < 3 ? wb : hb) + off);
-        }
-    } else {
-        // first and last blocks: unconditional loads from a clamped (in-bounds)
-        // row, then a select, so no branches around the loads
-#pragma unroll
-        for (int i = 0; i < kWin; ++i) {
-            const int64_t t = t0 - 3 + i;
-            const bool in = t >= 0 && t < T;
-            const int64_t tc = t < 0 ? 0 : (t >= T ? T - 1 : t);
-            const u32x2 qe = *reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(e16) + tc * (kD * 2) + cb);
-            const u32x2 qh = *reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(i < 3 ? hwin : h) +
-                                                             tc * (kD * 2) + cb);
-            ep[i] = in ? qe : zero;
-            hp[i] = in ? qh : zero;
-        }
-    }
-
-    // gate sums: four features per thread (bf16 dot products), then the rows
-    // of 16 lanes; lane 15 of each row keeps the row's sums
-#pragma unroll
-    for (int i = 0; i < kWin; ++i) gate_rows(ep[i], hp[i], lane, wave, red_s[i]);
-    __syncthreads();
-    if (tid < kWin) {
-        const int64_t t = t0 - 3 + tid;
-        if (t >= 0 && t < T) {
-            float ee = 0.0f, he = 0.0f, hh = 0.0f;
-#pragma unroll 8
-            for (int r = 0; r < kRows; ++r) {
-                ee += red_s[tid][r][0];
-                he += red_s[tid][r][1];
-                hh += red_s[tid][r][2];
-            }
-            const float g = gate_of(ee, he, hh, eps);
-            g_s[tid] = g;
-            if (gate_out && tid >= 3) gate_out[t] = g;
-            const int s = seq_of(cu, S, t);
-            int64_t st = cu[s], en = cu[s + 1];
-            if (st < 0 || st > t) st = t;            // malformed cu_seqlens: stay in bounds
-            if (en <= t || en > T) en = t + 1;
-            seg_s[tid] = s;
-            start_s[tid] = (int)st;
-            end_s[tid] = (int)en;
+    for (int k = 0; k < 4; ++k) {
+        if (k >= first) {
+            const int64_t p = t - 3 + k;
+            ep[k] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(e16 + p * kD) + cb);
+            hp[k] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>((k < 3 ? hwin : h) + p * kD) + cb);
         } else {
-            g_s[tid] = 0.0f;
-            seg_s[tid] = 0;
-            start_s[tid] = 0;
-            end_s[tid] = 0;
+            ep[k] = u32x2{0u, 0u};
+            hp[k] = u32x2{0u, 0u};
         }
     }
-    __syncthreads();
-
     float w[FPT][kTaps];
     {
         const u32x4* wp = reinterpret_cast<const u32x4*>(conv_w + tid * FPT * kTaps);
@@ -237,68 +185,53 @@ fuse_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ e16, in
         }
     }
 
-    // v = g e at every window position
-    float v[kWin][FPT];
 #pragma unroll
-    for (int j = 0; j < kWin; ++j) {
-        float e[FPT];
-        unpack4(ep[j], e);
-        const float g = g_s[j];
-#pragma unroll
-        for (int q = 0; q < FPT; ++q) v[j][q] = g * e[q];
+    for (int k = 0; k < 4; ++k)
+        if (k >= first) gate_rows(ep[k], hp[k], lane, wave, red_s[k]);
+    __syncthreads();
+    if (tid < 4 && tid >= first) {
+        float ee = 0.0f, he = 0.0f, hh = 0.0f;
+#pragma unroll 8
+        for (int r = 0; r < kRows; ++r) {
+            ee += red_s[tid][r][0];
+            he += red_s[tid][r][1];
+            hh += red_s[tid][r][2];
+        }
+        const float g = gate_of(ee, he, hh, eps);
+        g_s[tid] = g;
+        if (gate_out && tid == 3) gate_out[t] = g;
     }
-    char* ob = reinterpret_cast<char*>(out) + t0 * (kD * 2);
+    __syncthreads();
+
+    // taps: v = g e inside the sequence, the carried state before it
+    float a[4][FPT];
 #pragma unroll
-    for (int i = 0; i < BT; ++i) {
-        const int64_t t = t0 + i;
-        if (t >= T) break;
-        // sequence bounds of token t are the same in every lane: keep them scalar
-        const int s = __builtin_amdgcn_readfirstlane(seg_s[i + 3]);
-        const int st = __builtin_amdgcn_readfirstlane(start_s[i + 3]);
-        const int en = __builtin_amdgcn_readfirstlane(end_s[i + 3]);
-        // tap k is position t-3+k (window slot i+k); before the sequence start
-        // it comes from the carried state
-        auto tap = [&](int k, float a[FPT]) {
-            const int p = (int)t - 3 + k;
-            if (p >= st) {
+    for (int k = 0; k < 4; ++k) {
+        if (k < first) {
 #pragma unroll
-                for (int q = 0; q < FPT; ++q) a[q] = v[i + k][q];
-            } else {
-                const f32x4 c = *reinterpret_cast<const f32x4*>(snap + ((int64_t)s * 3 + 3 - (st - p)) * kD +
-                                                                tid * FPT);
-#pragma unroll
-                for (int q = 0; q < FPT; ++q) a[q] = c[q];
-            }
-        };
-        float y[FPT];
-        if ((int)t - 3 >= st) {
-#pragma unroll
-            for (int q = 0; q < FPT; ++q) y[q] = conv4(w[q], v[i][q], v[i + 1][q], v[i + 2][q], v[i + 3][q]);
+            for (int q = 0; q < FPT; ++q) a[k][q] = c[k][q];
         } else {
-            float a0[FPT], a1[FPT], a2[FPT], a3[FPT];
-            tap(0, a0);
-            tap(1, a1);
-            tap(2, a2);
-            tap(3, a3);
+            float e[FPT];
+            unpack4(ep[k], e);
+            const float g = g_s[k];
 #pragma unroll
-            for (int q = 0; q < FPT; ++q) y[q] = conv4(w[q], a0[q], a1[q], a2[q], a3[q]);
+            for (int q = 0; q < FPT; ++q) a[k][q] = g * e[q];
         }
-        float hv[FPT];
-        unpack4(hp[i + 3], hv);
-        const u32x2 o = {pack_bf16x2(hv[0] + y[0], hv[1] + y[1]), pack_bf16x2(hv[2] + y[2], hv[3] + y[3])};
-        __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(ob + (cb + (uint32_t)(i * kD * 2))));
-        if (y_out) *reinterpret_cast<f32x4*>(y_out + t * kD + tid * FPT) = f32x4{y[0], y[1], y[2], y[3]};
-        if ((int)t == en - 1) {
-            // last token of sequence s: new conv state = v at t-2, t-1, t
+    }
+    float y[FPT], hv[FPT];
 #pragma unroll
-            for (int r = 0; r < 3; ++r) {
-                float a[FPT];
-                tap(r + 1, a);
-                *reinterpret_cast<f32x4*>(conv_state + ((int64_t)s * 3 + r) * kD + tid * FPT) =
-                    f32x4{a[0], a[1], a[2], a[3]};
-            }
-            if (tid == 0) update_history(tokens, hist_ids, hist_len, s, st, en);
-        }
+    for (int q = 0; q < FPT; ++q) y[q] = conv4(w[q], a[0][q], a[1][q], a[2][q], a[3][q]);
+    unpack4(hp[3], hv);
+    const u32x2 o = {pack_bf16x2(hv[0] + y[0], hv[1] + y[1]), pack_bf16x2(hv[2] + y[2], hv[3] + y[3])};
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(reinterpret_cast<char*>(out + t * kD) + cb));
+    if (y_out) *reinterpret_cast<f32x4*>(y_out + t * kD + tid * FPT) = f32x4{y[0], y[1], y[2], y[3]};
+    if (t == en - 1) {
+        // last token of sequence s: new conv state = v at t-2, t-1, t
+        float* dp = conv_state + (int64_t)s * 3 * kD + tid * FPT;
+#pragma unroll
+        for (int r = 0; r < 3; ++r)
+            *reinterpret_cast<f32x4*>(dp + r * kD) = f32x4{a[r + 1][0], a[r + 1][1], a[r + 1][2], a[r + 1][3]};
+        if (tid == 0) update_history(tokens, hist_ids, hist_len, s, st, en);
     }
 }
 
@@ -428,7 +361,9 @@ fuse_stream_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
                 st = en;
                 en = cu[s + 1];
             }
-            if (en <= t || en > T) en = t + 1;  // malformed cu_seqlens: stay in bounds
+            // malformed cu_seqlens (flagged by the ID kernel): stay in bounds
+            if (st < 0 || st > t) st = t;
+            if (en <= t || en > T) en = t + 1;
             if (t == st) {
                 // a sequence starts: its three earlier taps are the carried state
                 const float* sp = snap + (int64_t)s * 3 * kD + tid * FPT;
@@ -524,7 +459,7 @@ hipError_t launch_fuse(const uint16_t* h, const uint16_t* e16, int64_t T, const 
             hipError_t e = hipMemcpyAsync(h_copy, h, (size_t)T * kD * 2, hipMemcpyDeviceToDevice, stream);
             if (e != hipSuccess) return e;
         }
-        hipLaunchKernelGGL(fuse_kernel<1>, dim3((unsigned)T), dim3(kThreads), 0, stream, h, e16, T, cu,
+        hipLaunchKernelGGL(fuse_token_kernel, dim3((unsigned)T), dim3(kThreads), 0, stream, h, e16, T, cu,
                            S, tokens, conv_w, state_snap, conv_state, hist_ids, hist_len, out, eps,
                            gate_out, y_out, in_place ? h_copy : nullptr);
     } else {

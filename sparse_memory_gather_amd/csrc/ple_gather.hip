@@ -15,7 +15,7 @@
 //     row IDs, plain stores of this layout take 19% longer and 32 bytes per
 //     lane per 16-byte load (each store instruction covering every other
 //     16-byte slot) 29% longer.
-#include "ple_kernels.h"
+#include "ple_ngram.h"
 
 namespace ple {
 namespace {
@@ -37,17 +37,40 @@ __device__ __forceinline__ void decode8(const u32x2& q, float s, float out[8]) {
     }
 }
 
+// kIds: the wave computes its token's two row IDs itself (short calls: one
+// launch instead of the ID kernel and this one). The launch then also
+// checks cu_seqlens (block 0) and copies the carried conv state (grid row 1),
+// as the ID kernel would.
+template <bool kIds>
 __global__ void __launch_bounds__(64 * kTokPerBlock)
 gather_kernel(const int32_t* __restrict__ row_ids, int64_t T, const uint8_t* __restrict__ table,
               const float* __restrict__ scales, int64_t R, uint16_t* __restrict__ x,
-              uint8_t* __restrict__ raw, int32_t* dev_err) {
+              uint8_t* __restrict__ raw, int32_t* dev_err, IdSource src) {
 #pragma clang fp contract(off)
     const int lane = threadIdx.x & 63;
+    if (kIds && blockIdx.y == 1) {
+        const f32x4* from = reinterpret_cast<const f32x4*>(src.conv_state);
+        f32x4* to = reinterpret_cast<f32x4*>(src.snap);
+        for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < src.snap_vec4;
+             i += (int64_t)gridDim.x * blockDim.x)
+            to[i] = from[i];
+        return;
+    }
+    if (kIds && blockIdx.x == 0) check_cu(src.cu, src.S, T, dev_err);
     const int64_t t = (int64_t)blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
     if (t >= T) return;
-    int2 ids = reinterpret_cast<const int2*>(row_ids)[t];
-    int r0 = __builtin_amdgcn_readfirstlane(ids.x);
-    int r1 = __builtin_amdgcn_readfirstlane(ids.y);
+    int r0, r1;
+    if (kIds) {
+        const NgramKeys k = ngram_keys(t, src.tokens, src.cu, src.S, src.hist_ids, src.hist_len, src.vocab,
+                                       dev_err);
+        r0 = __builtin_amdgcn_readfirstlane(k.j >= 1 ? (int32_t)(splitmix_finalize(k.k2) % (uint64_t)R) : -1);
+        r1 = __builtin_amdgcn_readfirstlane(k.j >= 2 ? (int32_t)(splitmix_finalize(k.k3) % (uint64_t)R) : -1);
+        if (src.row_ids_out && lane == 0) reinterpret_cast<int2*>(src.row_ids_out)[t] = make_int2(r0, r1);
+    } else {
+        const int2 ids = reinterpret_cast<const int2*>(row_ids)[t];
+        r0 = __builtin_amdgcn_readfirstlane(ids.x);
+        r1 = __builtin_amdgcn_readfirstlane(ids.y);
+    }
     if (r0 < -1 || (int64_t)r0 >= R) {
         if (lane == 0) flag_error(dev_err, 8);
         r0 = -1;
@@ -274,8 +297,19 @@ hipError_t launch_gather(const int32_t* row_ids, int64_t T, const uint8_t* table
                          const float* scales, int64_t R, uint16_t* x, uint8_t* raw,
                          int32_t* dev_err, hipStream_t stream) {
     int64_t blocks = (T + kTokPerBlock - 1) / kTokPerBlock;
-    hipLaunchKernelGGL(gather_kernel, dim3((unsigned)blocks), dim3(64 * kTokPerBlock), 0, stream,
-                       row_ids, T, table, scales, R, x, raw, dev_err);
+    hipLaunchKernelGGL(gather_kernel<false>, dim3((unsigned)blocks), dim3(64 * kTokPerBlock), 0, stream,
+                       row_ids, T, table, scales, R, x, raw, dev_err, IdSource{});
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_ids(const IdSource& src, int64_t T, const uint8_t* table, const float* scales,
+                             int64_t R, uint16_t* x, int32_t* dev_err, hipStream_t stream) {
+    int64_t blocks = (T + kTokPerBlock - 1) / kTokPerBlock;
+    const int64_t snap_blocks = (src.snap_vec4 + 64 * kTokPerBlock - 1) / (64 * kTokPerBlock);
+    if (snap_blocks > blocks) blocks = snap_blocks < 65536 ? snap_blocks : 65536;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(gather_kernel<true>, dim3((unsigned)blocks, src.snap ? 2 : 1), dim3(64 * kTokPerBlock), 0,
+                       stream, nullptr, T, table, scales, R, x, nullptr, dev_err, src);
     return hipGetLastError();
 }
 

@@ -15,16 +15,10 @@
 // bigram key, heads 8..15 on the trigram key, head h finalizing
 // key + (h mod 8) * 0x9E3779B97F4A7C15 (the h-th SplitMix64 output from the
 // key), so heads 0 and 8 equal the two-lookup IDs.
-#include "ple_kernels.h"
+#include "ple_ngram.h"
 
 namespace ple {
 namespace {
-
-__device__ __forceinline__ uint64_t splitmix_finalize(uint64_t z) {
-    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
-    z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
-    return z ^ (z >> 31);
-}
 
 constexpr int kHashBlock = 256;
 constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ULL;
@@ -46,43 +40,12 @@ hash_kernel(const int32_t* __restrict__ tokens, int64_t T, const int32_t* __rest
             dst[i] = src[i];
         return;
     }
-    // boundary checks (block 0 only): cu[0] == 0, non-decreasing, cu[S] == T
-    if (blockIdx.x == 0) {
-        for (int i = threadIdx.x; i <= S; i += kHashBlock) {
-            int32_t c = cu[i];
-            bool bad = (i == 0 && c != 0) || (i == S && c != T) || (i < S && c > cu[i + 1]);
-            if (bad) flag_error(dev_err, 2);
-        }
-    }
-    int64_t t = (int64_t)blockIdx.x * kHashBlock + threadIdx.x;
+    if (blockIdx.x == 0) check_cu(cu, S, T, dev_err);
+    const int64_t t = (int64_t)blockIdx.x * kHashBlock + threadIdx.x;
     if (t >= T) return;
-    // sequence of token t: the last s with cu[s] <= t
-    int lo = 0, hi = S - 1;
-    while (lo < hi) {
-        int mid = (lo + hi + 1) >> 1;
-        if ((int64_t)cu[mid] <= t) lo = mid; else hi = mid - 1;
-    }
-    const int s = lo;
-    int64_t start = cu[s];
-    if (start < 0 || start > t) start = t;  // malformed cu_seqlens (flagged above): stay in bounds
-    int hl = hist_len[s];
-    if (hl < 0 || hl > 2) {
-        flag_error(dev_err, 4);
-        hl = 0;
-    }
-    const int64_t j = hl + (t - start);  // index of token t in history ++ chunk
-    auto seq_at = [&](int64_t idx) -> uint32_t {
-        int32_t v = idx < hl ? hist_ids[2 * s + 2 - hl + idx] : tokens[start + idx - hl];
-        if (v < 0 || v >= vocab) flag_error(dev_err, 1);
-        return (uint32_t)v & 0xFFFFFu;
-    };
-    const uint32_t c = seq_at(j);
-    uint64_t k2 = 0, k3 = 0;
-    if (j >= 1) {
-        const uint32_t b = seq_at(j - 1);
-        k2 = (2ULL << 60) | ((uint64_t)b << 20) | c;
-        if (j >= 2) k3 = (3ULL << 60) | ((uint64_t)seq_at(j - 2) << 40) | ((uint64_t)b << 20) | c;
-    }
+    const NgramKeys k = ngram_keys(t, tokens, cu, S, hist_ids, hist_len, vocab, dev_err);
+    const int64_t j = k.j;
+    const uint64_t k2 = k.k2, k3 = k.k3;
     if (kHeads == 0) {
         const int32_t r2 = j >= 1 ? (int32_t)(splitmix_finalize(k2) % R) : -1;
         const int32_t r3 = j >= 2 ? (int32_t)(splitmix_finalize(k3) % R) : -1;

@@ -28,6 +28,20 @@ __device__ __forceinline__ void flag_error(int32_t* dev_err, int bit) {
     if (dev_err) atomicOr(dev_err, bit);
 }
 
+// what a gather launch needs to compute its own row IDs (launch_gather_ids)
+struct IdSource {
+    const int32_t* tokens;
+    const int32_t* cu;
+    int32_t S;
+    const int32_t* hist_ids;
+    const int32_t* hist_len;
+    int32_t vocab;
+    int32_t* row_ids_out;     // int32 [T][2], or NULL
+    const float* conv_state;  // copied to snap (snap_vec4 float4s) when snap is not NULL
+    float* snap;
+    int64_t snap_vec4;
+};
+
 // ---- launchers (each returns hipGetLastError()) ----------------------------
 
 // n-gram IDs for T tokens (2 per token, or 16 with heads); optionally also
@@ -52,6 +66,11 @@ hipError_t launch_state_copy(const float* conv_state, float* state_snap, int32_t
 hipError_t launch_gather_heads(const int32_t* row_ids, int64_t T, const uint8_t* table,
                                const float* scales, int64_t R, uint16_t* x, uint8_t* raw,
                                int32_t* dev_err, hipStream_t stream);
+
+// the two-lookup FP8 gather computing each token's IDs itself (the ID
+// kernel's work, cu_seqlens checks and state copy included)
+hipError_t launch_gather_ids(const IdSource& src, int64_t T, const uint8_t* table, const float* scales,
+                             int64_t R, uint16_t* x, int32_t* dev_err, hipStream_t stream);
 
 hipError_t launch_gather(const int32_t* row_ids, int64_t T, const uint8_t* table,
                          const float* scales, int64_t R, uint16_t* x, uint8_t* raw,

@@ -283,6 +283,60 @@ def test_in_place_equals_out_of_place_both_fuse_kernels(dev, small_table, dev_we
     assert np.array_equal(host_bits(hd), host_bits(ref))
 
 
+@pytest.mark.parametrize("T", [300, 2000])
+def test_forward_flags_bad_inputs_on_the_device(dev, small_table, dev_weights, T):
+    # 300 tokens: IDs computed inside the gather, one-token fuse; 2000: the
+    # ID kernel and the streaming fuse. Bad values the host cannot see are
+    # flagged in dev_err (1: token ID outside the vocabulary, 4: hist_len
+    # outside 0..2, 2: malformed cu_seqlens) and every kernel stays in bounds.
+    tab, sc = small_table
+    rng = np.random.default_rng(T)
+    h = dev_bf16(inputs.normal_bf16(rng, (T, D)), dev)
+
+    def run(toks, cu, hist_len):
+        st = ple.State(len(cu) - 1, dev)
+        st.hist_len.copy_(dev_i32(hist_len, dev))
+        err = torch.zeros(1, dtype=torch.int32, device=dev)
+        out = ple.ple_forward(dev_i32(toks, dev), dev_i32(cu, dev), tab, sc, dev_weights[0], dev_weights[1], h,
+                              st, dev_err=err)
+        torch.cuda.synchronize()
+        return int(err.item()), out
+
+    toks = inputs.uniform_tokens(rng, T)
+    good_cu = np.array([0, T // 2, T], np.int32)
+    assert run(toks, good_cu, [0, 0])[0] == 0
+    bad = toks.copy()
+    bad[T // 3] = inputs.VOCAB + 7
+    assert run(bad, good_cu, [0, 0])[0] == 1
+    assert run(toks, good_cu, [0, 5])[0] == 4
+    err, out = run(toks, np.array([0, T // 2, T // 4, T - 1], np.int32), [0, 0, 0])
+    assert err == 2
+    assert out.shape == (T, D)
+
+
+def test_prepared_forward_reuses_its_buffers(dev, small_table, dev_weights):
+    # a prepared call run on fixed buffers whose contents change between
+    # steps (a decode loop) equals ple_forward on each step's inputs
+    tab, sc = small_table
+    rng = np.random.default_rng(33)
+    S = 8
+    cu = dev_i32(np.arange(S + 1), dev)
+    toks_buf = torch.empty(S, dtype=torch.int32, device=dev)
+    h_buf = torch.empty((S, D), dtype=torch.bfloat16, device=dev)
+    st_a, st_b = ple.State(S, dev), ple.State(S, dev)
+    call = ple.Forward(toks_buf, cu, tab, sc, dev_weights[0], dev_weights[1], h_buf, st_a)
+    for step in range(4):
+        toks = inputs.uniform_tokens(rng, S)
+        h = inputs.normal_bf16(rng, (S, D))
+        toks_buf.copy_(dev_i32(toks, dev))
+        h_buf.copy_(dev_bf16(h, dev))
+        got = host_bits(call())
+        want = host_bits(ple.ple_forward(dev_i32(toks, dev), cu, tab, sc, dev_weights[0], dev_weights[1],
+                                         dev_bf16(h, dev), st_b))
+        assert np.array_equal(got, want), step
+    assert torch.equal(st_a.conv_state, st_b.conv_state) and torch.equal(st_a.hist_ids, st_b.hist_ids)
+
+
 def test_in_place_out_equals_h(dev, small_table, dev_weights):
     tab, sc = small_table
     rng = np.random.default_rng(7)
