@@ -63,8 +63,9 @@ gather_kernel(const int32_t* __restrict__ row_ids, int64_t T, const uint8_t* __r
     if (kIds) {
         const NgramKeys k = ngram_keys(t, src.tokens, src.cu, src.S, src.hist_ids, src.hist_len, src.vocab,
                                        dev_err);
-        r0 = __builtin_amdgcn_readfirstlane(k.j >= 1 ? (int32_t)(splitmix_finalize(k.k2) % (uint64_t)R) : -1);
-        r1 = __builtin_amdgcn_readfirstlane(k.j >= 2 ? (int32_t)(splitmix_finalize(k.k3) % (uint64_t)R) : -1);
+        const ModR mr{src.mod_R, src.mod_m};
+        r0 = __builtin_amdgcn_readfirstlane(k.j >= 1 ? (int32_t)mod_r(splitmix_finalize(k.k2), mr) : -1);
+        r1 = __builtin_amdgcn_readfirstlane(k.j >= 2 ? (int32_t)mod_r(splitmix_finalize(k.k3), mr) : -1);
         if (src.row_ids_out && lane == 0) reinterpret_cast<int2*>(src.row_ids_out)[t] = make_int2(r0, r1);
     } else {
         const int2 ids = reinterpret_cast<const int2*>(row_ids)[t];
@@ -308,8 +309,12 @@ hipError_t launch_gather_ids(const IdSource& src, int64_t T, const uint8_t* tabl
     const int64_t snap_blocks = (src.snap_vec4 + 64 * kTokPerBlock - 1) / (64 * kTokPerBlock);
     if (snap_blocks > blocks) blocks = snap_blocks < 65536 ? snap_blocks : 65536;
     if (blocks < 1) blocks = 1;
+    IdSource s = src;
+    const ModR mr = make_mod((uint64_t)R);
+    s.mod_R = mr.R;
+    s.mod_m = mr.m;
     hipLaunchKernelGGL(gather_kernel<true>, dim3((unsigned)blocks, src.snap ? 2 : 1), dim3(64 * kTokPerBlock), 0,
-                       stream, nullptr, T, table, scales, R, x, nullptr, dev_err, src);
+                       stream, nullptr, T, table, scales, R, x, nullptr, dev_err, s);
     return hipGetLastError();
 }
 

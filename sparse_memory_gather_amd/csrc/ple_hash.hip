@@ -28,7 +28,7 @@ template <int kHeads>
 __global__ void __launch_bounds__(kHashBlock)
 hash_kernel(const int32_t* __restrict__ tokens, int64_t T, const int32_t* __restrict__ cu, int32_t S,
             const int32_t* __restrict__ hist_ids, const int32_t* __restrict__ hist_len,
-            int32_t vocab, uint64_t R, int32_t* __restrict__ row_ids, int32_t* dev_err,
+            int32_t vocab, ModR mr, int32_t* __restrict__ row_ids, int32_t* dev_err,
             const float* __restrict__ conv_state, float* __restrict__ state_snap,
             int64_t snap_vec4) {
     if (blockIdx.y == 1) {
@@ -47,15 +47,15 @@ hash_kernel(const int32_t* __restrict__ tokens, int64_t T, const int32_t* __rest
     const int64_t j = k.j;
     const uint64_t k2 = k.k2, k3 = k.k3;
     if (kHeads == 0) {
-        const int32_t r2 = j >= 1 ? (int32_t)(splitmix_finalize(k2) % R) : -1;
-        const int32_t r3 = j >= 2 ? (int32_t)(splitmix_finalize(k3) % R) : -1;
+        const int32_t r2 = j >= 1 ? (int32_t)mod_r(splitmix_finalize(k2), mr) : -1;
+        const int32_t r3 = j >= 2 ? (int32_t)mod_r(splitmix_finalize(k3), mr) : -1;
         reinterpret_cast<int2*>(row_ids)[t] = make_int2(r2, r3);
     } else {
         int32_t id[16];
 #pragma unroll
         for (int h = 0; h < 8; ++h) {
-            id[h] = j >= 1 ? (int32_t)(splitmix_finalize(k2 + (uint64_t)h * kGamma) % R) : -1;
-            id[8 + h] = j >= 2 ? (int32_t)(splitmix_finalize(k3 + (uint64_t)h * kGamma) % R) : -1;
+            id[h] = j >= 1 ? (int32_t)mod_r(splitmix_finalize(k2 + (uint64_t)h * kGamma), mr) : -1;
+            id[8 + h] = j >= 2 ? (int32_t)mod_r(splitmix_finalize(k3 + (uint64_t)h * kGamma), mr) : -1;
         }
         int4* dst = reinterpret_cast<int4*>(row_ids + t * 16);
 #pragma unroll
@@ -93,11 +93,11 @@ hipError_t launch_hash(const int32_t* tokens, int64_t T, const int32_t* cu, int3
     dim3 grid((unsigned)blocks, state_snap ? 2 : 1);
     if (heads)
         hipLaunchKernelGGL(hash_kernel<16>, grid, dim3(kHashBlock), 0, stream, tokens, T, cu, S, hist_ids,
-                           hist_len, vocab, (uint64_t)R, row_ids, dev_err, conv_state, state_snap,
+                           hist_len, vocab, make_mod((uint64_t)R), row_ids, dev_err, conv_state, state_snap,
                            snap_vec4);
     else
         hipLaunchKernelGGL(hash_kernel<0>, grid, dim3(kHashBlock), 0, stream, tokens, T, cu, S, hist_ids,
-                           hist_len, vocab, (uint64_t)R, row_ids, dev_err, conv_state, state_snap,
+                           hist_len, vocab, make_mod((uint64_t)R), row_ids, dev_err, conv_state, state_snap,
                            snap_vec4);
     return hipGetLastError();
 }

@@ -40,6 +40,7 @@ struct IdSource {
     const float* conv_state;  // copied to snap (snap_vec4 float4s) when snap is not NULL
     float* snap;
     int64_t snap_vec4;
+    uint64_t mod_R, mod_m;  // set by launch_gather_ids (R and its reciprocal for mod_r)
 };
 
 // ---- launchers (each returns hipGetLastError()) ----------------------------

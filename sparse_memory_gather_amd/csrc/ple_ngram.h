@@ -20,6 +20,24 @@ __device__ __forceinline__ uint64_t splitmix_finalize(uint64_t z) {
     return z ^ (z >> 31);
 }
 
+// z mod R without a division (the GPU has none for 64-bit integers): with
+// m = floor((2^64 - 1) / R), the high half of z * m is floor(z / R) or one
+// less (Barrett reduction), so one conditional subtraction of R gives the
+// exact remainder; a second one is kept as a guard.
+struct ModR {
+    uint64_t R, m;
+};
+
+inline ModR make_mod(uint64_t R) { return ModR{R, ~0ULL / R}; }
+
+__device__ __forceinline__ uint32_t mod_r(uint64_t z, const ModR& d) {
+    const uint64_t q = __umul64hi(z, d.m);
+    uint64_t r = z - q * d.R;
+    if (r >= d.R) r -= d.R;
+    if (r >= d.R) r -= d.R;
+    return (uint32_t)r;
+}
+
 // sequence of token t: the last s with cu[s] <= t
 __device__ __forceinline__ int seq_of(const int32_t* cu, int32_t S, int64_t t) {
     int lo = 0, hi = S - 1;

@@ -63,10 +63,31 @@ def test_hash_parity_sequence_boundaries(dev):
     hl = [0, 0, 1, 2, 0, 1, 2, 2, 2]
     toks, cu, hist, hlen, _ = _case(1, lengths, hl)
     toks[:4] = [0, inputs.VOCAB - 1, 0, inputs.VOCAB - 1]  # vocabulary edges
-    for R in (1, 7, 1009, 20_000_096, 2 ** 31 - 1):
+    # the kernels reduce mod R by multiplying with a precomputed reciprocal:
+    # R at 1, 2, 3, powers of two and their neighbours, primes, the full row
+    # count and the largest allowed
+    for R in (1, 2, 3, 7, 1009, 1 << 16, (1 << 20) - 1, 1 << 30, 20_000_096, 2 ** 31 - 1):
         ref = oracle.ngram_ids(toks, cu, hist, hlen, R)
         got = ple.ple_hash(dev_i32(toks, dev), dev_i32(cu, dev), dev_i32(hist, dev), dev_i32(hlen, dev), R)
         assert np.array_equal(got.cpu().numpy(), ref), R
+        ref16 = oracle.ngram_ids_heads(toks, cu, hist, hlen, R)
+        got16 = ple.ple_hash(dev_i32(toks, dev), dev_i32(cu, dev), dev_i32(hist, dev), dev_i32(hlen, dev), R,
+                             heads=True)
+        assert np.array_equal(got16.cpu().numpy(), ref16), R
+
+
+@pytest.mark.parametrize("R", [1, 3, 1009])
+def test_ids_computed_inside_the_gather(dev, dev_weights, R):
+    # calls of up to 1024 tokens compute the IDs in the gather kernel
+    lengths = [1, 2, 3, 5, 300, 0, 700]
+    hl = [0, 1, 2, 0, 1, 2, 2]
+    toks, cu, hist, hlen, h = _case(2, lengths, hl)
+    tab, sc = table.table_gpu(R, device=dev)
+    st = ple.State(len(lengths), dev)
+    st.hist_ids.copy_(dev_i32(hist, dev))
+    st.hist_len.copy_(dev_i32(hlen, dev))
+    res = _forward(dev, tab, sc, dev_weights, toks, cu, h, st)
+    assert np.array_equal(res["row_ids"].cpu().numpy(), oracle.ngram_ids(toks, cu, hist, hlen, R))
 
 
 def test_lookup_parity_raw_bytes_and_x(dev, small_table):
