@@ -250,13 +250,14 @@ def test_kernel_variants_agree_bit_exactly(dev, small_table, dev_weights):
 
 
 def test_streaming_fuse_equals_per_sequence_calls(dev, small_table, dev_weights):
-    # one 1380-token call of eleven sequences with carried state runs the
-    # streaming fuse (block ranges of ~32 tokens cross sequence starts and
-    # ends); each sequence alone (<= 1024 tokens) runs the one-token fuse and
-    # the small-T projection: outputs, gates and the new state must be equal
+    # one 1380-token call of fourteen sequences (three empty, which must keep
+    # their state) with carried state runs the streaming fuse (block ranges of
+    # ~32 tokens cross sequence starts and ends); each sequence alone (<= 1024
+    # tokens) runs the one-token fuse and the small-T projection: outputs,
+    # gates and the new state must be equal
     tab, sc = small_table
-    lengths = [1, 2, 3, 5, 40, 33, 700, 31, 500, 1, 64]
-    hl = [0, 1, 2, 2, 0, 2, 1, 2, 2, 2, 0]
+    lengths = [1, 2, 0, 3, 5, 40, 33, 700, 0, 31, 500, 1, 64, 0]
+    hl = [0, 1, 2, 2, 2, 0, 2, 1, 1, 2, 2, 2, 0, 2]
     toks, cu, hist, hlen, h = _case(91, lengths, hl)
     S = len(lengths)
     rng = np.random.default_rng(92)
