@@ -222,32 +222,37 @@ proj_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __restric
     }
 }
 
-// Small-T projection (decode steps, short chunks): one block per (32-feature,
-// 32-token) tile, eight waves, wave w holding the fragments of k-steps
-// 20w .. 20w+19, all loaded up front. The tile's accumulator passes from
-// wave to wave through LDS, so it sees the same MFMA sequence over k as in
-// proj_kernel and every output element is bit-identical to what proj_kernel
-// produces; the loads of all eight waves are in flight together.
-template <bool kFwd>
+// Small-T projection (decode steps, short chunks): one block per (kRows-
+// feature, 32-token) tile, eight waves, wave w holding the fragments of
+// k-steps 20w .. 20w+19, all loaded up front. The tile's accumulator passes
+// from wave to wave through LDS, so it sees the same MFMA sequence over k as
+// in proj_kernel and every output element is bit-identical to what
+// proj_kernel produces; the loads of all eight waves are in flight together.
+// kRows < 32 leaves the MFMA's other A rows zero (an output element depends
+// only on its own row and column), so that short calls spread the W loads
+// over more CUs: an 8-token step runs 160 blocks of 16 features.
+template <bool kFwd, int kRows>
 __global__ void __launch_bounds__(512)
 proj_small_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __restrict__ W,
                   float* __restrict__ e32, uint16_t* __restrict__ e16) {
+    static_assert(kRows == 16 || kRows == 32, "feature rows per block");
     constexpr int KS = kD / 16;        // 160 k-steps
     constexpr int kW = 8;              // waves
     constexpr int SPW = KS / kW;       // k-steps per wave
     __shared__ f32x16 acc_s[64];       // the accumulator between waves
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int fr = lane & 31, kh = lane >> 5;
-    const int f0 = blockIdx.x * 32;
+    const int f0 = blockIdx.x * kRows;
     const int64_t tok = (int64_t)blockIdx.y * 32 + fr;
     const bool live = tok < M;
-    const uint16_t* wrow = W + (int64_t)(f0 + fr) * kD + wave * SPW * 16 + kh * 8;
+    const bool row = fr < kRows;
+    const uint16_t* wrow = W + (int64_t)(f0 + (row ? fr : 0)) * kD + wave * SPW * 16 + kh * 8;
     const uint16_t* xrow = x + (live ? tok : 0) * kD + wave * SPW * 16 + kh * 8;
     bf16x8 fa[SPW], fb[SPW];
     const bf16x8 zero = {};
 #pragma unroll
     for (int q = 0; q < SPW; ++q) {
-        fa[q] = *reinterpret_cast<const bf16x8*>(wrow + q * 16);
+        fa[q] = row ? *reinterpret_cast<const bf16x8*>(wrow + q * 16) : zero;
         fb[q] = live ? *reinterpret_cast<const bf16x8*>(xrow + q * 16) : zero;
     }
     f32x16 acc;
@@ -265,7 +270,7 @@ proj_small_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __r
     if (wave != kW - 1 || !live) return;
     // lane holds token `tok` and features f0 + 8 g + 4 kh + 0..3
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    for (int g = 0; g < kRows / 8; ++g) {
         const float v0 = acc[4 * g], v1 = acc[4 * g + 1], v2 = acc[4 * g + 2], v3 = acc[4 * g + 3];
         const int64_t off = tok * kD + f0 + g * 8 + kh * 4;
         if (!kFwd || e32) *reinterpret_cast<f32x4*>(e32 + off) = f32x4{v0, v1, v2, v3};
@@ -289,8 +294,16 @@ hipError_t launch(const uint16_t* x, int64_t T, const uint16_t* W, float* e32, u
         allowed.fetch_or(bit, std::memory_order_acq_rel);
     }
     if (T <= kSmallT) {
-        dim3 grid(kD / 32, (unsigned)((T + 31) / 32));
-        hipLaunchKernelGGL(proj_small_kernel<kFwd>, grid, dim3(512), 0, stream, x, T, W, e32, e16);
+        // feature rows per block: one token tile runs 160 blocks of 16 features
+        // (one block per CU at this kernel's register use, so 320 blocks of 8
+        // would take two rounds)
+        const unsigned tiles = (unsigned)((T + 31) / 32);
+        if (tiles == 1)
+            hipLaunchKernelGGL((proj_small_kernel<kFwd, 16>), dim3(kD / 16, tiles), dim3(512), 0, stream, x, T, W,
+                               e32, e16);
+        else
+            hipLaunchKernelGGL((proj_small_kernel<kFwd, 32>), dim3(kD / 32, tiles), dim3(512), 0, stream, x, T, W,
+                               e32, e16);
         return hipGetLastError();
     }
     dim3 grid((unsigned)(kNTiles * ((T + BM - 1) / BM)));

@@ -216,7 +216,9 @@ def test_chunked_equals_unchunked_and_decode_equals_prefill(dev, small_table, de
         return np.concatenate(outs), st.conv_state.cpu().numpy(), st.hist_ids.cpu().numpy()
 
     full = run([n])
-    for cuts in ([1, 2, 3, 264], [256, 14], [100, 0, 170], [1] * 20 + [250]):
+    # pieces of 1-32 and 33-256 tokens run the small-T projection with 16 and
+    # 32 feature rows per block; 257 and more the tiled one
+    for cuts in ([1, 2, 3, 264], [256, 14], [100, 0, 170], [1] * 20 + [250], [40, 64, 33, 32, 101]):
         got = run(cuts)
         for a, b in zip(got, full):
             assert np.array_equal(a, b), cuts
