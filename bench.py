@@ -377,7 +377,7 @@ def main():
                     "traffic": recorded_traffic(gather_name, name),
                     "per_launch": {"bytes": gather_bytes, "avg_us": round(float(stage_us[1]), 2)}}
     else:
-        k = ["ple_hash (hash_kernel)", "", "", "ple_gate_conv_fuse (fuse_stream_kernel / fuse_kernel)"][dominant]
+        k = ["ple_hash (hash_kernel)", "", "", "ple_gate_conv_fuse (fuse_stream_kernel / fuse_token_kernel)"][dominant]
         nb = fuse_bytes if dominant == 3 else tokens_per_call * 12
         gbs = nb / (stage_us[dominant] * 1e-6) / 1e9
         roofline = {"kernel": k, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,

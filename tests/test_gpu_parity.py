@@ -225,9 +225,10 @@ def test_chunked_equals_unchunked_and_decode_equals_prefill(dev, small_table, de
 
 
 def test_kernel_variants_agree_bit_exactly(dev, small_table, dev_weights):
-    # a 1300-token call runs the tiled projection and 16-token fuse blocks;
-    # its pieces (<= 256 and <= 1024 tokens) run the small-T projection and
-    # one-token fuse blocks: every output and the carried state must match
+    # a 1300-token call runs the tiled projection and the streaming fuse; its
+    # pieces (<= 256 and <= 1024 tokens) run the small-T projection, the
+    # in-gather IDs and the one-token fuse: every output and the carried state
+    # must match
     tab, sc = small_table
     rng = np.random.default_rng(16)
     n = 1300
