@@ -222,16 +222,19 @@ proj_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __restric
     }
 }
 
-// Small-T projection (decode steps, short chunks): one block per (kRows-
-// feature, 32-token) tile, eight waves, wave w holding the fragments of
-// k-steps 20w .. 20w+19, all loaded up front. The tile's accumulator passes
-// from wave to wave through LDS, so it sees the same MFMA sequence over k as
-// in proj_kernel and every output element is bit-identical to what
-// proj_kernel produces; the loads of all eight waves are in flight together.
-// kRows < 32 leaves the MFMA's other A rows zero (an output element depends
-// only on its own row and column), so that short calls spread the W loads
-// over more CUs: an 8-token step runs 160 blocks of 16 features.
-template <bool kFwd, int kRows>
+// Small-T projection (decode steps, short chunks): one block per kRows
+// features and kTiles consecutive 32-token tiles, eight waves, wave w holding
+// the fragments of k-steps 20w .. 20w+19, all loaded up front. A tile's
+// accumulator passes from wave to wave through LDS, so it sees the same MFMA
+// sequence over k as in proj_kernel and every output element is
+// bit-identical to what proj_kernel produces. kRows < 32 leaves the MFMA's
+// other A rows zero (an output element depends only on its own row and
+// column), so that an 8-token step spreads its W loads over 160 CUs; kTiles >
+// 1 runs the tiles' chains one after the other with the same W fragments,
+// each wave loading its x fragments of the next tile right after its segment
+// of the current chain, so that calls of up to 256 tokens take one round of
+// blocks (one block per CU fits at this register use).
+template <bool kFwd, int kRows, int kTiles>
 __global__ void __launch_bounds__(512)
 proj_small_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __restrict__ W,
                   float* __restrict__ e32, uint16_t* __restrict__ e16) {
@@ -243,38 +246,46 @@ proj_small_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __r
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int fr = lane & 31, kh = lane >> 5;
     const int f0 = blockIdx.x * kRows;
-    const int64_t tok = (int64_t)blockIdx.y * 32 + fr;
-    const bool live = tok < M;
     const bool row = fr < kRows;
     const uint16_t* wrow = W + (int64_t)(f0 + (row ? fr : 0)) * kD + wave * SPW * 16 + kh * 8;
-    const uint16_t* xrow = x + (live ? tok : 0) * kD + wave * SPW * 16 + kh * 8;
     bf16x8 fa[SPW], fb[SPW];
     const bf16x8 zero = {};
+    auto load_x = [&](int t) {
+        const int64_t tok = ((int64_t)blockIdx.y * kTiles + t) * 32 + fr;
+        const bool live = tok < M;
+        const uint16_t* xrow = x + (live ? tok : 0) * kD + wave * SPW * 16 + kh * 8;
 #pragma unroll
-    for (int q = 0; q < SPW; ++q) {
-        fa[q] = row ? *reinterpret_cast<const bf16x8*>(wrow + q * 16) : zero;
-        fb[q] = live ? *reinterpret_cast<const bf16x8*>(xrow + q * 16) : zero;
-    }
-    f32x16 acc;
+        for (int q = 0; q < SPW; ++q) fb[q] = live ? *reinterpret_cast<const bf16x8*>(xrow + q * 16) : zero;
+    };
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-    for (int w = 0; w < kW; ++w) {
-        if (wave == w) {
-            if (w > 0) acc = acc_s[lane];
+    for (int q = 0; q < SPW; ++q) fa[q] = row ? *reinterpret_cast<const bf16x8*>(wrow + q * 16) : zero;
+    load_x(0);
 #pragma unroll
-            for (int q = 0; q < SPW; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[q], fb[q], acc, 0, 0, 0);
-            if (w + 1 < kW) acc_s[lane] = acc;
+    for (int t = 0; t < kTiles; ++t) {
+        f32x16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+        for (int w = 0; w < kW; ++w) {
+            if (wave == w) {
+                if (w > 0) acc = acc_s[lane];
+#pragma unroll
+                for (int q = 0; q < SPW; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[q], fb[q], acc, 0, 0, 0);
+                if (w + 1 < kW) acc_s[lane] = acc;
+                if (t + 1 < kTiles) load_x(t + 1);
+            }
+            __syncthreads();
         }
-        __syncthreads();
-    }
-    if (wave != kW - 1 || !live) return;
-    // lane holds token `tok` and features f0 + 8 g + 4 kh + 0..3
+        const int64_t tok = ((int64_t)blockIdx.y * kTiles + t) * 32 + fr;
+        if (wave == kW - 1 && tok < M) {
+            // lane holds token `tok` and features f0 + 8 g + 4 kh + 0..3
 #pragma unroll
-    for (int g = 0; g < kRows / 8; ++g) {
-        const float v0 = acc[4 * g], v1 = acc[4 * g + 1], v2 = acc[4 * g + 2], v3 = acc[4 * g + 3];
-        const int64_t off = tok * kD + f0 + g * 8 + kh * 4;
-        if (!kFwd || e32) *reinterpret_cast<f32x4*>(e32 + off) = f32x4{v0, v1, v2, v3};
-        if (kFwd) *reinterpret_cast<u32x2*>(e16 + off) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+            for (int g = 0; g < kRows / 8; ++g) {
+                const float v0 = acc[4 * g], v1 = acc[4 * g + 1], v2 = acc[4 * g + 2], v3 = acc[4 * g + 3];
+                const int64_t off = tok * kD + f0 + g * 8 + kh * 4;
+                if (!kFwd || e32) *reinterpret_cast<f32x4*>(e32 + off) = f32x4{v0, v1, v2, v3};
+                if (kFwd) *reinterpret_cast<u32x2*>(e16 + off) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+            }
+        }
     }
 }
 
@@ -294,16 +305,21 @@ hipError_t launch(const uint16_t* x, int64_t T, const uint16_t* W, float* e32, u
         allowed.fetch_or(bit, std::memory_order_acq_rel);
     }
     if (T <= kSmallT) {
-        // feature rows per block: one token tile runs 160 blocks of 16 features
-        // (one block per CU at this kernel's register use, so 320 blocks of 8
-        // would take two rounds)
+        // about 160 blocks: one token tile runs 16 features per block, up to
+        // 3 tiles one block per (32-feature, tile), more tiles 2 or 4 per block
         const unsigned tiles = (unsigned)((T + 31) / 32);
         if (tiles == 1)
-            hipLaunchKernelGGL((proj_small_kernel<kFwd, 16>), dim3(kD / 16, tiles), dim3(512), 0, stream, x, T, W,
+            hipLaunchKernelGGL((proj_small_kernel<kFwd, 16, 1>), dim3(kD / 16, 1), dim3(512), 0, stream, x, T, W,
                                e32, e16);
+        else if (tiles <= 3)
+            hipLaunchKernelGGL((proj_small_kernel<kFwd, 32, 1>), dim3(kD / 32, tiles), dim3(512), 0, stream, x, T,
+                               W, e32, e16);
+        else if (tiles <= 6)
+            hipLaunchKernelGGL((proj_small_kernel<kFwd, 32, 2>), dim3(kD / 32, (tiles + 1) / 2), dim3(512), 0, stream,
+                               x, T, W, e32, e16);
         else
-            hipLaunchKernelGGL((proj_small_kernel<kFwd, 32>), dim3(kD / 32, tiles), dim3(512), 0, stream, x, T, W,
-                               e32, e16);
+            hipLaunchKernelGGL((proj_small_kernel<kFwd, 32, 4>), dim3(kD / 32, (tiles + 3) / 4), dim3(512), 0, stream,
+                               x, T, W, e32, e16);
         return hipGetLastError();
     }
     dim3 grid((unsigned)(kNTiles * ((T + BM - 1) / BM)));

@@ -216,9 +216,11 @@ def test_chunked_equals_unchunked_and_decode_equals_prefill(dev, small_table, de
         return np.concatenate(outs), st.conv_state.cpu().numpy(), st.hist_ids.cpu().numpy()
 
     full = run([n])
-    # pieces of 1-32 and 33-256 tokens run the small-T projection with 16 and
-    # 32 feature rows per block; 257 and more the tiled one
-    for cuts in ([1, 2, 3, 264], [256, 14], [100, 0, 170], [1] * 20 + [250], [40, 64, 33, 32, 101]):
+    # pieces of up to 256 tokens run the small-T projection (16 feature rows
+    # per block for 1-32 tokens, 32 rows and 1, 2 or 4 token tiles per block
+    # above), 257 and more the tiled one
+    for cuts in ([1, 2, 3, 264], [256, 14], [100, 0, 170], [1] * 20 + [250], [40, 64, 33, 32, 101],
+                 [150, 120], [200, 70]):
         got = run(cuts)
         for a, b in zip(got, full):
             assert np.array_equal(a, b), cuts
