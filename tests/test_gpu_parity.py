@@ -364,6 +364,44 @@ def test_prepared_forward_reuses_its_buffers(dev, small_table, dev_weights):
     assert torch.equal(st_a.conv_state, st_b.conv_state) and torch.equal(st_a.hist_ids, st_b.hist_ids)
 
 
+@pytest.mark.parametrize("T,S", [(8, 8), (1300, 2)])
+def test_graph_captured_forward_replays_like_eager(dev, small_table, dev_weights, T, S):
+    # a prepared call captured into a HIP graph (nothing in the path records a
+    # memset) and replayed three times, with eager work and synchronizations
+    # in between, advances the state exactly as three eager calls do
+    tab, sc = small_table
+    rng = np.random.default_rng(T)
+    toks = dev_i32(inputs.uniform_tokens(rng, T), dev)
+    cu = dev_i32(np.linspace(0, T, S + 1).astype(np.int32), dev)
+    h = dev_bf16(inputs.normal_bf16(rng, (T, D)), dev)
+    st_g, st_e = ple.State(S, dev), ple.State(S, dev)
+    out_g = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    call = ple.Forward(toks, cu, tab, sc, dev_weights[0], dev_weights[1], h, st_g, out=out_g)
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        call()                                   # warm-up outside the graph
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    st_g.hist_ids.zero_()
+    st_g.hist_len.zero_()
+    st_g.conv_state.zero_()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        call()
+    torch.cuda.synchronize()
+    # capture does not run the work: the state is still fresh
+    assert int(st_g.hist_len.abs().sum().item()) == 0
+    for rep in range(3):
+        g.replay()
+        want = ple.ple_forward(toks, cu, tab, sc, dev_weights[0], dev_weights[1], h, st_e)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(out_g), host_bits(want)), rep
+        assert torch.equal(st_g.conv_state, st_e.conv_state) and torch.equal(st_g.hist_ids, st_e.hist_ids), rep
+        _ = torch.randn(1000, device=dev).sum().item()   # unrelated eager work between replays
+
+
 def test_in_place_out_equals_h(dev, small_table, dev_weights):
     tab, sc = small_table
     rng = np.random.default_rng(7)
