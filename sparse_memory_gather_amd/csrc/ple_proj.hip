@@ -289,10 +289,129 @@ proj_small_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __r
     }
 }
 
+// Mid-size calls (257-1536 tokens): tiles of 128 tokens x 256 features so
+// that more blocks share the chip (the 256 x 256 tiles give such calls only
+// 20-60 blocks). Eight waves, each 64 features x 64 tokens (2 x 2 MFMA
+// tiles); both operands through LDS as in proj_kernel, 48 KB stages. The k
+// order of every output is proj_kernel's, so the bits are the same.
+constexpr int kMidT = 1536;           // largest call served by proj_mid_kernel
+constexpr int BMM = 128;              // tokens per block
+constexpr int STM = (BN + BMM) * BK;  // bf16 elements per stage
+constexpr int kMidLds = 2 * STM * 2;  // 98304
+
+template <bool kFwd>
+__global__ void __launch_bounds__(kThreads, 1)
+proj_mid_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __restrict__ W,
+                float* __restrict__ e32, uint16_t* __restrict__ e16) {
+    constexpr int LX = BMM / (kWaves * RPL);  // x loads per wave per stage
+    constexpr int LW = BN / (kWaves * RPL);   // W loads per wave per stage
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ff = wave & 3, tt = wave >> 2;  // 64-feature quarter, 64-token half
+    const int nb = gridDim.x, b = blockIdx.x;
+    const int per = nb / kXcds, rem = nb % kXcds, xcd = b % kXcds;
+    const int tile = xcd * per + (xcd < rem ? xcd : rem) + b / kXcds;
+    const int n0 = (tile % kNTiles) * BN;
+    const int64_t m0 = (int64_t)(tile / kNTiles) * BMM;
+
+    const uint16_t* gW[LW];
+    const uint16_t* gX[LX];
+#pragma unroll
+    for (int i = 0; i < LW; ++i) {
+        const int row = (wave * LW + i) * RPL + lane / CH;
+        gW[i] = W + (int64_t)(n0 + row) * kD + ((lane % CH) ^ swz(row)) * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < LX; ++i) {
+        const int row = (wave * LX + i) * RPL + lane / CH;
+        const int64_t tok = m0 + row;
+        // rows past the last token read token 0 (in bounds); their results are never stored
+        gX[i] = x + (tok < M ? tok : 0) * kD + ((lane % CH) ^ swz(row)) * 8;
+    }
+    auto issue = [&](int kt) {
+        uint16_t* sbase = lds + (kt & 1) * STM;
+        const int k0 = kt * BK;
+#pragma unroll
+        for (int i = 0; i < LW; ++i)
+            __builtin_amdgcn_global_load_lds((gbl_void*)(gW[i] + k0), (lds_void*)(sbase + (wave * LW + i) * RPL * BK),
+                                             16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < LX; ++i)
+            __builtin_amdgcn_global_load_lds((gbl_void*)(gX[i] + k0),
+                                             (lds_void*)(sbase + BN * BK + (wave * LX + i) * RPL * BK), 16, 0, 0);
+    };
+    const int fr = lane & 31, kh = lane >> 5, sw = swz(fr);
+    const int offA = (ff * 64 + fr) * BK, offB = BN * BK + (tt * 64 + fr) * BK;
+    bf16x8 fa[2][2], fb[2][2];
+    auto read = [&](int kt, int ks, int buf) {
+        const uint16_t* base = lds + (kt & 1) * STM;
+        const int c = ((ks * 2 + kh) ^ sw) * 8;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            fa[buf][i] = *reinterpret_cast<const bf16x8*>(base + offA + i * 32 * BK + c);
+            fb[buf][i] = *reinterpret_cast<const bf16x8*>(base + offB + i * 32 * BK + c);
+        }
+    };
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    auto mfma = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+    };
+    issue(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    issue(1);
+    read(0, 0, 0);
+    for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+        for (int ks = 0; ks < BK / 16 - 1; ++ks) {
+            read(kt, ks + 1, (ks + 1) & 1);
+            mfma(ks & 1);
+        }
+        // this wave's reads of stage kt are complete; after the barrier every
+        // wave's are, and stage kt+1 has landed
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        mfma(1);
+        if (kt + 1 < KT) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            __builtin_amdgcn_s_barrier();
+            if (kt + 2 < KT) issue(kt + 2);
+            read(kt + 1, 0, 0);
+        }
+    }
+    // lane holds token m0 + 64 tt + 32 j + fr and features n0 + 64 ff + 32 i + 8 g + 4 kh + 0..3
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int64_t tok = m0 + tt * 64 + 32 * j + fr;
+        if (tok >= M) continue;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int64_t off = tok * kD + n0 + ff * 64 + 32 * i + 8 * g + 4 * kh;
+                const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
+                const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+                if (!kFwd || e32) *reinterpret_cast<f32x4*>(e32 + off) = f32x4{v0, v1, v2, v3};
+                if (kFwd)
+                    __builtin_nontemporal_store(u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)},
+                                                reinterpret_cast<u32x2*>(e16 + off));
+            }
+    }
+}
+
 template <bool kFwd>
 hipError_t launch(const uint16_t* x, int64_t T, const uint16_t* W, float* e32, uint16_t* e16,
                   hipStream_t stream) {
-    // the 128 KB of dynamic LDS must be allowed once per device
+    // the dynamic LDS (128 KB, 96 KB) must be allowed once per device
     static std::atomic<uint64_t> allowed{0};
     int dev = 0;
     hipError_t err = hipGetDevice(&dev);
@@ -301,6 +420,9 @@ hipError_t launch(const uint16_t* x, int64_t T, const uint16_t* W, float* e32, u
     if (!(allowed.load(std::memory_order_acquire) & bit)) {
         err = hipFuncSetAttribute(reinterpret_cast<const void*>(&proj_kernel<kFwd>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+        if (err != hipSuccess) return err;
+        err = hipFuncSetAttribute(reinterpret_cast<const void*>(&proj_mid_kernel<kFwd>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, kMidLds);
         if (err != hipSuccess) return err;
         allowed.fetch_or(bit, std::memory_order_acq_rel);
     }
@@ -320,6 +442,11 @@ hipError_t launch(const uint16_t* x, int64_t T, const uint16_t* W, float* e32, u
         else
             hipLaunchKernelGGL((proj_small_kernel<kFwd, 32, 4>), dim3(kD / 32, (tiles + 3) / 4), dim3(512), 0, stream,
                                x, T, W, e32, e16);
+        return hipGetLastError();
+    }
+    if (T <= kMidT) {
+        hipLaunchKernelGGL(proj_mid_kernel<kFwd>, dim3((unsigned)(kNTiles * ((T + BMM - 1) / BMM))), dim3(kThreads),
+                           kMidLds, stream, x, T, W, e32, e16);
         return hipGetLastError();
     }
     dim3 grid((unsigned)(kNTiles * ((T + BM - 1) / BM)));

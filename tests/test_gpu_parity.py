@@ -227,13 +227,14 @@ def test_chunked_equals_unchunked_and_decode_equals_prefill(dev, small_table, de
 
 
 def test_kernel_variants_agree_bit_exactly(dev, small_table, dev_weights):
-    # a 1300-token call runs the tiled projection and the streaming fuse; its
-    # pieces (<= 256 and <= 1024 tokens) run the small-T projection, the
-    # in-gather IDs and the one-token fuse: every output and the carried state
-    # must match
+    # a 3100-token call runs the tiled projection, the ID kernel and the
+    # streaming fuse; its pieces run, by size, the mid-size projection (257-
+    # 1536 tokens), the small-T one (<= 256), IDs computed in the gather and
+    # the one-token fuse (<= 1024): every output and the carried state must
+    # match bit for bit
     tab, sc = small_table
     rng = np.random.default_rng(16)
-    n = 1300
+    n = 3100
     toks = inputs.uniform_tokens(rng, n)
     h = inputs.normal_bf16(rng, (n, D))
 
@@ -248,7 +249,8 @@ def test_kernel_variants_agree_bit_exactly(dev, small_table, dev_weights):
         return np.concatenate(outs), st.conv_state.cpu().numpy(), st.hist_ids.cpu().numpy()
 
     full = run([n])
-    for cuts in ([1024, 276], [200, 1100], [257, 255, 788], [3, 1297]):
+    for cuts in ([1024, 2076], [1500, 1600], [200, 1100, 1800], [3, 3097], [257, 1536, 1307]):
+        assert sum(cuts) == n
         got = run(cuts)
         for a, b in zip(got, full):
             assert np.array_equal(a, b), cuts
