@@ -65,7 +65,7 @@ extern "C" {
 typedef enum ple_status {
     PLE_OK = 0,
     PLE_ERR_NULL = -1,       /* a required pointer is NULL */
-    PLE_ERR_SHAPE = -2,      /* T < 0, S < 1, workspace sizes inconsistent */
+    PLE_ERR_SHAPE = -2,      /* T < 0 or (with cu_seqlens) T > 2^31-1, S < 1, sizes inconsistent */
     PLE_ERR_RANGE = -3,      /* R outside [1, 2^31-1], vocab outside [1, 2^20], eps < 0 */
     PLE_ERR_ALIGN = -4,      /* a pointer lacks the alignment stated below */
     PLE_ERR_ALIAS = -5,      /* an output overlaps another argument (out == h excepted) */

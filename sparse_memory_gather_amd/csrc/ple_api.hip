@@ -138,6 +138,7 @@ static int hash_impl(const int32_t* tokens, int64_t T, const int32_t* cu_seqlens
                      int32_t* row_ids, int32_t* dev_err, void* stream, bool heads) {
     const char* fn = heads ? "ple_hash_heads" : "ple_hash";
     if (T < 0) return fail(PLE_ERR_SHAPE, "T = %lld < 0", (long long)T);
+    if (T > 2147483647LL) return fail(PLE_ERR_SHAPE, "T = %lld > 2^31-1 (cu_seqlens are int32)", (long long)T);
     if (S < 1) return fail(PLE_ERR_SHAPE, "S = %d < 1", S);
     if (int st = check_R(R)) return st;
     if (vocab_size < 1 || vocab_size > PLE_MAX_VOCAB)
@@ -260,6 +261,7 @@ static int forward_impl(const ple_forward_args* a, void* stream, void* const* ev
     const int64_t T = a->T;
     const int32_t S = a->S;
     if (T < 0) return fail(PLE_ERR_SHAPE, "T = %lld < 0", (long long)T);
+    if (T > 2147483647LL) return fail(PLE_ERR_SHAPE, "T = %lld > 2^31-1 (cu_seqlens are int32)", (long long)T);
     if (S < 1) return fail(PLE_ERR_SHAPE, "S = %d < 1", S);
     if (!from_x) {
         if (int st = check_R(a->R)) return st;

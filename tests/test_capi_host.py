@@ -87,6 +87,7 @@ def _call(a):
 @pytest.mark.parametrize("over,status", [
     (dict(R=0), -3), (dict(R=2 ** 31), -3), (dict(vocab_size=0), -3),
     (dict(vocab_size=(1 << 20) + 1), -3), (dict(S=0), -2), (dict(T=-1), -2),
+    (dict(T=2 ** 31), -2),                            # beyond int32 cu_seqlens
     (dict(eps=-1.0), -3), (dict(eps=float("nan")), -3),
     (dict(tokens=None), -1), (dict(table=None), -1), (dict(conv_state=None), -1),
     (dict(workspace=None), -6), (dict(workspace_bytes=1000), -6),
@@ -117,6 +118,7 @@ def test_hash_lookup_proj_reject_bad_arguments():
     assert lib.ple_hash(FAKE, 10, FAKE + 0x100, 1, FAKE, FAKE, 100, 10, FAKE + 0x1004, None, None) == -4
     assert lib.ple_hash(FAKE, 10, FAKE + 0x100, 1, FAKE, FAKE, 100, 10, FAKE, None, None) == -5
     assert lib.ple_hash(FAKE, 0, None, 1, None, None, 100, 10, None, None, None) == 0
+    assert lib.ple_hash(FAKE, 2 ** 31, FAKE + 0x100, 1, FAKE, FAKE, 100, 10, FAKE + 0x1000, None, None) == -2
     assert lib.ple_lookup(FAKE, 4, FAKE + 0x10000, None, 10, FAKE + 0x100000, None, None, None) == -1
     assert lib.ple_lookup(FAKE, 4, FAKE + 0x10008, FAKE + 0x90000, 10, FAKE + 0x100000, None, None,
                           None) == -4
