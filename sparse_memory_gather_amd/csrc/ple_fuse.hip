@@ -22,11 +22,12 @@
 // fuse_token_kernel (short calls: decode steps, and calls of many short
 // sequences): one token per block, so the tokens of a call run side by side.
 // fuse_stream_kernel (long calls): one block per CU walks a contiguous range
-// of tokens, kStep at a time. The e and h rows of the next step are loaded
-// while the current step is computed, and the v of the last three tokens
-// stay in registers (a ring reset from the carried state at each sequence
-// start), so every row of e and h is read once; a block first runs the three
-// tokens before its range (without output) to fill the ring.
+// of tokens, kStep at a time, with one barrier per step (the gates of step i
+// are added up while step i-1 is convolved). The e and h rows of the next
+// step are loaded while the current ones are computed, and the v of the last
+// three tokens stay in registers (a ring reset from the carried state at
+// each sequence start), so every row of e and h is read once; a block first
+// runs the three tokens before its range (without output) to fill the ring.
 // Whichever block holds a sequence's last token writes the new conv state
 // and n-gram history; the old state is read from a copy taken before this
 // kernel, so the in-place update cannot race with readers.
@@ -40,8 +41,7 @@ constexpr int kThreads = kD / FPT;     // 640
 constexpr int kWaves = kThreads / 64;  // 10
 constexpr int kRows = kWaves * 4;      // rows of 16 lanes in a block
 constexpr int kSmallT = 1024;          // calls up to this many tokens run one token per block
-constexpr int kStep = 8;               // fuse_stream_kernel: tokens per step
-constexpr int kDepth = 1;              // fuse_stream_kernel: steps loaded ahead
+constexpr int kStep = 6;               // fuse_stream_kernel: tokens per step
 constexpr int kStreamBlocks = 256;     // fuse_stream_kernel: one block per CU
 constexpr int kMinRange = 32;          // fuse_stream_kernel: fewest tokens per block
 
@@ -251,28 +251,35 @@ __device__ __forceinline__ void load_step(const uint16_t* __restrict__ e16, cons
     }
 }
 
-template <int kN, int kAhead>
+// One block per CU walks tokens a .. b-1 (and up to three before a, without
+// output, to fill the ring) kN at a time, with one barrier per step: step
+// i's gate row sums go to LDS, then after the barrier one wave adds them up
+// while every wave convolves and writes step i-1, whose gates were formed
+// after the previous barrier. Three e/h register buffers rotate (step i+1
+// loading, step i gated, step i-1 convolved), the loop unrolled by three so
+// each is named statically. A step that neither starts nor ends a sequence
+// convolves from one statically indexed window with no per-token
+// bookkeeping; v of the last three tokens stays in registers, reset from the
+// carried state at a sequence start.
+template <int kN>
 __global__ void __launch_bounds__(kThreads)
 fuse_stream_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ e16, int64_t T,
-                   const int32_t* __restrict__ cu, int32_t S, const int32_t* __restrict__ tokens,
-                   const uint16_t* __restrict__ conv_w, const float* __restrict__ snap,
-                   float* __restrict__ conv_state, int32_t* __restrict__ hist_ids,
-                   int32_t* __restrict__ hist_len, uint16_t* out, float eps, float* __restrict__ gate_out,
-                   float* __restrict__ y_out, int64_t per_block, const uint16_t* __restrict__ halo) {
+                 const int32_t* __restrict__ cu, int32_t S, const int32_t* __restrict__ tokens,
+                 const uint16_t* __restrict__ conv_w, const float* __restrict__ snap,
+                 float* __restrict__ conv_state, int32_t* __restrict__ hist_ids,
+                 int32_t* __restrict__ hist_len, uint16_t* out, float eps, float* __restrict__ gate_out,
+                 float* __restrict__ y_out, int64_t per_block, const uint16_t* __restrict__ halo) {
     static_assert(kN >= 3, "the three tokens before a range must fit in the first step");
-    __shared__ float red_s[kN][kRows][3];
-    __shared__ float g_s[kN];
+    __shared__ float red_s[2][kN][kRows][3];
+    __shared__ float g_s[2][kN];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const uint32_t cb = (uint32_t)tid * FPT * 2;
-    const int64_t a = (int64_t)blockIdx.x * per_block;  // this block's tokens: a .. b-1
+    const int64_t a = (int64_t)blockIdx.x * per_block;
     if (a >= T) return;
     const int64_t b = a + per_block < T ? a + per_block : T;
-
-    // sequence of token a, and the first token to run: up to three before a
-    // in the same sequence, so that the ring holds v of a-3 .. a-1
     int s = seq_of(cu, S, a);
     int64_t st = cu[s], en = cu[s + 1];
-    if (st < 0 || st > a) st = a;  // malformed cu_seqlens (flagged by the ID kernel): stay in bounds
+    if (st < 0 || st > a) st = a;
     if (en <= a || en > T) en = a + 1;
     const int64_t a0 = a - 3 > st ? a - 3 : st;
 
@@ -290,35 +297,28 @@ fuse_stream_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
             }
         }
     }
-    // v of the three tokens before the current one (oldest first)
     float r0[FPT] = {}, r1[FPT] = {}, r2[FPT] = {};
 
-    // one step: tokens tb .. tb+kN-1 from (ce, ch), while the rows of the
-    // step kAhead later load into (ne, nh)
-    auto step = [&](int64_t tb, u32x2 (&ce)[kN], u32x2 (&ch)[kN], u32x2 (&ne)[kN], u32x2 (&nh)[kN]) {
-        load_step<kN>(e16, h, tb + kAhead * kN, b - 1, cb, ne, nh);  // past b: row b-1 again, unused
-#pragma unroll
-        for (int j = 0; j < kN; ++j) gate_rows(ce[j], ch[j], lane, wave, red_s[j]);
-        __syncthreads();
+    // gates of step tb from red_s[sel] (threads < kN)
+    auto reduce = [&](int64_t tb, int sel) {
         if (tid < kN) {
             float ee = 0.0f, he = 0.0f, hh = 0.0f;
 #pragma unroll 8
             for (int r = 0; r < kRows; ++r) {
-                ee += red_s[tid][r][0];
-                he += red_s[tid][r][1];
-                hh += red_s[tid][r][2];
+                ee += red_s[sel][tid][r][0];
+                he += red_s[sel][tid][r][1];
+                hh += red_s[sel][tid][r][2];
             }
             const float g = gate_of(ee, he, hh, eps);
-            g_s[tid] = g;
+            g_s[sel][tid] = g;
             const int64_t t = tb + tid;
             if (gate_out && t >= a && t < b) gate_out[t] = g;
         }
-        __syncthreads();
+    };
+    // conv, out and state of step tb with the gates in g_s[sel]
+    auto convolve = [&](int64_t tb, const u32x2 (&ce)[kN], const u32x2 (&ch)[kN], int sel) {
         char* ob = reinterpret_cast<char*>(out) + tb * (kD * 2);
         if (tb >= a && tb + kN <= b && st < tb && en > tb + kN && !y_out) {
-            // common case: every token of the step is in the range and in
-            // sequence s, none starts or ends it. v of the step and the three
-            // tokens before it in one statically indexed window
             float vw[kN + 3][FPT];
 #pragma unroll
             for (int q = 0; q < FPT; ++q) {
@@ -330,7 +330,7 @@ fuse_stream_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
             for (int j = 0; j < kN; ++j) {
                 float e[FPT];
                 unpack4(ce[j], e);
-                const float g = g_s[j];
+                const float g = g_s[sel][j];
 #pragma unroll
                 for (int q = 0; q < FPT; ++q) vw[j + 3][q] = g * e[q];
             }
@@ -355,17 +355,14 @@ fuse_stream_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
         for (int j = 0; j < kN; ++j) {
             const int64_t t = tb + j;
             if (t >= b) break;
-            // sequence bounds are the same in every lane
             while (t >= en && s + 1 < S) {
                 ++s;
                 st = en;
                 en = cu[s + 1];
             }
-            // malformed cu_seqlens (flagged by the ID kernel): stay in bounds
             if (st < 0 || st > t) st = t;
             if (en <= t || en > T) en = t + 1;
             if (t == st) {
-                // a sequence starts: its three earlier taps are the carried state
                 const float* sp = snap + (int64_t)s * 3 * kD + tid * FPT;
                 const f32x4 c0 = *reinterpret_cast<const f32x4*>(sp);
                 const f32x4 c1 = *reinterpret_cast<const f32x4*>(sp + kD);
@@ -379,7 +376,7 @@ fuse_stream_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
             }
             float e[FPT], v[FPT], y[FPT];
             unpack4(ce[j], e);
-            const float g = g_s[j];
+            const float g = g_s[sel][j];
 #pragma unroll
             for (int q = 0; q < FPT; ++q) {
                 v[q] = g * e[q];
@@ -388,14 +385,13 @@ fuse_stream_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
                 r1[q] = r2[q];
                 r2[q] = v[q];
             }
-            if (t < a) continue;  // a token before the range: ring only
+            if (t < a) continue;
             float hv[FPT];
             unpack4(ch[j], hv);
             const u32x2 o = {pack_bf16x2(hv[0] + y[0], hv[1] + y[1]), pack_bf16x2(hv[2] + y[2], hv[3] + y[3])};
             __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(ob + (cb + (uint32_t)(j * kD * 2))));
             if (y_out) *reinterpret_cast<f32x4*>(y_out + t * kD + tid * FPT) = f32x4{y[0], y[1], y[2], y[3]};
             if (t == en - 1) {
-                // last token of sequence s: new conv state = v at t-2, t-1, t
                 float* dp = conv_state + (int64_t)s * 3 * kD + tid * FPT;
                 *reinterpret_cast<f32x4*>(dp) = f32x4{r0[0], r0[1], r0[2], r0[3]};
                 *reinterpret_cast<f32x4*>(dp + kD) = f32x4{r1[0], r1[1], r1[2], r1[3]};
@@ -405,15 +401,9 @@ fuse_stream_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
         }
     };
 
-    // kAhead + 1 buffers in rotation, the loop unrolled so that each is named
-    // statically: step u computes from buffer u and loads into the one that
-    // step u-1 used
-    u32x2 be[kAhead + 1][kN], bh[kAhead + 1][kN];
-#pragma unroll
-    for (int d = 0; d < kAhead; ++d) load_step<kN>(e16, h, a0 + d * kN, b - 1, cb, be[d], bh[d]);
+    u32x2 be[3][kN], bh[3][kN];
+    load_step<kN>(e16, h, a0, b - 1, cb, be[0], bh[0]);
     if (halo) {
-        // out is h: the rows before a belong to the previous block, which
-        // overwrites them; take them from the copy made before this kernel
 #pragma unroll
         for (int j = 0; j < 3; ++j)
             if (a0 + j < a)
@@ -421,12 +411,28 @@ fuse_stream_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
                     reinterpret_cast<const char*>(halo) +
                     ((int64_t)blockIdx.x * 3 + 3 - (a - (a0 + j))) * (kD * 2) + cb);
     }
-    for (int64_t tb = a0; tb < b; tb += (kAhead + 1) * kN) {
+    // iteration i: load step i+1, gate step i, barrier, reduce step i and
+    // convolve step i-1; one extra iteration convolves the last step
+    const int64_t nsteps = (b - a0 + kN - 1) / kN;
+    auto iter = [&](int64_t i, u32x2 (&ce)[kN], u32x2 (&ch)[kN], u32x2 (&pe)[kN], u32x2 (&ph)[kN],
+                    u32x2 (&ne)[kN], u32x2 (&nh)[kN]) {
+        const int64_t tb = a0 + i * kN;
+        const int sel = (int)(i & 1);
+        load_step<kN>(e16, h, tb + kN, b - 1, cb, ne, nh);  // past b: row b-1 again, unused
+        if (i < nsteps) {
 #pragma unroll
-        for (int u = 0; u <= kAhead; ++u) {
-            if (tb + u * kN >= b) break;
-            step(tb + u * kN, be[u], bh[u], be[(u + kAhead) % (kAhead + 1)], bh[(u + kAhead) % (kAhead + 1)]);
+            for (int j = 0; j < kN; ++j) gate_rows(ce[j], ch[j], lane, wave, red_s[sel][j]);
         }
+        __syncthreads();
+        if (i < nsteps) reduce(tb, sel);
+        if (i >= 1) convolve(tb - kN, pe, ph, sel ^ 1);
+    };
+    for (int64_t i = 0; i <= nsteps; i += 3) {
+        iter(i, be[0], bh[0], be[2], bh[2], be[1], bh[1]);
+        if (i + 1 > nsteps) break;
+        iter(i + 1, be[1], bh[1], be[0], bh[0], be[2], bh[2]);
+        if (i + 2 > nsteps) break;
+        iter(i + 2, be[2], bh[2], be[1], bh[1], be[0], bh[0]);
     }
 }
 
@@ -473,7 +479,7 @@ hipError_t launch_fuse(const uint16_t* h, const uint16_t* e16, int64_t T, const 
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
-        hipLaunchKernelGGL((fuse_stream_kernel<kStep, kDepth>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, h, e16, T,
+        hipLaunchKernelGGL((fuse_stream_kernel<kStep>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, h, e16, T,
                            cu, S, tokens, conv_w, state_snap, conv_state, hist_ids, hist_len, out, eps,
                            gate_out, y_out, per_block, in_place ? h_copy : nullptr);
     }
