@@ -46,7 +46,9 @@
  *    outputs of the affected tokens are then unspecified but every access
  *    stays in bounds.
  *  - T = 0 is valid and enqueues nothing.
- *  - Thread-safe; the only global state is a thread-local error message.
+ *  - Thread-safe; the only global state is a thread-local error message and
+ *    a per-device flag recording that the projection kernels' LDS size has
+ *    been set (set once, under an atomic).
  */
 #ifndef PLE_H
 #define PLE_H
@@ -128,7 +130,9 @@ typedef struct ple_forward_args {
     const uint16_t* W;          /* bf16 [2560][2560], W[out][in], 16-byte aligned */
     const uint16_t* conv_w;     /* bf16 [2560][4], 16-byte aligned */
     const uint16_t* h;          /* bf16 [T][2560] hidden states in, 16-byte aligned */
-    uint16_t* out;              /* bf16 [T][2560] out; may equal h (in place), 16-byte aligned */
+    uint16_t* out;              /* bf16 [T][2560] out; may equal h (in place: the h rows other
+                                   blocks overwrite are first copied into the workspace),
+                                   16-byte aligned; any partial overlap is rejected */
     int32_t* hist_ids;          /* int32 [S][2] in/out */
     int32_t* hist_len;          /* int32 [S] in/out */
     float* conv_state;          /* float [S][3][2560] in/out, last three v, oldest first; 16-byte aligned */
@@ -152,7 +156,9 @@ int ple_forward(const ple_forward_args* args, void* stream);
 /* ple_forward with per-stage timing: the same launches on the same stream,
  * with events[0..4] (hipEvent_t, created by the caller) recorded before the
  * n-gram ID kernel and after the ID, gather/dequant, projection and
- * gate/conv/fuse kernels. events may not be NULL. */
+ * gate/conv/fuse kernels. Calls of up to 1024 tokens compute the IDs inside
+ * the gather, so events[0] and events[1] then bracket no kernel. events may
+ * not be NULL. */
 int ple_forward_profiled(const ple_forward_args* args, void* stream, void* const* events);
 
 /* Workspace bytes ple_forward (and ple_forward_x) needs for up to max_T
