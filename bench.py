@@ -190,8 +190,8 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        sys.exit("bench.py measures one GPU: this build runs the path on a single MI355X "
-                 "(multi-GPU sharding is design-only), so --gpus must be 1")
+        sys.exit("bench.py measures one GPU: the path runs on a single MI355X (how it would shard "
+                 "across GPUs is described, not implemented), so --gpus must be 1")
 
     import numpy as np
     import torch
