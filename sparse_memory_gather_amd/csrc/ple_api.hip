@@ -324,10 +324,9 @@ static int forward_impl(const ple_forward_args* a, void* stream, void* const* ev
     };
     hipError_t e = mark(0);
     if (int st = hip_status(e, "ple_forward: event record")) return st;
-    // short calls with the two-lookup FP8 table: the gather computes the IDs
-    // (one launch instead of two; the ID stage's event pair then brackets
-    // nothing)
-    const bool ids_in_gather = !from_x && !heads && !nv_blocks && T <= kIdsInGatherMaxT;
+    // short calls: the gather computes the IDs (one launch instead of two;
+    // the ID stage's event pair then brackets nothing)
+    const bool ids_in_gather = !from_x && T <= kIdsInGatherMaxT;
     if (from_x) {
         x = const_cast<uint16_t*>(x_in);  // read only from here on
         e = launch_state_copy(a->conv_state, snap, S, s);
@@ -341,7 +340,8 @@ static int forward_impl(const ple_forward_args* a, void* stream, void* const* ev
     if (ids_in_gather) {
         const IdSource src{a->tokens, a->cu_seqlens, S, a->hist_ids, a->hist_len, a->vocab_size,
                            a->row_ids_out, a->conv_state, snap, (int64_t)S * 3 * kD / 4};
-        e = launch_gather_ids(src, T, a->table, a->scales, a->R, x, a->dev_err, s);
+        e = launch_gather_ids(src, heads ? kLayoutHeads : nv_blocks ? kLayoutNvfp4 : kLayoutFp8, T, a->table,
+                              nv_blocks, a->scales, a->R, x, a->dev_err, s);
         if (int st = hip_status(e, "ple_forward: gather launch")) return st;
     } else if (!from_x) {
         e = nv_blocks ? launch_gather_nvfp4(row_ids, T, a->table, nv_blocks, a->scales, a->R, x, nullptr,

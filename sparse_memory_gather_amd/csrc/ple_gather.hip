@@ -37,10 +37,43 @@ __device__ __forceinline__ void decode8(const u32x2& q, float s, float out[8]) {
     }
 }
 
-// kIds: the wave computes its token's two row IDs itself (short calls: one
-// launch instead of the ID kernel and this one). The launch then also
-// checks cu_seqlens (block 0) and copies the carried conv state (grid row 1),
-// as the ID kernel would.
+// kIds (all three gathers): each wave computes its token's row IDs itself
+// (short calls: one launch instead of the ID kernel and the gather). The
+// launch then also checks cu_seqlens (block 0) and copies the carried conv
+// state (grid row 1), as the ID kernel would. False for the copy blocks.
+template <bool kIds>
+__device__ __forceinline__ bool ids_prologue(const IdSource& src, int64_t T, int32_t* dev_err) {
+    if (!kIds) return true;
+    if (blockIdx.y == 1) {
+        const f32x4* from = reinterpret_cast<const f32x4*>(src.conv_state);
+        f32x4* to = reinterpret_cast<f32x4*>(src.snap);
+        for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < src.snap_vec4;
+             i += (int64_t)gridDim.x * blockDim.x)
+            to[i] = from[i];
+        return false;
+    }
+    if (blockIdx.x == 0) check_cu(src.cu, src.S, T, dev_err);
+    return true;
+}
+
+// the token's two rows (wave-uniform): computed (kIds) or read from row_ids
+template <bool kIds>
+__device__ __forceinline__ void pair_rows(int64_t t, const int32_t* row_ids, const IdSource& src,
+                                          int32_t* dev_err, int lane, int& r0, int& r1) {
+    if (kIds) {
+        const NgramKeys k = ngram_keys(t, src.tokens, src.cu, src.S, src.hist_ids, src.hist_len, src.vocab,
+                                       dev_err);
+        const ModR mr{src.mod_R, src.mod_m};
+        r0 = __builtin_amdgcn_readfirstlane(bigram_row(k, mr));
+        r1 = __builtin_amdgcn_readfirstlane(trigram_row(k, mr));
+        if (src.row_ids_out && lane == 0) reinterpret_cast<int2*>(src.row_ids_out)[t] = make_int2(r0, r1);
+    } else {
+        const int2 ids = reinterpret_cast<const int2*>(row_ids)[t];
+        r0 = __builtin_amdgcn_readfirstlane(ids.x);
+        r1 = __builtin_amdgcn_readfirstlane(ids.y);
+    }
+}
+
 template <bool kIds>
 __global__ void __launch_bounds__(64 * kTokPerBlock)
 gather_kernel(const int32_t* __restrict__ row_ids, int64_t T, const uint8_t* __restrict__ table,
@@ -48,30 +81,11 @@ gather_kernel(const int32_t* __restrict__ row_ids, int64_t T, const uint8_t* __r
               uint8_t* __restrict__ raw, int32_t* dev_err, IdSource src) {
 #pragma clang fp contract(off)
     const int lane = threadIdx.x & 63;
-    if (kIds && blockIdx.y == 1) {
-        const f32x4* from = reinterpret_cast<const f32x4*>(src.conv_state);
-        f32x4* to = reinterpret_cast<f32x4*>(src.snap);
-        for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < src.snap_vec4;
-             i += (int64_t)gridDim.x * blockDim.x)
-            to[i] = from[i];
-        return;
-    }
-    if (kIds && blockIdx.x == 0) check_cu(src.cu, src.S, T, dev_err);
+    if (!ids_prologue<kIds>(src, T, dev_err)) return;
     const int64_t t = (int64_t)blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
     if (t >= T) return;
     int r0, r1;
-    if (kIds) {
-        const NgramKeys k = ngram_keys(t, src.tokens, src.cu, src.S, src.hist_ids, src.hist_len, src.vocab,
-                                       dev_err);
-        const ModR mr{src.mod_R, src.mod_m};
-        r0 = __builtin_amdgcn_readfirstlane(k.j >= 1 ? (int32_t)mod_r(splitmix_finalize(k.k2), mr) : -1);
-        r1 = __builtin_amdgcn_readfirstlane(k.j >= 2 ? (int32_t)mod_r(splitmix_finalize(k.k3), mr) : -1);
-        if (src.row_ids_out && lane == 0) reinterpret_cast<int2*>(src.row_ids_out)[t] = make_int2(r0, r1);
-    } else {
-        const int2 ids = reinterpret_cast<const int2*>(row_ids)[t];
-        r0 = __builtin_amdgcn_readfirstlane(ids.x);
-        r1 = __builtin_amdgcn_readfirstlane(ids.y);
-    }
+    pair_rows<kIds>(t, row_ids, src, dev_err, lane, r0, r1);
     if (r0 < -1 || (int64_t)r0 >= R) {
         if (lane == 0) flag_error(dev_err, 8);
         r0 = -1;
@@ -126,12 +140,14 @@ gather_kernel(const int32_t* __restrict__ row_ids, int64_t T, const uint8_t* __r
 // IDs and scales and the others take theirs with a lane shuffle.
 constexpr int kHeadTokPerWave = 1;
 
+template <bool kIds>
 __global__ void __launch_bounds__(64 * kTokPerBlock)
 gather_heads_kernel(const int32_t* __restrict__ row_ids, int64_t T, const uint8_t* __restrict__ table,
                     const float* __restrict__ scales, int64_t R, uint16_t* __restrict__ x,
-                    uint8_t* __restrict__ raw, int32_t* dev_err) {
+                    uint8_t* __restrict__ raw, int32_t* dev_err, IdSource src) {
 #pragma clang fp contract(off)
     const int lane = threadIdx.x & 63;
+    if (!ids_prologue<kIds>(src, T, dev_err)) return;
     const int64_t t0 = ((int64_t)blockIdx.x * kTokPerBlock + (threadIdx.x >> 6)) * kHeadTokPerWave;
     if (t0 >= T) return;
     u32x2 a[kHeadTokPerWave][kSpans];
@@ -149,7 +165,16 @@ gather_heads_kernel(const int32_t* __restrict__ row_ids, int64_t T, const uint8_
         const int64_t t = t0 + k;
         int my_id = -1;
         float my_scale = 0.0f;
-        if (lane < 16 && t < T) {
+        if (kIds && t < T) {
+            // lane h < 16 computes head h's row (the keys are wave-uniform)
+            const NgramKeys kk = ngram_keys(t, src.tokens, src.cu, src.S, src.hist_ids, src.hist_len, src.vocab,
+                                            dev_err);
+            if (lane < 16) {
+                my_id = head_row(kk, lane, ModR{src.mod_R, src.mod_m});
+                if (src.row_ids_out) src.row_ids_out[t * 16 + lane] = my_id;
+                if (my_id >= 0) my_scale = scales[(int64_t)lane * R + my_id];
+            }
+        } else if (lane < 16 && t < T) {
             int r = row_ids[t * 16 + lane];
             if (r < -1 || (int64_t)r >= R) {
                 flag_error(dev_err, 8);
@@ -213,17 +238,18 @@ __device__ __forceinline__ void decode_nvfp4(uint32_t w, float block, float s, f
     }
 }
 
+template <bool kIds>
 __global__ void __launch_bounds__(64 * kTokPerBlock)
 gather_nvfp4_kernel(const int32_t* __restrict__ row_ids, int64_t T, const uint8_t* __restrict__ codes,
                     const uint8_t* __restrict__ blocks, const float* __restrict__ scales, int64_t R,
-                    uint16_t* __restrict__ x, uint8_t* __restrict__ raw, int32_t* dev_err) {
+                    uint16_t* __restrict__ x, uint8_t* __restrict__ raw, int32_t* dev_err, IdSource src) {
 #pragma clang fp contract(off)
     const int lane = threadIdx.x & 63;
+    if (!ids_prologue<kIds>(src, T, dev_err)) return;
     const int64_t t = (int64_t)blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
     if (t >= T) return;
-    int2 ids = reinterpret_cast<const int2*>(row_ids)[t];
-    int r0 = __builtin_amdgcn_readfirstlane(ids.x);
-    int r1 = __builtin_amdgcn_readfirstlane(ids.y);
+    int r0, r1;
+    pair_rows<kIds>(t, row_ids, src, dev_err, lane, r0, r1);
     if (r0 < -1 || (int64_t)r0 >= R) {
         if (lane == 0) flag_error(dev_err, 8);
         r0 = -1;
@@ -279,8 +305,8 @@ hipError_t launch_gather_nvfp4(const int32_t* row_ids, int64_t T, const uint8_t*
                                const float* scales, int64_t R, uint16_t* x, uint8_t* raw, int32_t* dev_err,
                                hipStream_t stream) {
     int64_t blocks_n = (T + kTokPerBlock - 1) / kTokPerBlock;
-    hipLaunchKernelGGL(gather_nvfp4_kernel, dim3((unsigned)blocks_n), dim3(64 * kTokPerBlock), 0, stream, row_ids,
-                       T, codes, blocks, scales, R, x, raw, dev_err);
+    hipLaunchKernelGGL(gather_nvfp4_kernel<false>, dim3((unsigned)blocks_n), dim3(64 * kTokPerBlock), 0, stream,
+                       row_ids, T, codes, blocks, scales, R, x, raw, dev_err, IdSource{});
     return hipGetLastError();
 }
 
@@ -289,8 +315,8 @@ hipError_t launch_gather_heads(const int32_t* row_ids, int64_t T, const uint8_t*
                                int32_t* dev_err, hipStream_t stream) {
     const int64_t per_block = (int64_t)kTokPerBlock * kHeadTokPerWave;
     int64_t blocks = (T + per_block - 1) / per_block;
-    hipLaunchKernelGGL(gather_heads_kernel, dim3((unsigned)blocks), dim3(64 * kTokPerBlock), 0, stream,
-                       row_ids, T, table, scales, R, x, raw, dev_err);
+    hipLaunchKernelGGL(gather_heads_kernel<false>, dim3((unsigned)blocks), dim3(64 * kTokPerBlock), 0, stream,
+                       row_ids, T, table, scales, R, x, raw, dev_err, IdSource{});
     return hipGetLastError();
 }
 
@@ -303,8 +329,9 @@ hipError_t launch_gather(const int32_t* row_ids, int64_t T, const uint8_t* table
     return hipGetLastError();
 }
 
-hipError_t launch_gather_ids(const IdSource& src, int64_t T, const uint8_t* table, const float* scales,
-                             int64_t R, uint16_t* x, int32_t* dev_err, hipStream_t stream) {
+hipError_t launch_gather_ids(const IdSource& src, int layout, int64_t T, const uint8_t* table,
+                             const uint8_t* nv_blocks, const float* scales, int64_t R, uint16_t* x,
+                             int32_t* dev_err, hipStream_t stream) {
     int64_t blocks = (T + kTokPerBlock - 1) / kTokPerBlock;
     const int64_t snap_blocks = (src.snap_vec4 + 64 * kTokPerBlock - 1) / (64 * kTokPerBlock);
     if (snap_blocks > blocks) blocks = snap_blocks < 65536 ? snap_blocks : 65536;
@@ -313,8 +340,16 @@ hipError_t launch_gather_ids(const IdSource& src, int64_t T, const uint8_t* tabl
     const ModR mr = make_mod((uint64_t)R);
     s.mod_R = mr.R;
     s.mod_m = mr.m;
-    hipLaunchKernelGGL(gather_kernel<true>, dim3((unsigned)blocks, src.snap ? 2 : 1), dim3(64 * kTokPerBlock), 0,
-                       stream, nullptr, T, table, scales, R, x, nullptr, dev_err, s);
+    const dim3 grid((unsigned)blocks, src.snap ? 2 : 1), block(64 * kTokPerBlock);
+    if (layout == kLayoutHeads)
+        hipLaunchKernelGGL(gather_heads_kernel<true>, grid, block, 0, stream, nullptr, T, table, scales, R, x,
+                           nullptr, dev_err, s);
+    else if (layout == kLayoutNvfp4)
+        hipLaunchKernelGGL(gather_nvfp4_kernel<true>, grid, block, 0, stream, nullptr, T, table, nv_blocks, scales,
+                           R, x, nullptr, dev_err, s);
+    else
+        hipLaunchKernelGGL(gather_kernel<true>, grid, block, 0, stream, nullptr, T, table, scales, R, x, nullptr,
+                           dev_err, s);
     return hipGetLastError();
 }
 

@@ -21,7 +21,6 @@ namespace ple {
 namespace {
 
 constexpr int kHashBlock = 256;
-constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ULL;
 
 // kHeads = 0: two IDs per token (bigram, trigram); 16: the 16-lookup layout
 template <int kHeads>
@@ -44,19 +43,12 @@ hash_kernel(const int32_t* __restrict__ tokens, int64_t T, const int32_t* __rest
     const int64_t t = (int64_t)blockIdx.x * kHashBlock + threadIdx.x;
     if (t >= T) return;
     const NgramKeys k = ngram_keys(t, tokens, cu, S, hist_ids, hist_len, vocab, dev_err);
-    const int64_t j = k.j;
-    const uint64_t k2 = k.k2, k3 = k.k3;
     if (kHeads == 0) {
-        const int32_t r2 = j >= 1 ? (int32_t)mod_r(splitmix_finalize(k2), mr) : -1;
-        const int32_t r3 = j >= 2 ? (int32_t)mod_r(splitmix_finalize(k3), mr) : -1;
-        reinterpret_cast<int2*>(row_ids)[t] = make_int2(r2, r3);
+        reinterpret_cast<int2*>(row_ids)[t] = make_int2(bigram_row(k, mr), trigram_row(k, mr));
     } else {
         int32_t id[16];
 #pragma unroll
-        for (int h = 0; h < 8; ++h) {
-            id[h] = j >= 1 ? (int32_t)mod_r(splitmix_finalize(k2 + (uint64_t)h * kGamma), mr) : -1;
-            id[8 + h] = j >= 2 ? (int32_t)mod_r(splitmix_finalize(k3 + (uint64_t)h * kGamma), mr) : -1;
-        }
+        for (int h = 0; h < 16; ++h) id[h] = head_row(k, h, mr);
         int4* dst = reinterpret_cast<int4*>(row_ids + t * 16);
 #pragma unroll
         for (int q = 0; q < 4; ++q) dst[q] = make_int4(id[4 * q], id[4 * q + 1], id[4 * q + 2], id[4 * q + 3]);

@@ -36,7 +36,7 @@ struct IdSource {
     const int32_t* hist_ids;
     const int32_t* hist_len;
     int32_t vocab;
-    int32_t* row_ids_out;     // int32 [T][2], or NULL
+    int32_t* row_ids_out;     // int32 [T][2] (16-lookup layout: [T][16]), or NULL
     const float* conv_state;  // copied to snap (snap_vec4 float4s) when snap is not NULL
     float* snap;
     int64_t snap_vec4;
@@ -68,10 +68,13 @@ hipError_t launch_gather_heads(const int32_t* row_ids, int64_t T, const uint8_t*
                                const float* scales, int64_t R, uint16_t* x, uint8_t* raw,
                                int32_t* dev_err, hipStream_t stream);
 
-// the two-lookup FP8 gather computing each token's IDs itself (the ID
-// kernel's work, cu_seqlens checks and state copy included)
-hipError_t launch_gather_ids(const IdSource& src, int64_t T, const uint8_t* table, const float* scales,
-                             int64_t R, uint16_t* x, int32_t* dev_err, hipStream_t stream);
+// a gather computing each token's row IDs itself (the ID kernel's work,
+// cu_seqlens checks and state copy included): the FP8 table (two lookups),
+// the 16-lookup layout, or the NVFP4 table (nv_blocks)
+constexpr int kLayoutFp8 = 0, kLayoutHeads = 1, kLayoutNvfp4 = 2;
+hipError_t launch_gather_ids(const IdSource& src, int layout, int64_t T, const uint8_t* table,
+                             const uint8_t* nv_blocks, const float* scales, int64_t R, uint16_t* x,
+                             int32_t* dev_err, hipStream_t stream);
 
 hipError_t launch_gather(const int32_t* row_ids, int64_t T, const uint8_t* table,
                          const float* scales, int64_t R, uint16_t* x, uint8_t* raw,

@@ -87,6 +87,25 @@ __device__ __forceinline__ NgramKeys ngram_keys(int64_t t, const int32_t* __rest
     return k;
 }
 
+// two-lookup rows: bigram and trigram, -1 where the sequence is too short
+__device__ __forceinline__ int32_t bigram_row(const NgramKeys& k, const ModR& mr) {
+    return k.j >= 1 ? (int32_t)mod_r(splitmix_finalize(k.k2), mr) : -1;
+}
+__device__ __forceinline__ int32_t trigram_row(const NgramKeys& k, const ModR& mr) {
+    return k.j >= 2 ? (int32_t)mod_r(splitmix_finalize(k.k3), mr) : -1;
+}
+
+// 16-lookup layout: heads 0..7 on the bigram key, 8..15 on the trigram key,
+// head h finalizing key + (h mod 8) * 0x9E3779B97F4A7C15 (the h-th SplitMix64
+// output from the key), so heads 0 and 8 equal the two-lookup rows
+constexpr uint64_t kHeadGamma = 0x9E3779B97F4A7C15ULL;
+
+__device__ __forceinline__ int32_t head_row(const NgramKeys& k, int h, const ModR& mr) {
+    const bool tri = h >= 8;
+    if (k.j < (tri ? 2 : 1)) return -1;
+    return (int32_t)mod_r(splitmix_finalize((tri ? k.k3 : k.k2) + (uint64_t)(h & 7) * kHeadGamma), mr);
+}
+
 // cu_seqlens checks (one block of a launch): cu[0] == 0, non-decreasing, cu[S] == T
 __device__ __forceinline__ void check_cu(const int32_t* cu, int32_t S, int64_t T, int32_t* dev_err) {
     for (int i = threadIdx.x; i <= S; i += blockDim.x) {

@@ -662,3 +662,36 @@ def test_nvfp4_forward_parity_with_edge_cases(dev, small_nvfp4, dev_weights, wei
     assert np.all(np.abs(got["e"].astype(np.float64) - ref["e"]) <= E_REL * eb + 1e-7)
     assert np.array_equal(st.hist_len.cpu().numpy(), ref["hist_len"])
     np.testing.assert_allclose(st.conv_state.cpu().numpy(), ref["conv_state"], rtol=2e-2, atol=1e-4)
+
+
+@pytest.mark.parametrize("layout", ["heads", "nvfp4"])
+def test_other_layouts_chunked_equals_unchunked(dev, small_table, small_head_scales, small_nvfp4, dev_weights,
+                                                layout):
+    # calls of up to 1024 tokens compute the row IDs inside the gather, longer
+    # ones run the ID kernel: the 16-lookup and NVFP4 paths must agree bit
+    # for bit across the switch, state included
+    rng = np.random.default_rng(40)
+    n = 1300
+    toks = inputs.uniform_tokens(rng, n)
+    h = inputs.normal_bf16(rng, (n, D))
+    if layout == "heads":
+        tab, sc, kw = small_table[0], small_head_scales, dict(heads=True)
+    else:
+        tab, sc, kw = small_nvfp4[0], small_nvfp4[2], dict(nvfp4_blocks=small_nvfp4[1])
+
+    def run(cuts):
+        st = ple.State(1, dev)
+        outs, ids, pos = [], [], 0
+        for L in cuts:
+            r = _forward(dev, tab, sc, dev_weights, toks[pos:pos + L], np.array([0, L], np.int32),
+                         h[pos:pos + L], st, **kw)
+            outs.append(host_bits(r["out"]))
+            ids.append(r["row_ids"].cpu().numpy())
+            pos += L
+        return np.concatenate(outs), np.concatenate(ids), st.conv_state.cpu().numpy(), st.hist_ids.cpu().numpy()
+
+    full = run([n])
+    for cuts in ([1024, 276], [300, 1000], [1, 2, 1297], [8] * 10 + [1220]):
+        got = run(cuts)
+        for a, b in zip(got, full):
+            assert np.array_equal(a, b), (layout, cuts)
