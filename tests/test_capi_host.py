@@ -145,3 +145,31 @@ def test_forward_x_and_heads_reject_bad_arguments():
     # x placed 320 bytes after the scales: outside 10 scales, inside 16 x 10
     assert lib.ple_lookup_heads(FAKE, 4, FAKE + 0x10000, FAKE + 0x90000, 10, FAKE + 0x90140, None, None,
                                 None) == -5
+
+
+def test_binding_refuses_cpu_tensors_and_bad_dtypes():
+    # the binding only marshals: CPU tensors are refused (there is no CPU
+    # fallback), as are wrong dtypes, shapes and non-contiguous tensors
+    toks = torch.zeros(4, dtype=torch.int32)
+    cu = torch.tensor([0, 4], dtype=torch.int32)
+    hist = torch.zeros((1, 2), dtype=torch.int32)
+    hl = torch.zeros(1, dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU"):
+        ple.ple_hash(toks, cu, hist, hl, 10)
+    with pytest.raises(ValueError, match="GPU"):
+        ple.ple_lookup(torch.zeros((4, 2), dtype=torch.int32), torch.zeros((10, 2560), dtype=torch.uint8),
+                       torch.zeros(10))
+    with pytest.raises(ValueError, match="GPU"):
+        ple.ple_proj(torch.zeros((4, 2560), dtype=torch.bfloat16), torch.zeros((2560, 2560), dtype=torch.bfloat16))
+    # the device is checked first, whatever else is wrong; non-tensors are refused
+    with pytest.raises(ValueError, match="GPU"):
+        ple._dev(torch.zeros(4, dtype=torch.int64), "tokens", torch.int32)
+    with pytest.raises(TypeError):
+        ple._dev([1, 2, 3], "tokens", torch.int32)
+
+
+def test_binding_raises_when_the_library_is_missing(tmp_path, monkeypatch):
+    # a missing libple.so is an error, never a silent fallback
+    monkeypatch.setattr(ple, "_lib", None)
+    with pytest.raises(ImportError, match="not built"):
+        ple.load_library(str(tmp_path / "libple.so"))
