@@ -493,6 +493,39 @@ def test_gather_dequant_nvfp4_matches_torch_fp32():
             assert np.array_equal(raw[t, k], codes[r] if r >= 0 else np.zeros(1280, np.uint8))
 
 
+def test_gather_dequant_nvfp4_close_to_exact_rational_sum():
+    # the E2M1 values are taken from the OCP table (not from the oracle's
+    # decoder) and the sum is formed exactly: each row's product is rounded to
+    # fp32 once (code x block is exact), their sum once more, then to bf16
+    rng = np.random.default_rng(71)
+    n = 6
+    codes = rng.integers(0, 256, (n, 1280), dtype=np.uint8)
+    blocks = rng.integers(0x20, 0x58, (n, 160), dtype=np.uint8)
+    blocks[:, ::5] |= 0x80
+    scales = rng.uniform(0.01, 0.1, n).astype(np.float32)
+    ids = np.array([[0, 1], [2, -1], [-1, 3], [4, 4], [5, 0], [-1, -1]], np.int32)
+    x = oracle.gather_dequant_nvfp4(ids, codes, blocks, scales)
+    e2m1 = {c: Fraction(v) for c, v in _e2m1_golden().items()}   # tests/golden/e2m1_ocp.txt
+    blk = torch.from_numpy(blocks).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for t in range(ids.shape[0]):
+        for c in range(0, D, 7):
+            terms = []
+            for r in ids[t]:
+                if r >= 0:
+                    nib = (int(codes[r, c // 2]) >> (4 * (c & 1))) & 15
+                    val = e2m1[nib]
+                    terms.append(val * Fraction(float(blk[r, c // 16])) * Fraction(float(scales[r])))
+            exact = sum(terms, Fraction(0))
+            got = Fraction(float(inputs.bf16_bits_to_f32(np.array([x[t, c]], np.uint16))[0]))
+            if not terms or all(v == 0 for v in terms):
+                assert got == 0
+                continue
+            mag = max(abs(exact), abs(got), Fraction(2) ** -126)
+            ulp = Fraction(2) ** (math.floor(math.log2(float(mag))) - 7)
+            fp32_err = sum(abs(v) for v in terms) / 2 ** 23 + abs(exact) / 2 ** 24
+            assert abs(got - exact) <= ulp / 2 + fp32_err, (t, c)
+
+
 def test_gather_dequant_nvfp4_element_and_block_placement():
     codes = np.zeros((1, 1280), np.uint8)
     blocks = np.zeros((1, 160), np.uint8)
