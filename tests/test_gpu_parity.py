@@ -695,3 +695,42 @@ def test_other_layouts_chunked_equals_unchunked(dev, small_table, small_head_sca
         got = run(cuts)
         for a, b in zip(got, full):
             assert np.array_equal(a, b), (layout, cuts)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_streaming_fuse_random_sequence_structures(dev, small_table, dev_weights, seed):
+    # random sequence structures (empty, short and long sequences, random
+    # history lengths and carried state) in one call of more than 1024 tokens
+    # (streaming fuse, block ranges crossing sequence starts and ends at
+    # random places) against each sequence alone (one-token fuse or, above
+    # 1024 tokens, the streaming fuse on its own ranges), bit for bit
+    tab, sc = small_table
+    rng = np.random.default_rng(1000 + seed)
+    S = int(rng.integers(2, 14))
+    lengths = []
+    for _ in range(S):
+        kind = rng.integers(0, 4)
+        lengths.append(0 if kind == 0 else int(rng.integers(1, 8)) if kind == 1 else int(rng.integers(30, 700)))
+    lengths[int(rng.integers(0, S))] += 1100 - sum(lengths) if sum(lengths) < 1100 else 0
+    hl = [int(v) for v in rng.integers(0, 3, S)]
+    toks, cu, hist, hlen, h = _case(2000 + seed, lengths, hl)
+    T = int(cu[-1])
+    assert T > 1024 and T >= 32 * S
+    state0 = (rng.standard_normal((S, 3, D)) * 0.5).astype(np.float32)
+
+    def fresh(lo, hi):
+        st = ple.State(hi - lo, dev)
+        st.hist_ids.copy_(dev_i32(hist[lo:hi], dev))
+        st.hist_len.copy_(dev_i32(hlen[lo:hi], dev))
+        st.conv_state.copy_(torch.from_numpy(state0[lo:hi]).to(dev))
+        return st
+
+    st = fresh(0, S)
+    whole = _forward(dev, tab, sc, dev_weights, toks, cu, h, st)
+    for i in range(S):
+        a, b = int(cu[i]), int(cu[i + 1])
+        si = fresh(i, i + 1)
+        one = _forward(dev, tab, sc, dev_weights, toks[a:b], np.array([0, b - a], np.int32), h[a:b], si)
+        assert np.array_equal(host_bits(one["out"]), host_bits(whole["out"][a:b])), (seed, i, lengths)
+        assert torch.equal(si.conv_state[0], st.conv_state[i]), (seed, i, lengths)
+        assert torch.equal(si.hist_ids[0], st.hist_ids[i]) and torch.equal(si.hist_len[0], st.hist_len[i])
