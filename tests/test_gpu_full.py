@@ -250,3 +250,40 @@ def test_max_size_single_call(dev, dev_weights, weights):
     print("max size", check_samples(gather_debug(res, idx), ref, W, "max size"))
     del res, h
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("layout", ["heads", "nvfp4"])
+def test_ragged_other_layouts(dev, full_table, dev_weights, weights, layout):
+    # the ragged workload (64 x 256 tokens, 20,000,096 rows) in the 16-lookup
+    # layout (the 51.2 GB table read as 16 head tables) and over the NVFP4
+    # table (28.9 GB): every row ID, and sampled tokens of five sequences
+    W, cw = weights
+    wl = inputs.make_workload("ragged")
+    toks, cu = wl.chunks[0]
+    h = wl.hidden(0)
+    R = wl.R
+    if layout == "heads":
+        tab, sc, kw = full_table[0], table.head_scales_gpu(R, device=dev), dict(heads=True)
+        ref_ids = oracle.ngram_ids_heads(toks, cu, np.zeros((wl.S, 2), np.int32), np.zeros(wl.S, np.int32), R)
+    else:
+        codes, blocks, sc = table.nvfp4_gpu(R, device=dev)
+        tab, kw = codes, dict(nvfp4_blocks=blocks)
+        ref_ids = oracle.ngram_ids(toks, cu, np.zeros((wl.S, 2), np.int32), np.zeros(wl.S, np.int32), R)
+    st = ple.State(wl.S, dev)
+    res = ple.ple_forward(dev_i32(toks, dev), dev_i32(cu, dev), tab, sc, dev_weights[0], dev_weights[1],
+                          dev_bf16(h, dev), st, debug=True, **kw)
+    assert np.array_equal(res["row_ids"].cpu().numpy(), ref_ids)
+    rng = np.random.default_rng(21)
+    seqs, samples, idx = [], [], []
+    for s in (0, 1, 31, 62, 63):
+        a, b = int(cu[s]), int(cu[s + 1])
+        seqs.append((toks[a:b], h[a:b]))
+        pos = sorted(set([0, 1, 2, 3, b - a - 1] + _interior(rng, 4, b - a - 1, 2)))
+        samples += [(len(seqs) - 1, p) for p in pos]
+        idx += [a + p for p in pos]
+    ref = oracle_samples(seqs, samples, W, cw, R, heads=layout == "heads", nvfp4=layout == "nvfp4")
+    print("ragged", layout, check_samples(gather_debug(res, idx), ref, W, f"ragged {layout}"))
+    del res
+    if layout == "nvfp4":
+        del codes, blocks
+    torch.cuda.empty_cache()
