@@ -339,6 +339,24 @@ def main():
     stage_med_us = 1e3 * np.median(per_launch, axis=0)
     tokens_per_call = tokens_per_step / n_calls
 
+    # the same kernels cold: before each step a 1 GiB buffer is read (a sum,
+    # so no dirty lines are left to write back), which evicts the L2s and the
+    # 256 MB Infinity Cache, so no table row can be served from a cache filled
+    # by the previous step
+    cold_us = None
+    if name in ("prefill", "ragged", "tiny"):
+        flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+        sink = torch.zeros(reps, dtype=torch.int64, device=dev)
+        ev_cold = [hev.create(5) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for k in range(reps):
+            torch.sum(flush, dim=0, dtype=torch.int64, out=sink[k])
+            step(k, events=ev_cold[k])
+        torch.cuda.synchronize()
+        cold_us = 1e3 * np.array([[hev.elapsed_ms(e[i], e[i + 1]) for i in range(4)] for e in ev_cold]).mean(axis=0)
+        assert int(sink.sum().item()) == reps * (1 << 28)
+        del flush, sink
+
     # valid lookups per call (for the gather's algorithmic bytes)
     rid = ple.ple_hash(batches[0][0], batches[0][1], torch.zeros((wl.S, 2), dtype=torch.int32, device=dev),
                        torch.full((wl.S,), 2 if name == "decode" else 0, dtype=torch.int32, device=dev), wl.R,
@@ -406,6 +424,11 @@ def main():
                    "bytes_per_launch": gather_bytes, "lookups_per_launch": lookups,
                    "unique_rows_per_launch": unique_rows,
                    "traffic": recorded_traffic(gather_name, name)},
+        "gather_cold": None if cold_us is None else {
+            "avg_us": round(float(cold_us[1]), 2), "achieved": round(gather_bytes / (cold_us[1] * 1e-6) / 1e9, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gather_bytes / (cold_us[1] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "stages_us": {k: round(float(v), 2) for k, v in zip(("hash", "gather", "proj", "fuse"), cold_us)}},
         "proj": {"bound": "mfma", "achieved": round(proj_tflops, 2), "peak": BF16_PEAK_TFLOPS,
                  "unit": "TFLOP/s", "frac": round(proj_tflops / BF16_PEAK_TFLOPS, 4)},
         "fuse": {"bound": "hbm", "achieved": round(fuse_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
