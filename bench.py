@@ -166,10 +166,41 @@ def cpu_baseline(wl, name, W, cw, h0, budget_s=12.0, layout="two"):
     tp = run(probe)
     n = int(min(T, max(probe, round(probe * budget_s / max(tp, 1e-6) / 64) * 64)))
     dt = run(n)
-    return {"value": round(n / dt, 2), "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"first {n} of {T} tokens of the {name} workload's first chunk, one call "
-                      f"({dt:.1f} s); table rows rebuilt on demand by the CPU generator"}
+    result = {"value": round(n / dt, 2), "unit": "tokens/s", "cores": oracle.num_threads(),
+              "kind": "oracle",
+              "sample": f"first {n} of {T} tokens of the {name} workload's first chunk, one call "
+                        f"({dt:.1f} s); table rows rebuilt on demand by the CPU generator"}
+    # the same oracle on one thread, a smaller sample (about a quarter of the budget)
+    threads = oracle.num_threads()
+    try:
+        oracle.set_num_threads(1)
+        n1 = int(min(T, max(probe, round(n / max(threads, 1) / 4 / 64) * 64)))
+        dt1 = run(n1)
+    finally:
+        oracle.set_num_threads(threads)
+    result["single_thread"] = {"value": round(n1 / dt1, 2), "unit": "tokens/s",
+                               "sample": f"first {n1} tokens, one call ({dt1:.1f} s)"}
+    result["host"] = host_description()
+    return result
+
+
+def host_description():
+    """CPU model, logical CPUs and memory of the machine the oracle ran on."""
+    model, mem_gb = None, None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemTotal"):
+                    mem_gb = round(int(line.split()[1]) / 2 ** 20, 1)
+                    break
+    except OSError:
+        pass
+    return {"cpu": model, "logical_cpus": os.cpu_count(), "mem_gib": mem_gb}
 
 
 def main():

@@ -56,6 +56,7 @@ def _load():
         lib = ctypes.CDLL(LIB)
         sig = {
             "oracle_num_threads": ([], ctypes.c_int),
+            "oracle_set_num_threads": ([ctypes.c_int], None),
             "oracle_mix64": ([ctypes.c_uint64], ctypes.c_uint64),
             "oracle_key2": ([ctypes.c_uint32, ctypes.c_uint32], ctypes.c_uint64),
             "oracle_key3": ([ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32], ctypes.c_uint64),
@@ -94,6 +95,11 @@ def _ptr(a):
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads for later calls; results do not depend on it."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def mix64(z: int) -> int:

@@ -50,6 +50,16 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Threads for later calls (each output element is still computed by one
+ * thread in one fixed order, so results do not depend on the count). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------ */
 /* n-gram IDs                                                                */
 /* ------------------------------------------------------------------------ */

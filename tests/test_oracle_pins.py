@@ -735,3 +735,22 @@ def test_sequences_in_one_call_are_independent(weights):
         alone = oracle.forward(toks[a:b], np.array([0, b - a], np.int32), h[a:b], W, cw, 65_536, _rows)
         assert np.array_equal(alone["out"], r["out"][a:b])
         assert np.array_equal(alone["row_ids"], r["row_ids"][a:b])
+
+
+def test_results_do_not_depend_on_the_thread_count(weights):
+    # the bench reports the oracle on all host cores and on one thread; each
+    # output element is computed by one thread in one fixed order
+    W, cw = weights
+    toks, h = _small_stream(40, seed=16)
+    cu = np.array([0, 7, 40], np.int32)
+    before = oracle.num_threads()
+    try:
+        oracle.set_num_threads(1)
+        assert oracle.num_threads() == 1
+        one = oracle.forward(toks, cu, h, W, cw, 65_536, _rows)
+        oracle.set_num_threads(4)
+        four = oracle.forward(toks, cu, h, W, cw, 65_536, _rows)
+    finally:
+        oracle.set_num_threads(before)
+    for k in ("row_ids", "x", "e", "g", "y", "out", "conv_state"):
+        assert np.array_equal(one[k], four[k]), k
