@@ -289,12 +289,17 @@ proj_small_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __r
     }
 }
 
-// Mid-size calls (257-1536 tokens): tiles of 128 tokens x 256 features so
+// Mid-size calls (257-3200 tokens): tiles of 128 tokens x 256 features so
 // that more blocks share the chip (the 256 x 256 tiles give such calls only
-// 20-60 blocks). Eight waves, each 64 features x 64 tokens (2 x 2 MFMA
-// tiles); both operands through LDS as in proj_kernel, 48 KB stages. The k
-// order of every output is proj_kernel's, so the bits are the same.
-constexpr int kMidT = 1536;           // largest call served by proj_mid_kernel
+// 20-130 blocks); up to 3200 tokens the grid (at most 250 blocks) is one
+// round on the 256 CUs. Eight waves, each 64 features x 64 tokens (2 x 2
+// MFMA tiles); both operands through LDS as in proj_kernel, 48 KB stages.
+// The bf16 tile is staged through LDS as 512-byte token rows (16-byte chunk
+// c of row r at chunk c ^ (r & 31)), so that each store instruction writes
+// two whole row segments; stores straight from the accumulators (16 bytes
+// per row per instruction) took up to 60% longer. The k order of every
+// output is proj_kernel's, so the bits are the same.
+constexpr int kMidT = 3200;           // largest call served by proj_mid_kernel
 constexpr int BMM = 128;              // tokens per block
 constexpr int STM = (BN + BMM) * BK;  // bf16 elements per stage
 constexpr int kMidLds = 2 * STM * 2;  // 98304
@@ -305,6 +310,7 @@ proj_mid_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __res
                 float* __restrict__ e32, uint16_t* __restrict__ e16) {
     constexpr int LX = BMM / (kWaves * RPL);  // x loads per wave per stage
     constexpr int LW = BN / (kWaves * RPL);   // W loads per wave per stage
+    static_assert(BMM * BN * 2 <= kMidLds && BMM == kWaves * 16, "bf16 tile staging");
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ff = wave & 3, tt = wave >> 2;  // 64-feature quarter, 64-token half
@@ -389,22 +395,47 @@ proj_mid_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __res
         }
     }
     // lane holds token m0 + 64 tt + 32 j + fr and features n0 + 64 ff + 32 i + 8 g + 4 kh + 0..3
+    if (!kFwd || e32) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int64_t tok = m0 + tt * 64 + 32 * j + fr;
-        if (tok >= M) continue;
+        for (int j = 0; j < 2; ++j) {
+            const int64_t tok = m0 + tt * 64 + 32 * j + fr;
+            if (tok >= M) continue;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int64_t off = tok * kD + n0 + ff * 64 + 32 * i + 8 * g + 4 * kh;
-                const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
-                const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
-                if (!kFwd || e32) *reinterpret_cast<f32x4*>(e32 + off) = f32x4{v0, v1, v2, v3};
-                if (kFwd)
-                    __builtin_nontemporal_store(u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)},
-                                                reinterpret_cast<u32x2*>(e16 + off));
-            }
+                for (int g = 0; g < 4; ++g) {
+                    const int64_t off = tok * kD + n0 + ff * 64 + 32 * i + 8 * g + 4 * kh;
+                    *reinterpret_cast<f32x4*>(e32 + off) =
+                        f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                }
+        }
+    }
+    if (kFwd) {
+        // every wave has finished reading the stages before they are reused
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int r = tt * 64 + 32 * j + fr;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int c = ff * 8 + 4 * i + g;
+                    *reinterpret_cast<u32x2*>(lds + r * 256 + (c ^ (r & 31)) * 8 + kh * 4) =
+                        u32x2{pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]),
+                              pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3])};
+                }
+        }
+        __syncthreads();
+        // wave w stores rows 16 w .. 16 w + 15, two 512-byte rows per instruction
+        const int c = lane & 31;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int r = wave * 16 + q * 2 + (lane >> 5);
+            const int64_t tok = m0 + r;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(lds + r * 256 + (c ^ (r & 31)) * 8);
+            if (tok < M) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(e16 + tok * kD + n0 + c * 8));
+        }
     }
 }
 

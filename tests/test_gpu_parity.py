@@ -218,7 +218,7 @@ def test_chunked_equals_unchunked_and_decode_equals_prefill(dev, small_table, de
     full = run([n])
     # pieces of up to 256 tokens run the small-T projection (16 feature rows
     # per block for 1-32 tokens, 32 rows and 1, 2 or 4 token tiles per block
-    # above), 257 and more the tiled one
+    # above), 257 and more the mid-size one
     for cuts in ([1, 2, 3, 264], [256, 14], [100, 0, 170], [1] * 20 + [250], [40, 64, 33, 32, 101],
                  [150, 120], [200, 70]):
         got = run(cuts)
@@ -227,14 +227,15 @@ def test_chunked_equals_unchunked_and_decode_equals_prefill(dev, small_table, de
 
 
 def test_kernel_variants_agree_bit_exactly(dev, small_table, dev_weights):
-    # a 3100-token call runs the tiled projection, the ID kernel and the
+    # a 4000-token call runs the tiled projection, the ID kernel and the
     # streaming fuse; its pieces run, by size, the mid-size projection (257-
-    # 1536 tokens), the small-T one (<= 256), IDs computed in the gather and
-    # the one-token fuse (<= 1024): every output and the carried state must
-    # match bit for bit
+    # 3200 tokens, both ends included), the tiled one again (3201 and more),
+    # the small-T one (<= 256), IDs computed in the gather and the one-token
+    # fuse (<= 1024): every output and the carried state must match bit for
+    # bit
     tab, sc = small_table
     rng = np.random.default_rng(16)
-    n = 3100
+    n = 4000
     toks = inputs.uniform_tokens(rng, n)
     h = inputs.normal_bf16(rng, (n, D))
 
@@ -249,7 +250,7 @@ def test_kernel_variants_agree_bit_exactly(dev, small_table, dev_weights):
         return np.concatenate(outs), st.conv_state.cpu().numpy(), st.hist_ids.cpu().numpy()
 
     full = run([n])
-    for cuts in ([1024, 2076], [1500, 1600], [200, 1100, 1800], [3, 3097], [257, 1536, 1307]):
+    for cuts in ([1024, 2976], [1500, 2500], [200, 1100, 2700], [3, 3997], [257, 3200, 543], [3201, 799]):
         assert sum(cuts) == n
         got = run(cuts)
         for a, b in zip(got, full):
