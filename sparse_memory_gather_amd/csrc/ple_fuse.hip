@@ -43,7 +43,7 @@ constexpr int kRows = kWaves * 4;      // rows of 16 lanes in a block
 constexpr int kSmallT = 1024;          // calls up to this many tokens run one token per block
 constexpr int kStep = 6;               // fuse_stream_kernel: tokens per step
 constexpr int kStreamBlocks = 256;     // fuse_stream_kernel: one block per CU
-constexpr int kMinRange = 32;          // fuse_stream_kernel: fewest tokens per block
+constexpr int kMinRange = 8;           // fuse_stream_kernel: fewest tokens per block
 
 __device__ __forceinline__ void unpack4(const u32x2& q, float v[4]) {
     v[0] = bf16_to_f32(q[0] & 0xFFFFu);

@@ -260,7 +260,7 @@ def test_kernel_variants_agree_bit_exactly(dev, small_table, dev_weights):
 def test_streaming_fuse_equals_per_sequence_calls(dev, small_table, dev_weights):
     # one 1380-token call of fourteen sequences (three empty, which must keep
     # their state) with carried state runs the streaming fuse (block ranges of
-    # ~32 tokens cross sequence starts and ends); each sequence alone (<= 1024
+    # 8 tokens cross sequence starts and ends); each sequence alone (<= 1024
     # tokens) runs the one-token fuse and the small-T projection: outputs,
     # gates and the new state must be equal
     tab, sc = small_table
