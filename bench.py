@@ -53,6 +53,8 @@ FUSE_BYTES_PER_TOKEN = 3 * 2 * D
 
 KERNEL_SOURCES = {
     "proj_kernel": ["sparse_memory_gather_amd/csrc/ple_proj.hip", "sparse_memory_gather_amd/csrc/ple_kernels.h"],
+    "proj_w320_kernel": ["sparse_memory_gather_amd/csrc/ple_proj.hip",
+                         "sparse_memory_gather_amd/csrc/ple_kernels.h"],
     "gather_kernel": ["sparse_memory_gather_amd/csrc/ple_gather.hip", "sparse_memory_gather_amd/csrc/ple_kernels.h"],
     "gather_heads_kernel": ["sparse_memory_gather_amd/csrc/ple_gather.hip",
                             "sparse_memory_gather_amd/csrc/ple_kernels.h"],
@@ -413,11 +415,12 @@ def main():
 
     gather_name = "gather_heads_kernel" if heads else "gather_nvfp4_kernel" if nvfp4 else "gather_kernel"
     dominant = int(np.argmax(stage_us))
+    proj_name = ple.proj_tiling(int(tokens_per_call))
     if dominant == 2:
-        roofline = {"kernel": "ple_proj (proj_kernel, forward variant)", "bound": "mfma",
+        roofline = {"kernel": f"ple_proj ({proj_name})", "bound": "mfma",
                     "achieved": round(proj_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(proj_tflops / BF16_PEAK_TFLOPS, 4),
-                    "traffic": recorded_traffic("proj_kernel", name),
+                    "traffic": recorded_traffic(proj_name, name),
                     "per_launch": {"flop": proj_flop, "avg_us": round(float(stage_us[2]), 2)}}
     elif dominant == 1:
         roofline = {"kernel": f"ple_gather_dequant ({gather_name})", "bound": "hbm",
@@ -460,8 +463,8 @@ def main():
             "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gather_bytes / (cold_us[1] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "stages_us": {k: round(float(v), 2) for k, v in zip(("hash", "gather", "proj", "fuse"), cold_us)}},
-        "proj": {"bound": "mfma", "achieved": round(proj_tflops, 2), "peak": BF16_PEAK_TFLOPS,
-                 "unit": "TFLOP/s", "frac": round(proj_tflops / BF16_PEAK_TFLOPS, 4)},
+        "proj": {"kernel": proj_name, "bound": "mfma", "achieved": round(proj_tflops, 2),
+                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(proj_tflops / BF16_PEAK_TFLOPS, 4)},
         "fuse": {"bound": "hbm", "achieved": round(fuse_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                  "frac": round(fuse_gbs / HBM_PEAK_GBS, 4)},
         "cpu_baseline": None,

@@ -254,6 +254,14 @@ int ple_forward_nvfp4(const ple_forward_args* args, const uint8_t* blocks, void*
 int ple_forward_nvfp4_profiled(const ple_forward_args* args, const uint8_t* blocks, void* stream,
                                void* const* events);
 
+/* Which projection tiling ple_forward (and its variants) runs for a T-token
+ * call: 0 none (T <= 0), 1 small-T (T <= 256: 16 or 32 features x 32-token
+ * tiles, the k chain split over eight waves), 2 mid-size (T <= 3200: 128
+ * tokens x 256 features), 3 256 x 256, 4 256 tokens x 320 features (chosen
+ * over 3 when it needs fewer rounds of 256 blocks). All give the same bits.
+ * Host-only, enqueues nothing; for labelling measurements. */
+int ple_proj_tiling(int64_t T);
+
 /* Static description of a status code. */
 const char* ple_status_string(int status);
 

@@ -64,7 +64,7 @@ EXPORTS = ("ple_hash", "ple_lookup", "ple_proj", "ple_forward", "ple_forward_pro
            "ple_forward_workspace_size", "ple_hash_heads", "ple_lookup_heads", "ple_forward_heads",
            "ple_forward_heads_profiled", "ple_forward_heads_workspace_size", "ple_forward_x",
            "ple_lookup_nvfp4", "ple_forward_nvfp4", "ple_forward_nvfp4_profiled",
-           "ple_status_string", "ple_last_error")
+           "ple_status_string", "ple_last_error", "ple_proj_tiling")
 HEADS = 16            # 16-lookup layout: head tables of 160-byte rows
 SLICE = D // HEADS
 
@@ -108,8 +108,18 @@ def load_library(path: str = LIB_PATH):
     lib.ple_status_string.restype = ctypes.c_char_p
     lib.ple_last_error.argtypes = []
     lib.ple_last_error.restype = ctypes.c_char_p
+    lib.ple_proj_tiling.argtypes = [I64]
+    lib.ple_proj_tiling.restype = ctypes.c_int
     _lib = lib
     return lib
+
+
+PROJ_TILINGS = {0: None, 1: "proj_small_kernel", 2: "proj_mid_kernel", 3: "proj_kernel", 4: "proj_w320_kernel"}
+
+
+def proj_tiling(T: int):
+    """Name of the projection kernel a T-token forward runs (None for T <= 0)."""
+    return PROJ_TILINGS[int(load_library().ple_proj_tiling(int(T)))]
 
 
 def _check(status: int):

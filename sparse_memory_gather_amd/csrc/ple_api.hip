@@ -121,6 +121,8 @@ const char* ple_status_string(int status) {
 
 const char* ple_last_error(void) { return g_last_error.c_str(); }
 
+int ple_proj_tiling(int64_t T) { return ple::proj_tiling(T); }
+
 size_t ple_forward_workspace_size(int64_t max_T, int32_t max_S) {
     if (max_T < 0 || max_S < 0) return 0;
     return layout(max_T, max_S, false).total;

@@ -85,6 +85,10 @@ hipError_t launch_gather(const int32_t* row_ids, int64_t T, const uint8_t* table
 hipError_t launch_proj(const uint16_t* x, int64_t T, const uint16_t* W, float* e32,
                        uint16_t* e16, hipStream_t stream);
 
+// The tiling launch_proj uses in forward mode for T tokens (values as
+// ple_proj_tiling in ple.h).
+int proj_tiling(int64_t T);
+
 // Gate (from h and the bf16 e), causal short conv with carried state,
 // residual add; updates conv_state and the n-gram history in place.
 hipError_t launch_fuse(const uint16_t* h, const uint16_t* e16, int64_t T, const int32_t* cu,

@@ -439,10 +439,169 @@ proj_mid_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __res
     }
 }
 
+// Tiles of 256 tokens x 320 features (8 per token tile instead of 10):
+// fewer, larger tiles, so that token counts whose 256 x 256 grid ends in a
+// partly filled round of 256 blocks fill whole rounds instead (8192 tokens:
+// 256 tiles, one round, against 320; 16384 tokens: 512 against 640), and
+// 12% fewer operand bytes per flop from L2. Eight waves of 160 features x 64
+// tokens (5 x 2 MFMA tiles), both operands through LDS in two 72 KB stages,
+// the main loop of proj_kernel with one more A fragment per k-step; the k
+// order of every output is proj_kernel's, so the bits are the same. The bf16
+// tile leaves in two passes of 128 tokens staged as 656-byte rows (320
+// features and 16 bytes of padding, so that the 32 rows an MFMA-layout store
+// touches spread over the LDS banks), stored as whole 640-byte segments.
+constexpr int BNW = 320;                   // features per block
+constexpr int kNTilesW = kD / BNW;         // feature tiles per token tile
+constexpr int NFW = BNW / 2 / 32;          // A tiles per wave
+constexpr int LWW = BNW / (kWaves * RPL);  // W loads per wave per stage
+constexpr int STW = (BNW + BM) * BK;       // bf16 elements per stage
+constexpr int kLdsW = 2 * STW * 2;         // 147456
+constexpr int kPadRow = BNW + 8;           // staging row in bf16 elements
+
+__global__ void __launch_bounds__(kThreads, 1)
+proj_w320_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __restrict__ W,
+                 float* __restrict__ e32, uint16_t* __restrict__ e16) {
+    static_assert(BNW % (kWaves * RPL) == 0 && 128 * kPadRow * 2 <= kLdsW, "tile shape");
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int fh = wave & 1, tq = wave >> 1;  // 160-feature half, 64-token quarter
+    const int nb = gridDim.x, b = blockIdx.x;
+    const int per = nb / kXcds, rem = nb % kXcds, xcd = b % kXcds;
+    const int tile = xcd * per + (xcd < rem ? xcd : rem) + b / kXcds;
+    const int n0 = (tile % kNTilesW) * BNW;
+    const int64_t m0 = (int64_t)(tile / kNTilesW) * BM;
+
+    const uint16_t* gW[LWW];
+    const uint16_t* gX[LPW];
+#pragma unroll
+    for (int i = 0; i < LWW; ++i) {
+        const int row = (wave * LWW + i) * RPL + lane / CH;
+        gW[i] = W + (int64_t)(n0 + row) * kD + ((lane % CH) ^ swz(row)) * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+        const int row = (wave * LPW + i) * RPL + lane / CH;
+        const int64_t tok = m0 + row;
+        // rows past the last token read token 0 (in bounds); their results are never stored
+        gX[i] = x + (tok < M ? tok : 0) * kD + ((lane % CH) ^ swz(row)) * 8;
+    }
+    auto issue = [&](int kt) {
+        uint16_t* sbase = lds + (kt & 1) * STW;
+        const int k0 = kt * BK;
+#pragma unroll
+        for (int i = 0; i < LWW; ++i)
+            __builtin_amdgcn_global_load_lds((gbl_void*)(gW[i] + k0), (lds_void*)(sbase + (wave * LWW + i) * RPL * BK),
+                                             16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < LPW; ++i)
+            __builtin_amdgcn_global_load_lds((gbl_void*)(gX[i] + k0),
+                                             (lds_void*)(sbase + BNW * BK + (wave * LPW + i) * RPL * BK), 16, 0, 0);
+    };
+    const int fr = lane & 31, kh = lane >> 5, sw = swz(fr);
+    const int offA = (fh * (BNW / 2) + fr) * BK, offB = BNW * BK + (tq * 64 + fr) * BK;
+    bf16x8 fa[2][NFW], fb[2][2];
+    auto read = [&](int kt, int ks, int buf) {
+        const uint16_t* base = lds + (kt & 1) * STW;
+        const int c = ((ks * 2 + kh) ^ sw) * 8;
+#pragma unroll
+        for (int i = 0; i < NFW; ++i) fa[buf][i] = *reinterpret_cast<const bf16x8*>(base + offA + i * 32 * BK + c);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) fb[buf][j] = *reinterpret_cast<const bf16x8*>(base + offB + j * 32 * BK + c);
+    };
+    f32x16 acc[NFW][2];
+#pragma unroll
+    for (int i = 0; i < NFW; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    constexpr int NQ = 2 * NFW;  // MFMAs per k-step
+    auto mfma = [&](int buf, int lo, int hi) {
+#pragma unroll
+        for (int q = lo; q < hi; ++q)
+            acc[q >> 1][q & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][q >> 1], fb[buf][q & 1],
+                                                                         acc[q >> 1][q & 1], 0, 0, 0);
+    };
+    issue(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    issue(1);
+    read(0, 0, 0);
+    for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+        for (int ks = 0; ks < BK / 16 - 1; ++ks) {
+            read(kt, ks + 1, (ks + 1) & 1);
+            mfma(ks & 1, 0, NQ);
+            // one fragment read between consecutive MFMAs
+#pragma unroll
+            for (int q = 0; q < NFW + 2; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, NQ - NFW - 2, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        mfma(1, 0, NQ / 2);
+        if (kt + 1 < KT) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            __builtin_amdgcn_s_barrier();
+            if (kt + 2 < KT) issue(kt + 2);
+            read(kt + 1, 0, 0);
+        }
+        mfma(1, NQ / 2, NQ);
+    }
+    // lane holds token m0 + 64 tq + 32 j + fr and features n0 + 160 fh + 32 i + 8 g + 4 kh + 0..3
+    if (e32) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int64_t tok = m0 + tq * 64 + 32 * j + fr;
+            if (tok >= M) continue;
+#pragma unroll
+            for (int i = 0; i < NFW; ++i)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    *reinterpret_cast<f32x4*>(e32 + tok * kD + n0 + fh * (BNW / 2) + 32 * i + 8 * g + 4 * kh) =
+                        f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        // the stages (pass 0) or the previous pass's staging are no longer read
+        __syncthreads();
+        const int pr = tq * 32 + fr;  // staged row: token m0 + 64 (pr / 32) + 32 j + pr % 32
+#pragma unroll
+        for (int i = 0; i < NFW; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<u32x2*>(lds + pr * kPadRow + fh * (BNW / 2) + 32 * i + 8 * g + 4 * kh) =
+                    u32x2{pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]),
+                          pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3])};
+        __syncthreads();
+        // 128 rows x 40 chunks of 16 bytes, chunk q = tid + 512 k
+#pragma unroll
+        for (int k = 0; k < 128 * (BNW / 8) / kThreads; ++k) {
+            const int q = tid + kThreads * k;
+            const int row = q / (BNW / 8), col = q % (BNW / 8);
+            const int64_t tok = m0 + (row >> 5) * 64 + j * 32 + (row & 31);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(lds + row * kPadRow + col * 8);
+            if (tok < M) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(e16 + tok * kD + n0 + col * 8));
+        }
+    }
+}
+
+// Whether the 256 x 320 tiling is expected to finish first: rounds of 256
+// blocks, its tiles weighted 1.2x (measured per full round) against the
+// 256 x 256 tiles'.
+__host__ inline bool use_w320(int64_t T) {
+    const int64_t tt = (T + BM - 1) / BM;
+    const int64_t r256 = (kNTiles * tt + 255) / 256, r320 = (kNTilesW * tt + 255) / 256;
+    return 6 * r320 <= 5 * r256;
+}
+
 template <bool kFwd>
 hipError_t launch(const uint16_t* x, int64_t T, const uint16_t* W, float* e32, uint16_t* e16,
                   hipStream_t stream) {
-    // the dynamic LDS (128 KB, 96 KB) must be allowed once per device
+    // the dynamic LDS (128 KB, 96 KB, 144 KB) must be allowed once per device
     static std::atomic<uint64_t> allowed{0};
     int dev = 0;
     hipError_t err = hipGetDevice(&dev);
@@ -455,6 +614,11 @@ hipError_t launch(const uint16_t* x, int64_t T, const uint16_t* W, float* e32, u
         err = hipFuncSetAttribute(reinterpret_cast<const void*>(&proj_mid_kernel<kFwd>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, kMidLds);
         if (err != hipSuccess) return err;
+        if (kFwd) {
+            err = hipFuncSetAttribute(reinterpret_cast<const void*>(&proj_w320_kernel),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, kLdsW);
+            if (err != hipSuccess) return err;
+        }
         allowed.fetch_or(bit, std::memory_order_acq_rel);
     }
     if (T <= kSmallT) {
@@ -480,12 +644,24 @@ hipError_t launch(const uint16_t* x, int64_t T, const uint16_t* W, float* e32, u
                            kMidLds, stream, x, T, W, e32, e16);
         return hipGetLastError();
     }
+    if (kFwd && use_w320(T)) {
+        hipLaunchKernelGGL(proj_w320_kernel, dim3((unsigned)(kNTilesW * ((T + BM - 1) / BM))), dim3(kThreads), kLdsW,
+                           stream, x, T, W, e32, e16);
+        return hipGetLastError();
+    }
     dim3 grid((unsigned)(kNTiles * ((T + BM - 1) / BM)));
     hipLaunchKernelGGL(proj_kernel<kFwd>, grid, dim3(kThreads), kLdsBytes, stream, x, T, W, e32, e16);
     return hipGetLastError();
 }
 
 }  // namespace
+
+int proj_tiling(int64_t T) {
+    if (T <= 0) return 0;
+    if (T <= kSmallT) return 1;
+    if (T <= kMidT) return 2;
+    return use_w320(T) ? 4 : 3;
+}
 
 hipError_t launch_proj(const uint16_t* x, int64_t T, const uint16_t* W, float* e32,
                        uint16_t* e16, hipStream_t stream) {

@@ -38,6 +38,17 @@ def test_header_declarations_are_exported():
         assert hasattr(lib, n)
 
 
+def test_projection_tiling_by_call_size():
+    # small-T up to 256 tokens, mid-size up to 3200, then whichever of the
+    # 256 x 256 and 256 x 320 tilings needs fewer (weighted) rounds of 256 blocks
+    expect = {0: None, 1: "proj_small_kernel", 256: "proj_small_kernel", 257: "proj_mid_kernel",
+              3200: "proj_mid_kernel", 3201: "proj_kernel", 6144: "proj_kernel", 8100: "proj_w320_kernel",
+              8192: "proj_w320_kernel", 12000: "proj_kernel", 16384: "proj_w320_kernel",
+              24576: "proj_w320_kernel", 32768: "proj_w320_kernel"}
+    for T, name in expect.items():
+        assert ple.proj_tiling(T) == name, T
+
+
 def test_forward_args_struct_matches_header_field_order():
     src = open(HEADER).read()
     body = src[src.index("typedef struct ple_forward_args"):src.index("} ple_forward_args;")]

@@ -257,6 +257,36 @@ def test_kernel_variants_agree_bit_exactly(dev, small_table, dev_weights):
             assert np.array_equal(a, b), cuts
 
 
+def test_projection_tilings_agree_bit_exactly(dev, small_table, dev_weights):
+    # an 8100-token call runs the 256 x 320 tiling (its last token tile has
+    # 164 tokens); its halves run the 256 x 256 one, a 3200-token piece the
+    # mid-size one and a 1-token piece the small-T one: outputs and the carried
+    # state must match bit for bit
+    tab, sc = small_table
+    rng = np.random.default_rng(17)
+    n = 8100
+    toks = inputs.uniform_tokens(rng, n)
+    h = inputs.normal_bf16(rng, (n, D))
+    assert ple.proj_tiling(n) == "proj_w320_kernel" and ple.proj_tiling(n // 2) == "proj_kernel"
+
+    def run(cuts):
+        st = ple.State(1, dev)
+        outs, pos = [], 0
+        for L in cuts:
+            r = _forward(dev, tab, sc, dev_weights, toks[pos:pos + L], np.array([0, L], np.int32),
+                         h[pos:pos + L], st)
+            outs.append(host_bits(r["out"]))
+            pos += L
+        return np.concatenate(outs), st.conv_state.cpu().numpy(), st.hist_ids.cpu().numpy()
+
+    full = run([n])
+    for cuts in ([4050, 4050], [3200, 4900], [8099, 1]):
+        assert sum(cuts) == n
+        got = run(cuts)
+        for a, b in zip(got, full):
+            assert np.array_equal(a, b), cuts
+
+
 def test_streaming_fuse_equals_per_sequence_calls(dev, small_table, dev_weights):
     # one 1380-token call of fourteen sequences (three empty, which must keep
     # their state) with carried state runs the streaming fuse (block ranges of
