@@ -229,11 +229,13 @@ proj_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __restric
 // sequence over k as in proj_kernel and every output element is
 // bit-identical to what proj_kernel produces. kRows < 32 leaves the MFMA's
 // other A rows zero (an output element depends only on its own row and
-// column), so that an 8-token step spreads its W loads over 160 CUs; kTiles >
-// 1 runs the tiles' chains one after the other with the same W fragments,
-// each wave loading its x fragments of the next tile right after its segment
-// of the current chain, so that calls of up to 256 tokens take one round of
-// blocks (one block per CU fits at this register use).
+// column), so that an 8-token step spreads its W loads over 160 CUs. With
+// kTiles > 1 the tiles' chains are pipelined through the waves with the same
+// W fragments: in step s wave w runs its segment of tile s - w, so the block
+// takes kW + kTiles - 1 steps instead of kW x kTiles, each wave loading its x
+// fragments of the next tile right after its segment of the current one;
+// calls of up to 256 tokens take one round of blocks (one block per CU fits
+// at this register use).
 template <bool kFwd, int kRows, int kTiles>
 __global__ void __launch_bounds__(512)
 proj_small_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __restrict__ W,
@@ -242,7 +244,7 @@ proj_small_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __r
     constexpr int KS = kD / 16;        // 160 k-steps
     constexpr int kW = 8;              // waves
     constexpr int SPW = KS / kW;       // k-steps per wave
-    __shared__ f32x16 acc_s[64];       // the accumulator between waves
+    __shared__ f32x16 acc_s[kTiles][64];  // each tile's accumulator between waves
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int fr = lane & 31, kh = lane >> 5;
     const int f0 = blockIdx.x * kRows;
@@ -260,22 +262,21 @@ proj_small_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __r
 #pragma unroll
     for (int q = 0; q < SPW; ++q) fa[q] = row ? *reinterpret_cast<const bf16x8*>(wrow + q * 16) : zero;
     load_x(0);
-#pragma unroll
-    for (int t = 0; t < kTiles; ++t) {
+    if constexpr (kTiles == 1) {
+        // one tile: the chain passes from wave to wave
         f32x16 acc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
         for (int w = 0; w < kW; ++w) {
             if (wave == w) {
-                if (w > 0) acc = acc_s[lane];
+                if (w > 0) acc = acc_s[0][lane];
 #pragma unroll
                 for (int q = 0; q < SPW; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[q], fb[q], acc, 0, 0, 0);
-                if (w + 1 < kW) acc_s[lane] = acc;
-                if (t + 1 < kTiles) load_x(t + 1);
+                if (w + 1 < kW) acc_s[0][lane] = acc;
             }
             __syncthreads();
         }
-        const int64_t tok = ((int64_t)blockIdx.y * kTiles + t) * 32 + fr;
+        const int64_t tok = (int64_t)blockIdx.y * 32 + fr;
         if (wave == kW - 1 && tok < M) {
             // lane holds token `tok` and features f0 + 8 g + 4 kh + 0..3
 #pragma unroll
@@ -286,6 +287,41 @@ proj_small_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __r
                 if (kFwd) *reinterpret_cast<u32x2*>(e16 + off) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
             }
         }
+        return;
+    }
+    // step s: wave w runs k-steps 20w .. 20w+19 of tile s - w; tile t's
+    // accumulator goes from wave w to wave w+1 through acc_s[t] between steps
+    for (int s = 0; s < kW + kTiles - 1; ++s) {
+        const int t = s - wave;
+        if (t >= 0 && t < kTiles) {
+            f32x16 acc;
+            if (wave == 0) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+            } else {
+                acc = acc_s[t][lane];
+            }
+#pragma unroll
+            for (int q = 0; q < SPW; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[q], fb[q], acc, 0, 0, 0);
+            if (wave + 1 < kW) {
+                acc_s[t][lane] = acc;
+            } else {
+                const int64_t tok = ((int64_t)blockIdx.y * kTiles + t) * 32 + fr;
+                if (tok < M) {
+                    // lane holds token `tok` and features f0 + 8 g + 4 kh + 0..3
+#pragma unroll
+                    for (int g = 0; g < kRows / 8; ++g) {
+                        const float v0 = acc[4 * g], v1 = acc[4 * g + 1], v2 = acc[4 * g + 2], v3 = acc[4 * g + 3];
+                        const int64_t off = tok * kD + f0 + g * 8 + kh * 4;
+                        if (!kFwd || e32) *reinterpret_cast<f32x4*>(e32 + off) = f32x4{v0, v1, v2, v3};
+                        if (kFwd)
+                            *reinterpret_cast<u32x2*>(e16 + off) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+                    }
+                }
+            }
+            if (t + 1 < kTiles) load_x(t + 1);
+        }
+        __syncthreads();
     }
 }
 
