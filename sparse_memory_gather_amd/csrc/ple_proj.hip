@@ -27,6 +27,12 @@
 // Forward mode writes e as bf16 (the projection's output tensor), staged
 // through LDS into 256-byte token rows; the fp32 accumulators can also be
 // written for checking.
+//
+// Four tilings by call size, all with the same MFMA sequence over k for
+// every output element, so a token's e does not depend on the call it is
+// in: a small-T kernel (up to 256 tokens), 128 x 256 tiles (up to 3200),
+// and for larger calls the 256 x 256 tiles above or 256 x 320 tiles,
+// whichever needs fewer rounds of blocks on the 256 CUs.
 #include <atomic>
 
 #include "ple_kernels.h"
