@@ -397,7 +397,7 @@ def test_prepared_forward_reuses_its_buffers(dev, small_table, dev_weights):
     assert torch.equal(st_a.conv_state, st_b.conv_state) and torch.equal(st_a.hist_ids, st_b.hist_ids)
 
 
-@pytest.mark.parametrize("T,S", [(8, 8), (1300, 2)])
+@pytest.mark.parametrize("T,S", [(8, 8), (1300, 2), (8192, 4)])
 def test_graph_captured_forward_replays_like_eager(dev, small_table, dev_weights, T, S):
     # a prepared call captured into a HIP graph (nothing in the path records a
     # memset) and replayed three times, with eager work and synchronizations
