@@ -765,3 +765,41 @@ def test_streaming_fuse_random_sequence_structures(dev, small_table, dev_weights
         assert np.array_equal(host_bits(one["out"]), host_bits(whole["out"][a:b])), (seed, i, lengths)
         assert torch.equal(si.conv_state[0], st.conv_state[i]), (seed, i, lengths)
         assert torch.equal(si.hist_ids[0], st.hist_ids[i]) and torch.equal(si.hist_len[0], st.hist_len[i])
+
+
+def test_streaming_fuse_many_short_sequences(dev, small_table, dev_weights):
+    # about 150 sequences of 0-8 tokens (and a few longer ones) in one call of
+    # more than 1024 tokens: the streaming fuse, whose 8-token block ranges
+    # hold several sequence starts and ends each, against each sequence alone
+    # (the one-token fuse), bit for bit, carried state included
+    tab, sc = small_table
+    rng = np.random.default_rng(3000)
+    lengths = []
+    while sum(lengths) < 1100:
+        kind = rng.integers(0, 10)
+        lengths.append(0 if kind == 0 else 1 if kind < 4 else int(rng.integers(2, 9)) if kind < 9
+                       else int(rng.integers(20, 61)))
+    S = len(lengths)
+    hl = [int(v) for v in rng.integers(0, 3, S)]
+    toks, cu, hist, hlen, h = _case(3001, lengths, hl)
+    T = int(cu[-1])
+    assert T > 1024 and T >= 2 * S and T < 8 * S
+    state0 = (rng.standard_normal((S, 3, D)) * 0.5).astype(np.float32)
+
+    def fresh(lo, hi):
+        st = ple.State(hi - lo, dev)
+        st.hist_ids.copy_(dev_i32(hist[lo:hi], dev))
+        st.hist_len.copy_(dev_i32(hlen[lo:hi], dev))
+        st.conv_state.copy_(torch.from_numpy(state0[lo:hi]).to(dev))
+        return st
+
+    st = fresh(0, S)
+    whole = _forward(dev, tab, sc, dev_weights, toks, cu, h, st)
+    whole_out = host_bits(whole["out"])
+    for i in range(S):
+        a, b = int(cu[i]), int(cu[i + 1])
+        si = fresh(i, i + 1)
+        one = _forward(dev, tab, sc, dev_weights, toks[a:b], np.array([0, b - a], np.int32), h[a:b], si)
+        assert np.array_equal(host_bits(one["out"]), whole_out[a:b]), (i, lengths[i])
+        assert torch.equal(si.conv_state[0], st.conv_state[i]), (i, lengths[i])
+        assert torch.equal(si.hist_ids[0], st.hist_ids[i]) and torch.equal(si.hist_len[0], st.hist_len[i])
