@@ -485,7 +485,7 @@ proj_mid_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __res
 // fewer, larger tiles, so that token counts whose 256 x 256 grid ends in a
 // partly filled round of 256 blocks fill whole rounds instead (8192 tokens:
 // 256 tiles, one round, against 320; 16384 tokens: 512 against 640), and
-// 12% fewer operand bytes per flop from L2. Eight waves of 160 features x 64
+// 10% fewer operand bytes per flop from L2. Eight waves of 160 features x 64
 // tokens (5 x 2 MFMA tiles), both operands through LDS in two 72 KB stages,
 // the main loop of proj_kernel with one more A fragment per k-step; the k
 // order of every output is proj_kernel's, so the bits are the same. The bf16
