@@ -157,7 +157,7 @@ static int hash_impl(const int32_t* tokens, int64_t T, const int32_t* cu_seqlens
                  rng("row_ids", row_ids, ids, true), rng("dev_err", dev_err, 4, true)};
     if (int st = check_alias(r, 6)) return st;
     hipError_t e = launch_hash(tokens, T, cu_seqlens, S, hist_ids, hist_len, vocab_size, R, row_ids,
-                               dev_err, nullptr, nullptr, heads, reinterpret_cast<hipStream_t>(stream));
+                               dev_err, nullptr, nullptr, 1, heads, reinterpret_cast<hipStream_t>(stream));
     if (int st = hip_status(e, heads ? "ple_hash_heads launch" : "ple_hash launch")) return st;
     return ok();
 }
@@ -329,19 +329,21 @@ static int forward_impl(const ple_forward_args* a, void* stream, void* const* ev
     // short calls: the gather computes the IDs (one launch instead of two;
     // the ID stage's event pair then brackets nothing)
     const bool ids_in_gather = !from_x && T <= kIdsInGatherMaxT;
+    // the fuse's block size decides which sequences' carried state is copied
+    const int64_t pb = fuse_block_tokens(T, S);
     if (from_x) {
         x = const_cast<uint16_t*>(x_in);  // read only from here on
-        e = launch_state_copy(a->conv_state, snap, S, s);
+        e = launch_state_copy(a->conv_state, snap, a->cu_seqlens, S, pb, s);
         if (int st = hip_status(e, "ple_forward_x: state copy launch")) return st;
     } else if (!ids_in_gather) {
         e = launch_hash(a->tokens, T, a->cu_seqlens, S, a->hist_ids, a->hist_len, a->vocab_size,
-                        a->R, row_ids, a->dev_err, a->conv_state, snap, heads, s);
+                        a->R, row_ids, a->dev_err, a->conv_state, snap, pb, heads, s);
         if (int st = hip_status(e, "ple_forward: hash launch")) return st;
     }
     if (int st = hip_status(mark(1), "ple_forward: event record")) return st;
     if (ids_in_gather) {
         const IdSource src{a->tokens, a->cu_seqlens, S, a->hist_ids, a->hist_len, a->vocab_size,
-                           a->row_ids_out, a->conv_state, snap, (int64_t)S * 3 * kD / 4};
+                           a->row_ids_out, a->conv_state, snap, pb};
         e = launch_gather_ids(src, heads ? kLayoutHeads : nv_blocks ? kLayoutNvfp4 : kLayoutFp8, T, a->table,
                               nv_blocks, a->scales, a->R, x, a->dev_err, s);
         if (int st = hip_status(e, "ple_forward: gather launch")) return st;

@@ -153,10 +153,13 @@ fuse_token_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ e
     if (en <= t || en > T) en = t + 1;
     // window slot k is token t-3+k; slots below `first` lie before the start
     const int first = st > t - 3 ? (int)(st - (t - 3)) : 0;
+    // one token per block: a one-token sequence reads and rewrites its own
+    // state in this block, so it was not copied
+    const float* sbase = state_needs_copy(st, en, 1) ? snap : conv_state;
     f32x4 c[3];
 #pragma unroll
     for (int k = 0; k < 3; ++k)
-        c[k] = k < first ? *reinterpret_cast<const f32x4*>(snap + ((int64_t)s * 3 + 3 - (first - k)) * kD + tid * FPT)
+        c[k] = k < first ? *reinterpret_cast<const f32x4*>(sbase + ((int64_t)s * 3 + 3 - (first - k)) * kD + tid * FPT)
                          : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     const uint16_t* hwin = hw ? hw : h;
     u32x2 ep[4], hp[4];
@@ -364,7 +367,9 @@ fuse_stream_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
             if (st < 0 || st > t) st = t;
             if (en <= t || en > T) en = t + 1;
             if (t == st) {
-                const float* sp = snap + (int64_t)s * 3 * kD + tid * FPT;
+                // the copy, unless this sequence starts and ends in this block
+                const float* sp = (state_needs_copy(st, en, per_block) ? snap : conv_state) +
+                                  (int64_t)s * 3 * kD + tid * FPT;
                 const f32x4 c0 = *reinterpret_cast<const f32x4*>(sp);
                 const f32x4 c1 = *reinterpret_cast<const f32x4*>(sp + kD);
                 const f32x4 c2 = *reinterpret_cast<const f32x4*>(sp + 2 * kD);
@@ -453,18 +458,26 @@ halo_copy_kernel(const uint16_t* __restrict__ h, int64_t per_block, uint16_t* __
 
 }  // namespace
 
+int64_t fuse_block_tokens(int64_t T, int32_t S) {
+    // short calls, or calls of mostly one-token sequences (every token would
+    // start a sequence and stall a streaming block on its carried state): one
+    // token per block. From two tokens per sequence on average the streaming
+    // kernel is faster (16384 tokens in 4096 sequences: 117 against 199 us)
+    if (T <= kSmallT || T < (int64_t)kMinAvgSeq * S) return 1;
+    int64_t blocks = (T + kMinRange - 1) / kMinRange;
+    if (blocks > kStreamBlocks) blocks = kStreamBlocks;
+    return (T + blocks - 1) / blocks;
+}
+
 hipError_t launch_fuse(const uint16_t* h, const uint16_t* e16, int64_t T, const int32_t* cu,
                        int32_t S, const int32_t* tokens, const uint16_t* conv_w,
                        const float* state_snap, float* conv_state, int32_t* hist_ids,
                        int32_t* hist_len, uint16_t* out, float eps, float* gate_out, float* y_out,
                        uint16_t* h_copy, hipStream_t stream) {
     const bool in_place = out == h;
+    const int64_t per_block = fuse_block_tokens(T, S);
     if (T <= kSmallT || T < (int64_t)kMinAvgSeq * S) {
-        // short calls, or calls of mostly one-token sequences (every token
-        // would start a sequence and stall a streaming block on its carried
-        // state): one token per block. From two tokens per sequence on
-        // average the streaming kernel is faster (16384 tokens in 4096
-        // sequences: 117 against 199 us)
+        // one token per block (per_block == 1)
         if (in_place) {
             hipError_t e = hipMemcpyAsync(h_copy, h, (size_t)T * kD * 2, hipMemcpyDeviceToDevice, stream);
             if (e != hipSuccess) return e;
@@ -473,10 +486,7 @@ hipError_t launch_fuse(const uint16_t* h, const uint16_t* e16, int64_t T, const 
                            S, tokens, conv_w, state_snap, conv_state, hist_ids, hist_len, out, eps,
                            gate_out, y_out, in_place ? h_copy : nullptr);
     } else {
-        int64_t blocks = (T + kMinRange - 1) / kMinRange;
-        if (blocks > kStreamBlocks) blocks = kStreamBlocks;
-        const int64_t per_block = (T + blocks - 1) / blocks;
-        blocks = (T + per_block - 1) / per_block;
+        const int64_t blocks = (T + per_block - 1) / per_block;
         if (in_place) {
             hipLaunchKernelGGL(halo_copy_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, h, per_block,
                                h_copy);

@@ -45,11 +45,7 @@ template <bool kIds>
 __device__ __forceinline__ bool ids_prologue(const IdSource& src, int64_t T, int32_t* dev_err) {
     if (!kIds) return true;
     if (blockIdx.y == 1) {
-        const f32x4* from = reinterpret_cast<const f32x4*>(src.conv_state);
-        f32x4* to = reinterpret_cast<f32x4*>(src.snap);
-        for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < src.snap_vec4;
-             i += (int64_t)gridDim.x * blockDim.x)
-            to[i] = from[i];
+        copy_state(src.conv_state, src.snap, src.cu, src.S, src.snap_pb, blockIdx.x, gridDim.x);
         return false;
     }
     if (blockIdx.x == 0) check_cu(src.cu, src.S, T, dev_err);
@@ -333,7 +329,8 @@ hipError_t launch_gather_ids(const IdSource& src, int layout, int64_t T, const u
                              const uint8_t* nv_blocks, const float* scales, int64_t R, uint16_t* x,
                              int32_t* dev_err, hipStream_t stream) {
     int64_t blocks = (T + kTokPerBlock - 1) / kTokPerBlock;
-    const int64_t snap_blocks = (src.snap_vec4 + 64 * kTokPerBlock - 1) / (64 * kTokPerBlock);
+    // grid row 1 copies the state, one sequence per block and round
+    const int64_t snap_blocks = src.snap ? src.S : 0;
     if (snap_blocks > blocks) blocks = snap_blocks < 65536 ? snap_blocks : 65536;
     if (blocks < 1) blocks = 1;
     IdSource s = src;

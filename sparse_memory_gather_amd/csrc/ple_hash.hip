@@ -29,14 +29,10 @@ hash_kernel(const int32_t* __restrict__ tokens, int64_t T, const int32_t* __rest
             const int32_t* __restrict__ hist_ids, const int32_t* __restrict__ hist_len,
             int32_t vocab, ModR mr, int32_t* __restrict__ row_ids, int32_t* dev_err,
             const float* __restrict__ conv_state, float* __restrict__ state_snap,
-            int64_t snap_vec4) {
+            int64_t snap_pb) {
     if (blockIdx.y == 1) {
-        // copy of the carried conv state, float4 at a time
-        const f32x4* src = reinterpret_cast<const f32x4*>(conv_state);
-        f32x4* dst = reinterpret_cast<f32x4*>(state_snap);
-        for (int64_t i = (int64_t)blockIdx.x * kHashBlock + threadIdx.x; i < snap_vec4;
-             i += (int64_t)gridDim.x * kHashBlock)
-            dst[i] = src[i];
+        // copy of the carried conv state of the sequences that need one
+        copy_state(conv_state, state_snap, cu, S, snap_pb, blockIdx.x, gridDim.x);
         return;
     }
     if (blockIdx.x == 0) check_cu(cu, S, T, dev_err);
@@ -57,40 +53,40 @@ hash_kernel(const int32_t* __restrict__ tokens, int64_t T, const int32_t* __rest
 
 // the carried conv state alone (ple_forward_x: no ID kernel in the launch)
 __global__ void __launch_bounds__(kHashBlock)
-state_copy_kernel(const f32x4* __restrict__ src, f32x4* __restrict__ dst, int64_t n) {
-    for (int64_t i = (int64_t)blockIdx.x * kHashBlock + threadIdx.x; i < n; i += (int64_t)gridDim.x * kHashBlock)
-        dst[i] = src[i];
+state_copy_kernel(const float* __restrict__ conv_state, float* __restrict__ state_snap,
+                  const int32_t* __restrict__ cu, int32_t S, int64_t pb) {
+    copy_state(conv_state, state_snap, cu, S, pb, blockIdx.x, gridDim.x);
 }
 
 }  // namespace
 
-hipError_t launch_state_copy(const float* conv_state, float* state_snap, int32_t S, hipStream_t stream) {
-    const int64_t n = (int64_t)S * 3 * kD / 4;
-    int64_t blocks = (n + kHashBlock - 1) / kHashBlock;
-    if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)blocks), dim3(kHashBlock), 0, stream,
-                       reinterpret_cast<const f32x4*>(conv_state), reinterpret_cast<f32x4*>(state_snap), n);
+hipError_t launch_state_copy(const float* conv_state, float* state_snap, const int32_t* cu, int32_t S,
+                             int64_t pb, hipStream_t stream) {
+    int64_t blocks = S < 65536 ? S : 65536;  // one sequence per block and round
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)blocks), dim3(kHashBlock), 0, stream, conv_state,
+                       state_snap, cu, S, pb);
     return hipGetLastError();
 }
 
 hipError_t launch_hash(const int32_t* tokens, int64_t T, const int32_t* cu, int32_t S,
                        const int32_t* hist_ids, const int32_t* hist_len, int32_t vocab, int64_t R,
                        int32_t* row_ids, int32_t* dev_err, const float* conv_state,
-                       float* state_snap, bool heads, hipStream_t stream) {
+                       float* state_snap, int64_t snap_pb, bool heads, hipStream_t stream) {
     int64_t blocks = (T + kHashBlock - 1) / kHashBlock;
     if (blocks < 1) blocks = 1;
-    int64_t snap_vec4 = state_snap ? (int64_t)S * 3 * kD / 4 : 0;
-    int64_t snap_blocks = (snap_vec4 + kHashBlock - 1) / kHashBlock;
+    // grid row 1 copies the state, one sequence per block and round
+    const int64_t snap_blocks = state_snap ? S : 0;
     if (snap_blocks > blocks) blocks = snap_blocks < 65536 ? snap_blocks : 65536;
     dim3 grid((unsigned)blocks, state_snap ? 2 : 1);
     if (heads)
         hipLaunchKernelGGL(hash_kernel<16>, grid, dim3(kHashBlock), 0, stream, tokens, T, cu, S, hist_ids,
                            hist_len, vocab, make_mod((uint64_t)R), row_ids, dev_err, conv_state, state_snap,
-                           snap_vec4);
+                           snap_pb);
     else
         hipLaunchKernelGGL(hash_kernel<0>, grid, dim3(kHashBlock), 0, stream, tokens, T, cu, S, hist_ids,
                            hist_len, vocab, make_mod((uint64_t)R), row_ids, dev_err, conv_state, state_snap,
-                           snap_vec4);
+                           snap_pb);
     return hipGetLastError();
 }
 

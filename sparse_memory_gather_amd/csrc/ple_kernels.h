@@ -37,21 +37,22 @@ struct IdSource {
     const int32_t* hist_len;
     int32_t vocab;
     int32_t* row_ids_out;     // int32 [T][2] (16-lookup layout: [T][16]), or NULL
-    const float* conv_state;  // copied to snap (snap_vec4 float4s) when snap is not NULL
+    const float* conv_state;  // copied to snap when snap is not NULL (the sequences that need it)
     float* snap;
-    int64_t snap_vec4;
+    int64_t snap_pb;          // the fuse's tokens per block (fuse_block_tokens)
     uint64_t mod_R, mod_m;  // set by launch_gather_ids (R and its reciprocal for mod_r)
 };
 
 // ---- launchers (each returns hipGetLastError()) ----------------------------
 
 // n-gram IDs for T tokens (2 per token, or 16 with heads); optionally also
-// copies conv_state [S][3][kD] into state_snap (the fused path reads the old
-// state from the copy while it rewrites conv_state in place).
+// copies conv_state [S][3][kD] into state_snap for the sequences whose state
+// the fuse (snap_pb tokens per block) reads in one block and rewrites in
+// another.
 hipError_t launch_hash(const int32_t* tokens, int64_t T, const int32_t* cu, int32_t S,
                        const int32_t* hist_ids, const int32_t* hist_len, int32_t vocab, int64_t R,
                        int32_t* row_ids, int32_t* dev_err, const float* conv_state,
-                       float* state_snap, bool heads, hipStream_t stream);
+                       float* state_snap, int64_t snap_pb, bool heads, hipStream_t stream);
 
 // NVFP4 table: codes [R][1280] (E2M1, low nibble first), blocks [R][160]
 // (E4M3 per 16 elements), scales [R]; raw (optional) [T][2][1280]
@@ -59,8 +60,13 @@ hipError_t launch_gather_nvfp4(const int32_t* row_ids, int64_t T, const uint8_t*
                                const float* scales, int64_t R, uint16_t* x, uint8_t* raw, int32_t* dev_err,
                                hipStream_t stream);
 
-// copy of conv_state [S][3][kD] into state_snap
-hipError_t launch_state_copy(const float* conv_state, float* state_snap, int32_t S, hipStream_t stream);
+// copy of conv_state [S][3][kD] into state_snap (the sequences that need it)
+hipError_t launch_state_copy(const float* conv_state, float* state_snap, const int32_t* cu, int32_t S,
+                             int64_t pb, hipStream_t stream);
+
+// Tokens per block of the fuse for a T-token call of S sequences (1 when it
+// runs one token per block); the state copy and the fuse agree on it.
+int64_t fuse_block_tokens(int64_t T, int32_t S);
 
 // 16-lookup layout: table [16][R][160], scales [16][R], row_ids [T][16],
 // raw (optional) [T][16][160].

@@ -115,4 +115,28 @@ __device__ __forceinline__ void check_cu(const int32_t* cu, int32_t S, int64_t T
     }
 }
 
+// Sequence [st, en) needs its carried conv state copied before the fuse
+// runs when its first and last tokens fall in different fuse blocks of pb
+// tokens: the block holding the last token rewrites the state in place while
+// another may still read the old one. Within one block the state is read at
+// the first token and written at the last by the same thread, in order.
+__device__ __forceinline__ bool state_needs_copy(int64_t st, int64_t en, int64_t pb) {
+    return en > st && st / pb != (en - 1) / pb;
+}
+
+// Copy of the conv state ([S][3][kD] floats) of the sequences that need it:
+// block `blk` of `nblk` takes sequences blk, blk + nblk, ..., its threads
+// the float4s of each.
+__device__ __forceinline__ void copy_state(const float* __restrict__ from, float* __restrict__ to,
+                                           const int32_t* __restrict__ cu, int32_t S, int64_t pb,
+                                           int64_t blk, int64_t nblk) {
+    constexpr int kPerSeq = 3 * kD / 4;  // float4s per sequence
+    const f32x4* src = reinterpret_cast<const f32x4*>(from);
+    f32x4* dst = reinterpret_cast<f32x4*>(to);
+    for (int64_t s = blk; s < S; s += nblk) {
+        if (!state_needs_copy(cu[s], cu[s + 1], pb)) continue;  // uniform in the block
+        for (int i = threadIdx.x; i < kPerSeq; i += blockDim.x) dst[s * kPerSeq + i] = src[s * kPerSeq + i];
+    }
+}
+
 }  // namespace ple
