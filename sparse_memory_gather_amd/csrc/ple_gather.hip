@@ -10,11 +10,15 @@
 //   - E4M3FN -> fp32 with the hardware conversion, times the row scale, the
 //     two products added in fp32 (no FMA contraction), rounded once to bf16;
 //   - each span becomes 1 KB of output written by one store instruction
-//     (16 contiguous bytes per lane), marked non-temporal: x is streamed to
-//     HBM once and only read back by the projection. On MI355X with uniform
-//     row IDs, plain stores of this layout take 19% longer and 32 bytes per
-//     lane per 16-byte load (each store instruction covering every other
-//     16-byte slot) 29% longer.
+//     (16 contiguous bytes per lane); 32 bytes per lane per 16-byte load
+//     (each store instruction covering every other 16-byte slot) took 29%
+//     longer. The stores are plain, not non-temporal: x then stays in the
+//     memory-side cache, and its write-back to HBM overlaps the
+//     compute-bound projection that reads it next (a 32K-token call: 54-55
+//     us against 60-61 us with non-temporal stores, the projection no
+//     slower). A gather run back to back with itself, as in an isolated
+//     timing loop, is the opposite case: each run then pays for the
+//     previous run's write-back, and non-temporal stores are faster.
 #include "ple_ngram.h"
 
 namespace ple {
@@ -114,7 +118,7 @@ gather_kernel(const int32_t* __restrict__ row_ids, int64_t T, const uint8_t* __r
         u32x4 o;
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
-        __builtin_nontemporal_store(o, xrow + s * 64);
+        *(xrow + s * 64) = o;
     }
     if (raw) {
         u32x2* d0 = reinterpret_cast<u32x2*>(raw + (t * 2 + 0) * kD) + lane;
@@ -201,7 +205,7 @@ gather_heads_kernel(const int32_t* __restrict__ row_ids, int64_t T, const uint8_
             u32x4 o;
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[i] = ok[k][s] ? pack_bf16x2(p[2 * i], p[2 * i + 1]) : 0u;
-            __builtin_nontemporal_store(o, xrow + s * 64);
+            *(xrow + s * 64) = o;
         }
         if (raw) {
 #pragma unroll
@@ -282,7 +286,7 @@ gather_nvfp4_kernel(const int32_t* __restrict__ row_ids, int64_t T, const uint8_
         u32x4 o;
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
-        __builtin_nontemporal_store(o, xrow + s * 64);
+        *(xrow + s * 64) = o;
     }
     if (raw) {
         uint32_t* d0 = reinterpret_cast<uint32_t*>(raw + (t * 2 + 0) * (kD / 2)) + lane;

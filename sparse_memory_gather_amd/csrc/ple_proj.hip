@@ -215,7 +215,8 @@ proj_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __restric
     if (kFwd) {
         // the wave's own LDS writes are complete before its reads (in-order LDS
         // queue per wave); each store instruction writes four 256-byte token
-        // rows, non-temporal since e is only read back once, by the fuse kernel
+        // rows. Plain stores leave e in the memory-side cache for the fuse
+        // kernel, which reads it next.
         const int c = lane & 15;
 #pragma unroll 4
         for (int q = 0; q < 16; ++q) {
@@ -223,7 +224,7 @@ proj_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __restric
             const int64_t tok = m0 + tq * 64 + r;
             const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * 128 + (c ^ (r & 15)) * 8);
             if (tok < M)
-                __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(e16 + tok * kD + n0 + fh * 128 + c * 8));
+                *reinterpret_cast<u32x4*>(e16 + tok * kD + n0 + fh * 128 + c * 8) = v;
         }
     }
 }
@@ -476,7 +477,7 @@ proj_mid_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __res
             const int r = wave * 16 + q * 2 + (lane >> 5);
             const int64_t tok = m0 + r;
             const u32x4 v = *reinterpret_cast<const u32x4*>(lds + r * 256 + (c ^ (r & 31)) * 8);
-            if (tok < M) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(e16 + tok * kD + n0 + c * 8));
+            if (tok < M) *reinterpret_cast<u32x4*>(e16 + tok * kD + n0 + c * 8) = v;
         }
     }
 }
@@ -626,7 +627,7 @@ proj_w320_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __re
             const int row = q / (BNW / 8), col = q % (BNW / 8);
             const int64_t tok = m0 + (row >> 5) * 64 + j * 32 + (row & 31);
             const u32x4 v = *reinterpret_cast<const u32x4*>(lds + row * kPadRow + col * 8);
-            if (tok < M) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(e16 + tok * kD + n0 + col * 8));
+            if (tok < M) *reinterpret_cast<u32x4*>(e16 + tok * kD + n0 + col * 8) = v;
         }
     }
 }
