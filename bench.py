@@ -220,6 +220,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--copy-ceiling", action="store_true",
+                    help="also time a plain device copy of the gather's output size (x bytes read, "
+                         "x bytes written) after a 1 GiB cache flush: the rate an HBM-bound kernel "
+                         "moving the gather's bytes could reach")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -485,6 +489,25 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         result["copy_calibration_bytes"] = 1 << 30
+    if args.copy_ceiling:
+        nbytes = int(tokens_per_call) * 2560 * 2
+        src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        sink = torch.empty(12, dtype=torch.uint8, device=dev)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(12)]
+        for k in range(12):
+            torch.amax(flush, dim=0, out=sink[k])
+            ev[k][0].record()
+            dst.copy_(src)
+            ev[k][1].record()
+        torch.cuda.synchronize()
+        us = [a.elapsed_time(b) * 1e3 for a, b in ev[2:]]
+        avg = sum(us) / len(us)
+        result["copy_ceiling"] = {"bytes": 2 * nbytes, "avg_us": round(avg, 2),
+                                  "achieved": round(2 * nbytes / avg * 1e-3, 1), "unit": "GB/s",
+                                  "kernel": "torch copy_ (uint8, contiguous)"}
+        del src, dst, flush, sink
     print(json.dumps(result), flush=True)
 
 
