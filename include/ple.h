@@ -46,9 +46,10 @@
  *    outputs of the affected tokens are then unspecified but every access
  *    stays in bounds.
  *  - T = 0 is valid and enqueues nothing.
- *  - Thread-safe; the only global state is a thread-local error message and
- *    a per-device flag recording that the projection kernels' LDS size has
- *    been set (set once, under an atomic).
+ *  - Thread-safe; the only global state is a thread-local error message, a
+ *    per-device flag recording that the projection kernels' LDS size has
+ *    been set (set once, under an atomic) and, for ple_forward_noalloc only,
+ *    a per-device device array and its address (see that call).
  */
 #ifndef PLE_H
 #define PLE_H
@@ -261,6 +262,26 @@ int ple_forward_nvfp4_profiled(const ple_forward_args* args, const uint8_t* bloc
  * over 3 when it needs fewer rounds of 256 blocks). All give the same bits.
  * Host-only, enqueues nothing; for labelling measurements. */
 int ple_proj_tiling(int64_t T);
+
+/* ---- One call that allocates nothing -----------------------------------
+ * For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation. ple_forward_noalloc is ple_forward (same arguments, kernels and
+ * results, bit for bit) with args->workspace NULL and args->workspace_bytes 0:
+ * its workspace is a device array inside the library, 28,852,224 bytes on
+ * each GPU it runs on, held until the process ends, enough for a call of up
+ * to ple_forward_noalloc_max_tokens() = 2048 tokens and
+ * ple_forward_noalloc_max_sequences() = 256 sequences. Larger calls return
+ * PLE_ERR_SHAPE before anything is enqueued; a non-NULL workspace returns
+ * PLE_ERR_WORKSPACE. The call allocates and frees nothing (the array's device
+ * address is looked up once per device, on the first call with that device
+ * current). Every call on one GPU shares that GPU's array: calls that overlap
+ * on one GPU (two streams, or two threads without ordering) race and give
+ * unspecified results; calls ordered on one stream are safe. Nothing in the
+ * array needs to start at zero. */
+int ple_forward_noalloc(const ple_forward_args* args, void* stream);
+size_t ple_forward_noalloc_max_tokens(void);
+size_t ple_forward_noalloc_max_sequences(void);
 
 /* Static description of a status code. */
 const char* ple_status_string(int status);

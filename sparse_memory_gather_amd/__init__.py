@@ -64,7 +64,8 @@ EXPORTS = ("ple_hash", "ple_lookup", "ple_proj", "ple_forward", "ple_forward_pro
            "ple_forward_workspace_size", "ple_hash_heads", "ple_lookup_heads", "ple_forward_heads",
            "ple_forward_heads_profiled", "ple_forward_heads_workspace_size", "ple_forward_x",
            "ple_lookup_nvfp4", "ple_forward_nvfp4", "ple_forward_nvfp4_profiled",
-           "ple_status_string", "ple_last_error", "ple_proj_tiling")
+           "ple_status_string", "ple_last_error", "ple_proj_tiling", "ple_forward_noalloc",
+           "ple_forward_noalloc_max_tokens", "ple_forward_noalloc_max_sequences")
 HEADS = 16            # 16-lookup layout: head tables of 160-byte rows
 SLICE = D // HEADS
 
@@ -110,6 +111,11 @@ def load_library(path: str = LIB_PATH):
     lib.ple_last_error.restype = ctypes.c_char_p
     lib.ple_proj_tiling.argtypes = [I64]
     lib.ple_proj_tiling.restype = ctypes.c_int
+    lib.ple_forward_noalloc.argtypes = [ctypes.POINTER(ForwardArgs), _P]
+    lib.ple_forward_noalloc.restype = ctypes.c_int
+    for name in ("ple_forward_noalloc_max_tokens", "ple_forward_noalloc_max_sequences"):
+        getattr(lib, name).argtypes = []
+        getattr(lib, name).restype = ctypes.c_size_t
     _lib = lib
     return lib
 
@@ -284,7 +290,8 @@ class Forward:
 
     def __init__(self, tokens, cu_seqlens, table, scales, W, conv_w, h, state: State, out=None,
                  workspace=None, vocab_size: int = DEFAULT_VOCAB, eps: float = DEFAULT_EPS,
-                 dev_err=None, debug: bool = False, heads: bool = False, nvfp4_blocks=None):
+                 dev_err=None, debug: bool = False, heads: bool = False, nvfp4_blocks=None,
+                 noalloc: bool = False):
         T = tokens.numel()
         S = cu_seqlens.numel() - 1
         nv = nvfp4_blocks is not None
@@ -295,9 +302,15 @@ class Forward:
         dev = tokens.device
         if out is None:
             out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
-        if workspace is None:
-            workspace = Workspace(dev)
-        ws = workspace.get(T, S, heads) if isinstance(workspace, Workspace) else workspace
+        if noalloc:
+            # ple_forward_noalloc: the library's own device array is the workspace
+            if workspace is not None or heads or nv:
+                raise ValueError("noalloc runs the two-lookup FP8 table with the library's own workspace")
+            ws = None
+        else:
+            if workspace is None:
+                workspace = Workspace(dev)
+            ws = workspace.get(T, S, heads) if isinstance(workspace, Workspace) else workspace
         dbg = {}
         if debug:
             dbg = dict(row_ids=torch.empty((T, n), dtype=torch.int32, device=dev),
@@ -321,8 +334,8 @@ class Forward:
         a.hist_ids = _dev(state.hist_ids, "hist_ids", torch.int32, (S, 2))
         a.hist_len = _dev(state.hist_len, "hist_len", torch.int32, (S,))
         a.conv_state = _dev(state.conv_state, "conv_state", torch.float32, (S, 3, D))
-        a.workspace = _dev(ws, "workspace", torch.uint8)
-        a.workspace_bytes = ws.numel()
+        a.workspace = None if ws is None else _dev(ws, "workspace", torch.uint8)
+        a.workspace_bytes = 0 if ws is None else ws.numel()
         a.dev_err = _opt(dev_err, "dev_err", torch.int32, (1,))
         a.eps = eps
         if debug:
@@ -336,7 +349,10 @@ class Forward:
         byref = ctypes.byref(a)
         # the tensors whose addresses the struct holds stay referenced here
         self._keep = (tokens, cu_seqlens, table, scales, W, conv_w, h, state, ws, dev_err, nvfp4_blocks)
-        if nv:
+        if noalloc:
+            self._run = lambda st: lib.ple_forward_noalloc(byref, st)
+            self._run_ev = None
+        elif nv:
             blk = _dev(nvfp4_blocks, "nvfp4_blocks", torch.uint8, (R, D // 16))
             self._run = lambda st: lib.ple_forward_nvfp4(byref, blk, st)
             self._run_ev = lambda st, ev: lib.ple_forward_nvfp4_profiled(byref, blk, st, ev)
@@ -352,6 +368,8 @@ class Forward:
         returns out, or the debug dict. `events` as for ple_forward."""
         if events is None:
             _check(self._run(_stream(stream)))
+        elif self._run_ev is None:
+            raise ValueError("per-stage events are not recorded by ple_forward_noalloc")
         else:
             _check(self._run_ev(_stream(stream), (_P * 5)(*[ctypes.c_void_p(int(e)) for e in events])))
         if self.debug is not None:
@@ -363,16 +381,24 @@ class Forward:
 def ple_forward(tokens, cu_seqlens, table, scales, W, conv_w, h, state: State, out=None,
                 workspace=None, vocab_size: int = DEFAULT_VOCAB, eps: float = DEFAULT_EPS,
                 dev_err=None, debug: bool = False, stream=None, events=None, heads: bool = False,
-                nvfp4_blocks=None):
+                nvfp4_blocks=None, noalloc: bool = False):
     """a1..a4 for one chunk. Updates `state` in place; returns out (bf16
     [T][2560]) or, with debug=True, a dict with out, row_ids, x, e, gate, y.
     `events`: optional sequence of five hipEvent_t handles (ints) recorded
     around the four stages (ple_forward_profiled). heads=True: the 16-lookup
     layout (scales [16][R], row_ids [T][16]). nvfp4_blocks (uint8 [R][160]):
-    the NVFP4 table, `table` then being the packed codes uint8 [R][1280]."""
+    the NVFP4 table, `table` then being the packed codes uint8 [R][1280].
+    noalloc=True: ple_forward_noalloc (no workspace; up to
+    noalloc_limits() tokens and sequences)."""
     return Forward(tokens, cu_seqlens, table, scales, W, conv_w, h, state, out=out, workspace=workspace,
                    vocab_size=vocab_size, eps=eps, dev_err=dev_err, debug=debug, heads=heads,
-                   nvfp4_blocks=nvfp4_blocks)(stream=stream, events=events)
+                   nvfp4_blocks=nvfp4_blocks, noalloc=noalloc)(stream=stream, events=events)
+
+
+def noalloc_limits():
+    """(max tokens, max sequences) of one ple_forward_noalloc call."""
+    lib = load_library()
+    return int(lib.ple_forward_noalloc_max_tokens()), int(lib.ple_forward_noalloc_max_sequences())
 
 
 def ple_forward_x(x, tokens, cu_seqlens, W, conv_w, h, state: State, out=None, workspace=None,

@@ -8,6 +8,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
 #include <string>
 
 #include "../../include/ple.h"
@@ -75,12 +76,12 @@ struct WsLayout {
     size_t row_ids, x, e16, snap, total;
 };
 
-size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
+constexpr size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // row IDs per token: 2 (bigram, trigram) or 16 in the 16-lookup layout
-int ids_per_token(bool heads) { return heads ? 16 : 2; }
+constexpr int ids_per_token(bool heads) { return heads ? 16 : 2; }
 
-WsLayout layout(int64_t T, int32_t S, bool heads) {
+constexpr WsLayout layout(int64_t T, int32_t S, bool heads) {
     WsLayout w{};
     size_t off = 0;
     w.row_ids = off; off = up256(off + (size_t)T * ids_per_token(heads) * sizeof(int32_t));
@@ -408,6 +409,69 @@ int ple_forward_nvfp4_profiled(const ple_forward_args* a, const uint8_t* blocks,
 int ple_forward_x(const ple_forward_args* a, const uint16_t* x_bf16, void* stream) {
     if (!x_bf16) return fail(PLE_ERR_NULL, "ple_forward_x: x is NULL");
     return forward_impl(a, stream, nullptr, false, x_bf16);
+}
+
+}  // extern "C"
+
+// ---- ple_forward_noalloc: the workspace in a static device array ----------
+//
+// For callers that cannot allocate device memory. The workspace of a call of
+// up to kNoAllocMaxT tokens and kNoAllocMaxS sequences lives in `scratch`, a
+// file-scope device array that each GPU the library runs on holds until the
+// process ends. Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in for the symbol): its device address is looked up
+// once per device with hipGetSymbolAddress, with that device current, and
+// kept in g_scratch. Every call on one GPU shares that GPU's array; the
+// kernels write each region before reading it, so nothing has to start at
+// zero, and calls that overlap on one GPU (on different streams, or from
+// different threads without ordering) race on it.
+namespace {
+constexpr int64_t kNoAllocMaxT = 2048;
+constexpr int32_t kNoAllocMaxS = 256;
+constexpr size_t kScratchBytes = layout(kNoAllocMaxT, kNoAllocMaxS, false).total;
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// device address of this device's scratch (looked up on the first call)
+static int scratch_ptr(void** out) {
+    int dev = 0;
+    if (int st = hip_status(hipGetDevice(&dev), "ple_forward_noalloc: hipGetDevice")) return st;
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(PLE_ERR_HIP, "ple_forward_noalloc: device %d beyond the %d supported", dev, kMaxDevices);
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (int st = hip_status(e, "ple_forward_noalloc: hipGetSymbolAddress(scratch)")) return st;
+        if (!p) return fail(PLE_ERR_HIP, "ple_forward_noalloc: no device address for the scratch array");
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return PLE_OK;
+}
+
+extern "C" {
+
+size_t ple_forward_noalloc_max_tokens(void) { return (size_t)kNoAllocMaxT; }
+
+size_t ple_forward_noalloc_max_sequences(void) { return (size_t)kNoAllocMaxS; }
+
+int ple_forward_noalloc(const ple_forward_args* a, void* stream) {
+    if (!a) return fail(PLE_ERR_NULL, "ple_forward_noalloc: args is NULL");
+    if (a->T > kNoAllocMaxT || a->S > kNoAllocMaxS)
+        return fail(PLE_ERR_SHAPE, "ple_forward_noalloc: T = %lld, S = %d beyond its limits (T <= %lld, S <= %d)",
+                    (long long)a->T, a->S, (long long)kNoAllocMaxT, kNoAllocMaxS);
+    if (a->workspace || a->workspace_bytes)
+        return fail(PLE_ERR_WORKSPACE, "ple_forward_noalloc: workspace must be NULL and workspace_bytes 0 "
+                                       "(the call uses the library's own scratch)");
+    void* ws = nullptr;
+    if (int st = scratch_ptr(&ws)) return st;
+    ple_forward_args b = *a;
+    b.workspace = ws;
+    b.workspace_bytes = kScratchBytes;
+    return forward_impl(&b, stream, nullptr, false);
 }
 
 }  // extern "C"

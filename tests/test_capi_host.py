@@ -184,3 +184,18 @@ def test_binding_raises_when_the_library_is_missing(tmp_path, monkeypatch):
     monkeypatch.setattr(ple, "_lib", None)
     with pytest.raises(ImportError, match="not built"):
         ple.load_library(str(tmp_path / "libple.so"))
+
+
+@cpu_only
+def test_noalloc_refuses_oversize_calls_and_a_workspace_before_any_launch():
+    lib = ple.load_library()
+    assert lib.ple_forward_noalloc_max_tokens() == 2048 and lib.ple_forward_noalloc_max_sequences() == 256
+    # beyond the array's limits: PLE_ERR_SHAPE, with the limits in the message
+    for over in (dict(T=2049), dict(S=257)):
+        a = _fwd_args(workspace=None, workspace_bytes=0, **over)
+        assert lib.ple_forward_noalloc(ctypes.byref(a), None) == -2
+        assert b"beyond its limits" in lib.ple_last_error()
+    # the call brings no workspace of its own
+    a = _fwd_args()
+    assert lib.ple_forward_noalloc(ctypes.byref(a), None) == -6
+    assert lib.ple_forward_noalloc(None, None) == -1
