@@ -12,7 +12,7 @@ HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-shared", "-std=c++17",
 
 
 def commands():
-    host = ["gcc", "-O2", "-fPIC", "-shared", "-std=c11", "-ffp-contract=off",
+    host = ["gcc", "-O2", "-fPIC", "-shared", "-std=c11", "-fopenmp", "-ffp-contract=off",
             os.path.join(HERE, "csrc", "tablegen_host.c"),
             "-o", os.path.join(HERE, "libplegen_host.so")]
     hip = ["/opt/rocm/bin/hipcc", *HIPCC_FLAGS, os.path.join(HERE, "csrc", "tablegen.hip"),

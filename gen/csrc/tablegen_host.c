@@ -67,6 +67,8 @@ void gen_table_rows(uint64_t seed, const int64_t* ids, int64_t n, const uint32_t
                     uint32_t scale_lo, uint32_t scale_span,
                     uint8_t* rows_out, float* scales_out) {
     const uint64_t key[2] = {seed, 0};
+    /* rows are independent: one thread per row */
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) {
         uint64_t r = (uint64_t)ids[i];
         uint8_t* row = rows_out + i * ROW;
@@ -103,10 +105,18 @@ void gen_table_span(uint64_t seed, uint64_t g0, int64_t n, const uint32_t* thr, 
     }
 }
 
+/* 160-byte rows q[0..n) of the 16 x [R][160] view (row q = h R + r starts at
+ * element 160 q) into out[n][160]. */
+void gen_table_slices(uint64_t seed, const int64_t* q, int64_t n, const uint32_t* thr, uint8_t* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) gen_table_span(seed, (uint64_t)q[i] * 160, 160, thr, out + i * 160);
+}
+
 /* Scales number ids[0..n) into out[n]. */
 void gen_scales(uint64_t seed, const int64_t* ids, int64_t n, uint32_t scale_lo, uint32_t scale_span,
                 float* out) {
     const uint64_t key[2] = {seed, 0};
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) {
         uint64_t sc[4] = {(uint64_t)ids[i], 1, 0, 0}, so[4];
         gen_philox4x64_10(sc, key, so);
@@ -120,6 +130,7 @@ void gen_scales(uint64_t seed, const int64_t* ids, int64_t n, uint32_t scale_lo,
 void gen_nvfp4_rows(uint64_t seed, const int64_t* ids, int64_t n, const uint32_t* thr7,
                     uint32_t block_lo, uint32_t block_span, uint8_t* codes_out, uint8_t* blocks_out) {
     const uint64_t key[2] = {seed, 1};
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) {
         uint64_t r = (uint64_t)ids[i];
         uint8_t* codes = codes_out + i * (ROW / 2);

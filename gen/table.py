@@ -44,6 +44,9 @@ def _host_lib():
         lib.gen_table_span.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int64, ctypes.c_void_p,
                                        ctypes.c_void_p]
         lib.gen_table_span.restype = None
+        lib.gen_table_slices.argtypes = [ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                         ctypes.c_void_p]
+        lib.gen_table_slices.restype = None
         lib.gen_scales.argtypes = [ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32,
                                    ctypes.c_uint32, ctypes.c_void_p]
         lib.gen_scales.restype = None
@@ -91,8 +94,8 @@ def slices_cpu(heads, ids, R: int, seed: int = inputs.TABLE_SEED):
     q = np.ascontiguousarray(heads * R + ids)
     thr = np.ascontiguousarray(thresholds())
     lib = _host_lib()
-    for i in range(n):
-        lib.gen_table_span(seed, int(q[i]) * SLICE, SLICE, thr.ctypes.data, codes[i].ctypes.data)
+    if n:
+        lib.gen_table_slices(seed, q.ctypes.data, n, thr.ctypes.data, codes.ctypes.data)
     scales = np.empty(n, dtype=np.float32)
     if n:
         lib.gen_scales(seed, q.ctypes.data, n, inputs.SCALE_M_LO, inputs.SCALE_M_SPAN, scales.ctypes.data)

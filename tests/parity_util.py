@@ -115,56 +115,78 @@ def head_rows(R: int):
     return lambda hs, rs: table.slices_cpu(hs, rs, R)
 
 
-def oracle_samples(seqs, samples, W, cw, R, eps=1e-6, heads: bool = False, nvfp4: bool = False):
-    """Reference outputs of sampled tokens.
+def oracle_windows(seqs, windows, W, cw, R, eps=1e-6, heads: bool = False, nvfp4: bool = False):
+    """Reference outputs of windows of consecutive tokens.
 
     seqs: list of (tokens int32[n], h bf16 bits [n][D]) — whole sequences
-          from their first token (history included).
-    samples: list of (seq index, position) pairs.
-    Each sample becomes its own short segment: the token and up to three
-    before it, with the two tokens before that as n-gram history. Its
-    output depends on nothing earlier, so the last token of each segment is
-    the exact reference of the sampled token."""
-    toks, hs, cu, hid, hln = [], [], [0], [], []
-    for si, p in samples:
+          from their first token (history included), fresh state at 0.
+    windows: list of (seq index, lo, hi): the outputs at positions lo..hi-1.
+    Each window becomes its own segment: positions max(0, lo - 3) .. hi-1,
+    with the two tokens before it as n-gram history. An output depends on
+    its own n-grams and on v of the three tokens before it, nothing earlier,
+    so rows lo..hi-1 of each segment are exact references. Returns the
+    concatenated rows (window order) of row_ids, x, e, e_b, g, y, out, v
+    (= g e_b, what the conv state carries) and the tolerances ytol, gtol."""
+    toks, hs, cu, hid, hln, keep = [], [], [0], [], [], []
+    for si, lo, hi in windows:
         st, hh = seqs[si]
-        q = max(0, p - 3)
-        toks.append(st[q:p + 1])
-        hs.append(hh[q:p + 1])
-        cu.append(cu[-1] + p + 1 - q)
+        assert 0 <= lo < hi <= len(st), (si, lo, hi)
+        q = max(0, lo - 3)
+        toks.append(st[q:hi])
+        hs.append(hh[q:hi])
+        keep.extend(range(cu[-1] + lo - q, cu[-1] + hi - q))
+        cu.append(cu[-1] + hi - q)
         k = min(2, q)
         hist = np.zeros(2, np.int32)
         if k:
             hist[2 - k:] = st[q - k:q]
         hid.append(hist)
         hln.append(k)
-    S = len(samples)
+    S = len(windows)
     if nvfp4:
         fwd, src = oracle.forward_nvfp4, table.nvfp4_rows_cpu
     elif heads:
         fwd, src = oracle.forward_heads, head_rows(R)
     else:
         fwd, src = oracle.forward, rows
-    r = fwd(np.concatenate(toks), np.array(cu, np.int32), np.concatenate(hs), W, cw, R,
+    cu = np.array(cu, np.int32)
+    r = fwd(np.concatenate(toks), cu, np.concatenate(hs), W, cw, R,
             src, np.array(hid, np.int32), np.array(hln, np.int32), np.zeros((S, 3, D)), eps)
-    last = np.array(cu[1:]) - 1
-    # y tolerance from the (up to) four taps that feed each sample; taps
-    # before a sequence start are zero on both sides
-    w = np.abs(inputs.bf16_bits_to_f32(cw).astype(np.float64))
-    v = np.abs(r["g"][:, None] * r["e_b"])
+    keep = np.array(keep, np.int64)
+    # tolerances: per token of the segments, then the kept rows. The y bound
+    # sums |w_k| (dv + fp32 rounding of v) over the taps inside the segment;
+    # taps before a sequence start are zero on both sides
     h_all = np.concatenate(hs)
     dv = dv_bound(r, W, h_all)
-    gtol = gate_bound(r, h_all, W)[last]
-    ytol = np.full((S, D), 1e-7)
-    for i in range(S):
-        a, b = cu[i], cu[i + 1]
-        n = b - a
-        for k in range(4):
-            j = n - 4 + k
-            if j >= 0:
-                ytol[i] += w[:, k] * (dv[a + j] + Y_FP32 * v[a + j])
-    return dict(row_ids=r["row_ids"][last], x=r["x"][last], e=r["e"][last], e_b=r["e_b"][last],
-                g=r["g"][last], y=r["y"][last], out=r["out"][last], ytol=ytol, gtol=gtol)
+    wa = np.asarray(cw) & 0x7FFF
+    zero_h = np.zeros(r["e"].shape, np.uint16)
+    v = np.abs(r["g"][:, None] * r["e_b"])
+    ytol, _, _ = oracle.conv_fuse(zero_h, dv + Y_FP32 * v, np.ones(len(r["g"])), cu, wa, np.zeros((S, 3, D)))
+    gtol = gate_bound(r, h_all, W)
+    return dict(row_ids=r["row_ids"][keep], x=r["x"][keep], e=r["e"][keep], e_b=r["e_b"][keep],
+                g=r["g"][keep], y=r["y"][keep], out=r["out"][keep], v=(r["g"][:, None] * r["e_b"])[keep],
+                dv=dv[keep], ytol=ytol[keep] + 1e-7, gtol=gtol[keep])
+
+
+def oracle_samples(seqs, samples, W, cw, R, eps=1e-6, heads: bool = False, nvfp4: bool = False):
+    """Reference outputs of sampled tokens: samples = (seq index, position)
+    pairs, each a one-token window of oracle_windows."""
+    return oracle_windows(seqs, [(si, p, p + 1) for si, p in samples], W, cw, R, eps, heads, nvfp4)
+
+
+def state_bound(ref: dict, cu, cw, W, h_bits) -> np.ndarray:
+    """Per-element bound on |conv_state_gpu - conv_state_ref| after a chunk
+    whose incoming state the GPU received exactly: the new state holds the
+    last three v of each sequence (dv_bound each, fp32 storage included) or,
+    for sequences shorter than three tokens, shifted carried values (copied,
+    exact). The oracle's own state update applied to dv with g = 1 and a
+    zero carried state places each bound where its v went."""
+    wa = np.asarray(cw) & 0x7FFF
+    S = len(cu) - 1
+    zero_h = np.zeros(ref["e"].shape, np.uint16)
+    _, _, st = oracle.conv_fuse(zero_h, dv_bound(ref, W, h_bits), np.ones(len(ref["g"])), cu, wa,
+                                np.zeros((S, 3, D)))
+    return st + 1e-7
 
 
 def check_samples(got: dict, ref: dict, W, label=""):
