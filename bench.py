@@ -3,15 +3,16 @@
 
 A step is one ple_forward over one batch of the workload (n-gram IDs ->
 gather/dequant from the 51.2 GB FP8 table in HBM -> projection -> gate /
-short conv / residual add). The default workload is the 32,768-token Zipf
+short conv / residual add). The headline workload is the 32,768-token Zipf
 prefill, the one the gather roofline target is stated for; --workload picks
 another (tiny, decode, ragged, long). Inputs are resident in HBM before the
 timed region; the timed region is K back-to-back steps between two device
 synchronizations.
 
 Printed: one JSON line with the step throughput (tokens/s), the roofline of
-the dominant kernel measured with HIP events inside the same run, per-stage
-durations, and the CPU oracle timed on a bounded sample of the same workload.
+the dominant kernel measured with HIP events in the same run, per-stage
+durations, the other four workloads measured the same way (per_config), and
+the CPU oracle timed on a bounded sample of the same workload.
 """
 
 from __future__ import annotations
@@ -23,6 +24,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -32,24 +35,28 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 D = 2560
 
-# Algorithmic bytes / flop per unit (one token, or one valid lookup).
-#  gather: per valid lookup 2560 B of codes + 4 B scale; per token 8 B of row
-#          ids read and 5120 B of bf16 x written
-#  proj:   2 * 2560 * 2560 flop per token
+# Algorithmic bytes / flop per unit (one token, or one distinct table row).
+#  gather: per distinct row read 2560 B of codes + 4 B scale (a row looked up
+#          twice needs to come from HBM once); per token 8 B of row ids read
+#          and 5120 B of bf16 x written
+#  proj:   2 * 2560 * 2560 flop per token; W (13,107,200 B) read once per call
 #  fuse:   per token h 5120 B + e 5120 B read, out 5120 B written
 #  hash:   per token 4 B token read (+ history), 8 B ids written
-GATHER_BYTES_PER_LOOKUP = 2560 + 4
+GATHER_BYTES_PER_ROW = 2560 + 4
 GATHER_BYTES_PER_TOKEN = 8 + 2 * D
-# 16-lookup layout: per valid head lookup 160 B of codes + 4 B scale; per
+# 16-lookup layout: per distinct (head, row) 160 B of codes + 4 B scale; per
 # token 64 B of row ids and 5120 B of bf16 x
-HEADS_BYTES_PER_LOOKUP = 160 + 4
+HEADS_BYTES_PER_ROW = 160 + 4
 HEADS_BYTES_PER_TOKEN = 64 + 2 * D
-# NVFP4 table: per valid lookup 1280 B of E2M1 codes + 160 B of E4M3 block
+# NVFP4 table: per distinct row 1280 B of E2M1 codes + 160 B of E4M3 block
 # scales + 4 B row scale; per token as the FP8 table
-NVFP4_BYTES_PER_LOOKUP = D // 2 + D // 16 + 4
+NVFP4_BYTES_PER_ROW = D // 2 + D // 16 + 4
 PROJ_FLOP_PER_TOKEN = 2 * D * D
+W_BYTES = D * D * 2
 FUSE_BYTES_PER_TOKEN = 3 * 2 * D
 
+# the other workloads of the same run: (name, timed steps, warm-up steps)
+PER_CONFIG = (("tiny", 50, 10), ("decode", 64, 8), ("ragged", 20, 5), ("long", 4, 1))
 
 KERNEL_SOURCES = {
     "proj_kernel": ["sparse_memory_gather_amd/csrc/ple_proj.hip", "sparse_memory_gather_amd/csrc/ple_kernels.h"],
@@ -136,16 +143,38 @@ def describe(name, wl, layout="two"):
     return f"tiny: 1 x {T} uniform tokens, {wl.R:,}-row FP8 table"
 
 
-def cpu_baseline(wl, name, W, cw, h0, budget_s=12.0, layout="two"):
-    """The CPU oracle (as it stands) on the first N tokens of the workload's
-    first chunk, N sized so that the run takes about `budget_s` seconds."""
-    import numpy as np
+def mem_available_gib():
+    try:
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemAvailable"):
+                    return int(line.split()[1]) / 2 ** 20
+    except OSError:
+        pass
+    return 0.0
 
+
+def cpu_baseline(wl, name, W, cw, h0, budget_s=12.0, layout="two", dev_table=None):
+    """The CPU oracle (as it stands) on the first N tokens of the workload's
+    first chunk, N sized so that the run takes about `budget_s` seconds.
+    With dev_table (the FP8 table and scales in HBM) and enough host memory,
+    the oracle reads its rows from a host-resident copy of the table's bytes
+    (copied before timing); otherwise the CPU generator rebuilds the rows a
+    call needs inside the call."""
     import oracle
     from gen import table
 
     toks, cu = wl.chunks[0]
     S = len(cu) - 1
+    row_source, source = table.rows_cpu, "table rows rebuilt on demand by the CPU generator inside the call"
+    host = None
+    if layout == "two" and dev_table is not None:
+        nbytes = dev_table[0].numel() + 4 * dev_table[1].numel()
+        if mem_available_gib() * 2 ** 30 > 1.5 * nbytes:
+            print(f"[bench] copying the {nbytes / 1e9:.1f} GB table to host memory", file=sys.stderr, flush=True)
+            host = (dev_table[0].cpu().numpy(), dev_table[1].cpu().numpy())
+            row_source = lambda ids: (host[0][ids], host[1][ids])
+            source = f"rows read from a host-resident copy of the {nbytes / 1e9:.1f} GB table"
 
     def run(n):
         # the first n tokens, cut at the same sequence boundaries
@@ -159,7 +188,7 @@ def cpu_baseline(wl, name, W, cw, h0, budget_s=12.0, layout="two"):
                                  lambda hs, rs: table.slices_cpu(hs, rs, wl.R),
                                  np.zeros((S, 2), np.int32), np.zeros(S, np.int32), np.zeros((S, 3, D)))
         else:
-            oracle.forward(toks[:n], cut, h0[:n], W, cw, wl.R, table.rows_cpu,
+            oracle.forward(toks[:n], cut, h0[:n], W, cw, wl.R, row_source,
                            np.zeros((S, 2), np.int32), np.zeros(S, np.int32), np.zeros((S, 3, D)))
         return time.perf_counter() - t0
 
@@ -171,7 +200,7 @@ def cpu_baseline(wl, name, W, cw, h0, budget_s=12.0, layout="two"):
     result = {"value": round(n / dt, 2), "unit": "tokens/s", "cores": oracle.num_threads(),
               "kind": "oracle",
               "sample": f"first {n} of {T} tokens of the {name} workload's first chunk, one call "
-                        f"({dt:.1f} s); table rows rebuilt on demand by the CPU generator"}
+                        f"({dt:.1f} s); {source}"}
     # the same oracle on one thread, a smaller sample (about a quarter of the budget)
     threads = oracle.num_threads()
     try:
@@ -183,6 +212,7 @@ def cpu_baseline(wl, name, W, cw, h0, budget_s=12.0, layout="two"):
     result["single_thread"] = {"value": round(n1 / dt1, 2), "unit": "tokens/s",
                                "sample": f"first {n1} tokens, one call ({dt1:.1f} s)"}
     result["host"] = host_description()
+    del host
     return result
 
 
@@ -205,72 +235,76 @@ def host_description():
     return {"cpu": model, "logical_cpus": os.cpu_count(), "mem_gib": mem_gb}
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="prefill", choices=["tiny", "decode", "prefill", "ragged", "long"])
-    ap.add_argument("--overlap", action="store_true",
-                    help="long workload: IDs and rows of the next chunk on a second stream (ple_forward_x)")
-    ap.add_argument("--layout", default="two", choices=["two", "heads", "nvfp4"],
-                    help="two: 2 lookups of 2560-byte FP8 rows per token; heads: 16 lookups of 160-byte "
-                         "rows; nvfp4: 2 lookups of NVFP4 rows (E2M1 codes, E4M3 scale per 16 elements)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
-    ap.add_argument("--copy-ceiling", action="store_true",
-                    help="also time a plain device copy of the gather's output size (x bytes read, "
-                         "x bytes written) after a 1 GiB cache flush: the rate an HBM-bound kernel "
-                         "moving the gather's bytes could reach")
-    args = ap.parse_args()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        sys.exit("bench.py measures one GPU: the path runs on a single MI355X (how it would shard "
-                 "across GPUs is described, not implemented), so --gpus must be 1")
+class Context:
+    """Device, weights and tables shared by the workloads of one run; the
+    51.2 GB table is generated once."""
 
-    import numpy as np
+    def __init__(self, dev):
+        import torch
+
+        from gen import inputs
+        self.dev = dev
+        self.W, self.cw = inputs.weights()
+
+        def bf16(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        self.bf16 = bf16
+        self.Wd, self.cwd = bf16(self.W), bf16(self.cw)
+        self._tables = {}
+        self.hev = HipEvents()
+
+    def table(self, R, layout):
+        """(table, scales, nvfp4 blocks or None) for R rows in the layout."""
+        from gen import table
+        key = (R, layout)
+        if key not in self._tables:
+            print(f"[bench] generating the {R:,}-row {layout} table", file=sys.stderr, flush=True)
+            if layout == "nvfp4":
+                codes, blocks, sc = table.nvfp4_gpu(R, device=self.dev)
+                self._tables[key] = (codes, sc, blocks)
+            elif layout == "heads":
+                tab, _, _ = self.table(R, "two")
+                self._tables[key] = (tab, table.head_scales_gpu(R, device=self.dev), None)
+            else:
+                tab, sc = table.table_gpu(R, device=self.dev)
+                self._tables[key] = (tab, sc, None)
+        return self._tables[key]
+
+    def drop_tables(self, keep_R):
+        import torch
+        for k in [k for k in self._tables if k[0] != keep_R]:
+            del self._tables[k]
+        torch.cuda.empty_cache()
+
+
+def measure(ctx, name, layout, steps, warmup, overlap=False, graph=False, cold=True):
+    """Time `steps` steps of workload `name` after `warmup` steps. Returns the
+    workload's figures: tokens/s from wall time and from events around the
+    timed loop, per-stage averages and medians from a second pass with
+    events around each kernel, the gather's bytes, and (cold) the same
+    stages with the caches flushed before each step."""
     import torch
 
     import sparse_memory_gather_amd as ple
-    from gen import inputs, table
+    from gen import inputs
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    ple.load_library()
-    name = args.workload
-    wl = inputs.make_workload(name, decode_steps=max(1, args.steps + args.warmup))
-    W, cw = inputs.weights()
-
-    def bf16(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    print(f"[bench] {name}: generating the {wl.R:,}-row table", file=sys.stderr, flush=True)
-    heads = args.layout == "heads"
-    nvfp4 = args.layout == "nvfp4"
-    blocks = None
-    if nvfp4:
-        tab, blocks, sc = table.nvfp4_gpu(wl.R, device=dev)
-    else:
-        tab, sc = table.table_gpu(wl.R, device=dev)
-    if heads:
-        sc = table.head_scales_gpu(wl.R, device=dev)
-    Wd, cwd = bf16(W), bf16(cw)
+    dev, hev = ctx.dev, ctx.hev
+    wl = inputs.make_workload(name, decode_steps=max(1, steps + warmup))
+    heads, nvfp4 = layout == "heads", layout == "nvfp4"
+    tab, sc, blocks = ctx.table(wl.R, layout)
+    Wd, cwd, bf16 = ctx.Wd, ctx.cwd, ctx.bf16
     ws = ple.Workspace(dev)
 
     # batches, all resident on the device before timing
+    print(f"[bench] {name}: inputs", file=sys.stderr, flush=True)
     batches = []
-    if name == "long":
-        for i, (t, c) in enumerate(wl.chunks):
-            batches.append((torch.from_numpy(t).to(dev), torch.from_numpy(c).to(dev), bf16(wl.hidden(i))))
-    elif name == "decode":
+    if name in ("long", "decode"):
         for i, (t, c) in enumerate(wl.chunks):
             batches.append((torch.from_numpy(t).to(dev), torch.from_numpy(c).to(dev), bf16(wl.hidden(i))))
     else:
         t, c = wl.chunks[0]
         batches.append((torch.from_numpy(t).to(dev), torch.from_numpy(c).to(dev), bf16(wl.hidden(0))))
-    h0 = wl.hidden(0) if name != "long" else None
     state = ple.State(wl.S, dev)
     if name == "decode":
         hist = wl.history[0]
@@ -279,12 +313,27 @@ def main():
         ple.ple_forward(torch.from_numpy(hist.reshape(-1)).to(dev), cu_h, tab, sc, Wd, cwd, hh, state,
                         workspace=ws, heads=heads, nvfp4_blocks=blocks)
         del hh
-    outs = [torch.empty_like(b[2]) for b in batches] if name in ("long", "decode") else \
-        [torch.empty_like(batches[0][2])]
+    outs = [torch.empty_like(b[2]) for b in batches]
     for b in batches:
-        ws.get(b[0].numel(), b[1].numel() - 1)
+        ws.get(b[0].numel(), b[1].numel() - 1, heads)
+    n_calls = len(batches) if name == "long" else 1
+    tokens_per_step = sum(b[0].numel() for b in batches) if name == "long" else batches[0][0].numel()
+    stream = torch.cuda.current_stream().cuda_stream
 
-    if name == "long" and args.overlap:
+    # one prepared call per fixed set of buffers (each long chunk, each decode
+    # step's batch, the single prefill/ragged/tiny batch): the argument
+    # checks and marshalling happen once, outside the timing
+    calls = [ple.Forward(t, c, tab, sc, Wd, cwd, h, state, out=o, workspace=ws, heads=heads,
+                         nvfp4_blocks=blocks) for (t, c, h), o in zip(batches, outs)]
+
+    def eager_step(k, events=None):
+        if name == "long":
+            for j, call in enumerate(calls):
+                call(events=None if events is None else events[j])
+        else:
+            calls[k % len(calls)](events=None if events is None else events[0])
+
+    if name == "long" and overlap:
         # IDs and rows of chunk i+1 on a side stream while chunk i is
         # projected and fused (ple_forward_x); each chunk's n-gram history
         # comes from the token stream, two x buffers alternate
@@ -308,7 +357,7 @@ def main():
         for e in free:
             e.record(main)
 
-        def step(k, events=None):
+        def step(k):
             for i, ((t, c, h), o) in enumerate(zip(batches, outs)):
                 j = i % 2
                 with torch.cuda.stream(side):
@@ -324,162 +373,261 @@ def main():
                     main.wait_event(ready[j])
                     ple.ple_forward_x(xbuf[j], t, c, Wd, cwd, h, state, out=o, workspace=ws)
                     free[j].record(main)
-        tokens_per_step = sum(b[0].numel() for b in batches)
-    else:
-        # one prepared call per fixed set of buffers (each long chunk, each
-        # decode step's batch, the single prefill/ragged/tiny batch): the
-        # argument checks and marshalling happen once, outside the timing
-        calls = [ple.Forward(t, c, tab, sc, Wd, cwd, h, state, out=o, workspace=ws, heads=heads,
-                             nvfp4_blocks=blocks) for (t, c, h), o in zip(batches, outs)]
-        if name == "long":
-            def step(k, events=None):
-                for call in calls:
-                    call(events=events)
-            tokens_per_step = sum(b[0].numel() for b in batches)
-        else:
-            def step(k, events=None):
-                calls[k % len(calls)](events=events)
-            tokens_per_step = batches[0][0].numel()
+    elif graph:
+        # each step's calls captured once into a HIP graph and replayed (the
+        # forward records no memset and allocates nothing)
+        eager_step(0)
+        torch.cuda.synchronize()
+        graphs = []
+        for k in range(len(calls) if name != "long" else 1):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                eager_step(k)
+            graphs.append(g)
+        torch.cuda.synchronize()
 
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for k in range(args.warmup):
+        def step(k):
+            graphs[k % len(graphs)].replay()
+    else:
+        def step(k):
+            eager_step(k)
+
+    print(f"[bench] {name}: warmup {warmup}, timing {steps} steps", file=sys.stderr, flush=True)
+    for k in range(warmup):
         step(k)
     torch.cuda.synchronize()
-
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    loop_ev = hev.create(2)
     t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(args.warmup + k)
+    hev.record(loop_ev[0], stream)
+    for k in range(steps):
+        step(warmup + k)
+    hev.record(loop_ev[1], stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = 1e3 * wall / args.steps
-    value = tokens_per_step * args.steps / wall
+    gpu_ms = hev.elapsed_ms(loop_ev[0], loop_ev[1])
+    res = {"name": name, "layout": layout, "steps": steps, "warmup": warmup,
+           "tokens_per_step": tokens_per_step, "ms_per_step": 1e3 * wall / steps,
+           "value": tokens_per_step * steps / wall, "gpu_ms_per_step": gpu_ms / steps,
+           "workload": describe(name, wl, layout), "S": wl.S, "R": wl.R, "graph": graph}
+    if graph or overlap:
+        return res
 
     # per-kernel durations inside the real forward: events around each kernel
-    hev = HipEvents()
-    stream = torch.cuda.current_stream().cuda_stream
-    n_calls = len(batches) if name == "long" else 1
-    reps = args.steps
-    ev = [hev.create(5) for _ in range(reps * n_calls)]
+    # (a second pass of the same steps, so that the event records do not
+    # perturb the timed loop)
+    ev = [[hev.create(5) for _ in range(n_calls)] for _ in range(steps)]
     torch.cuda.synchronize()
-    for k in range(reps):
-        if name == "long":
-            for j, (t, c, h) in enumerate(batches):
-                (calls[j] if not args.overlap else
-                 ple.Forward(t, c, tab, sc, Wd, cwd, h, state, out=outs[j], workspace=ws, heads=heads,
-                             nvfp4_blocks=blocks))(events=ev[k * n_calls + j])
-        else:
-            step(k, events=ev[k])
+    for k in range(steps):
+        eager_step(warmup + k, events=ev[k])
     torch.cuda.synchronize()
-    per_launch = np.array([[hev.elapsed_ms(e[i], e[i + 1]) for i in range(4)] for e in ev])
-    stage_us = 1e3 * per_launch.mean(axis=0)  # average per launch
-    stage_med_us = 1e3 * np.median(per_launch, axis=0)
-    tokens_per_call = tokens_per_step / n_calls
+    per_launch = np.array([[hev.elapsed_ms(e[i], e[i + 1]) for i in range(4)] for es in ev for e in es])
+    res["stage_us"] = 1e3 * per_launch.mean(axis=0)
+    res["stage_med_us"] = 1e3 * np.median(per_launch, axis=0)
+    res["stage_min_us"] = 1e3 * per_launch.min(axis=0)
+    res["stage_max_us"] = 1e3 * per_launch.max(axis=0)
 
-    # the same kernels cold: before each step a 1 GiB buffer is read (a max,
+    # the same kernels cold: before each call a 1 GiB buffer is read (a max,
     # so no dirty lines are left to write back and nothing is converted),
     # which evicts the L2s and the 256 MB Infinity Cache, so no table row can
     # be served from a cache filled by the previous step
-    cold_us = None
-    if name in ("prefill", "ragged", "tiny"):
+    if cold:
         flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
-        sink = torch.zeros(reps, dtype=torch.uint8, device=dev)
-        ev_cold = [hev.create(5) for _ in range(reps)]
+        n_cold = min(steps, 8) if name == "long" else steps
+        sink = torch.zeros(n_cold * n_calls, dtype=torch.uint8, device=dev)
+        ev_cold = [[hev.create(5) for _ in range(n_calls)] for _ in range(n_cold)]
         torch.cuda.synchronize()
-        for k in range(reps):
-            torch.amax(flush, dim=0, out=sink[k])
-            step(k, events=ev_cold[k])
+        for k in range(n_cold):
+            if name == "long":
+                for j, call in enumerate(calls):
+                    torch.amax(flush, dim=0, out=sink[k * n_calls + j])
+                    call(events=ev_cold[k][j])
+            else:
+                torch.amax(flush, dim=0, out=sink[k])
+                calls[(warmup + k) % len(calls)](events=ev_cold[k][0])
         torch.cuda.synchronize()
-        cold_us = 1e3 * np.array([[hev.elapsed_ms(e[i], e[i + 1]) for i in range(4)] for e in ev_cold]).mean(axis=0)
-        assert int(sink.sum().item()) == reps
+        cold = np.array([[hev.elapsed_ms(e[i], e[i + 1]) for i in range(4)] for es in ev_cold for e in es])
+        res["cold_stage_us"] = 1e3 * cold.mean(axis=0)
+        assert int(sink.sum().item()) == n_cold * n_calls
         del flush, sink
 
-    # valid lookups per call (for the gather's algorithmic bytes)
-    rid = ple.ple_hash(batches[0][0], batches[0][1], torch.zeros((wl.S, 2), dtype=torch.int32, device=dev),
-                       torch.full((wl.S,), 2 if name == "decode" else 0, dtype=torch.int32, device=dev), wl.R,
-                       heads=heads)
-    n_ids = 16 if heads else 2
-    lookups = int((rid >= 0).sum().item()) if name != "decode" else n_ids * batches[0][0].numel()
-    if heads:   # distinct (head, row) pairs
-        key = rid.to(torch.int64) + torch.arange(16, device=dev, dtype=torch.int64)[None, :] * wl.R
-        unique_rows = int(torch.unique(key[rid >= 0]).numel()) if name != "decode" else None
-    else:
-        unique_rows = int(torch.unique(rid[rid >= 0]).numel()) if name != "decode" else None
-    if heads:
-        gather_bytes = lookups * HEADS_BYTES_PER_LOOKUP + tokens_per_call * HEADS_BYTES_PER_TOKEN
-    elif nvfp4:
-        gather_bytes = lookups * NVFP4_BYTES_PER_LOOKUP + tokens_per_call * GATHER_BYTES_PER_TOKEN
-    else:
-        gather_bytes = lookups * GATHER_BYTES_PER_LOOKUP + tokens_per_call * GATHER_BYTES_PER_TOKEN
-    gather_gbs = gather_bytes / (stage_us[1] * 1e-6) / 1e9
-    proj_flop = tokens_per_call * PROJ_FLOP_PER_TOKEN
-    proj_tflops = proj_flop / (stage_us[2] * 1e-6) / 1e12
-    fuse_bytes = tokens_per_call * FUSE_BYTES_PER_TOKEN
-    fuse_gbs = fuse_bytes / (stage_us[3] * 1e-6) / 1e9
+    # lookups and distinct rows per call (the gather's algorithmic bytes),
+    # each call with the history it runs with
+    lookups, uniq = [], []
+    for i, (t, c, _) in enumerate(batches if name == "long" else batches[:1]):
+        S = wl.S
+        if name == "decode":
+            hid = torch.from_numpy(wl.history[0][:, -2:].astype(np.int32)).to(dev)
+            hl = torch.full((S,), 2, dtype=torch.int32, device=dev)
+        elif name == "long" and i > 0:
+            hid = torch.from_numpy(wl.chunks[i - 1][0][-2:].reshape(1, 2).astype(np.int32)).to(dev)
+            hl = torch.full((1,), 2, dtype=torch.int32, device=dev)
+        else:
+            hid = torch.zeros((S, 2), dtype=torch.int32, device=dev)
+            hl = torch.zeros((S,), dtype=torch.int32, device=dev)
+        rid = ple.ple_hash(t, c, hid, hl, wl.R, heads=heads)
+        valid = rid >= 0
+        lookups.append(int(valid.sum().item()))
+        key = rid.to(torch.int64)
+        if heads:   # distinct (head, row) pairs
+            key = key + torch.arange(16, device=dev, dtype=torch.int64)[None, :] * wl.R
+        uniq.append(int(torch.unique(key[valid]).numel()))
+    res["lookups_per_call"] = float(np.mean(lookups))
+    res["distinct_rows_per_call"] = float(np.mean(uniq))
+    res["tokens_per_call"] = tokens_per_step / n_calls
+    res["proj_kernel"] = ple.proj_tiling(int(res["tokens_per_call"]))
+    del calls, batches, outs, ws, state
+    torch.cuda.empty_cache()
+    return res
 
-    gather_name = "gather_heads_kernel" if heads else "gather_nvfp4_kernel" if nvfp4 else "gather_kernel"
-    dominant = int(np.argmax(stage_us))
-    proj_name = ple.proj_tiling(int(tokens_per_call))
-    if dominant == 2:
-        roofline = {"kernel": f"ple_proj ({proj_name})", "bound": "mfma",
-                    "achieved": round(proj_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(proj_tflops / BF16_PEAK_TFLOPS, 4),
-                    "traffic": recorded_traffic(proj_name, name),
-                    "per_launch": {"flop": proj_flop, "avg_us": round(float(stage_us[2]), 2)}}
-    elif dominant == 1:
-        roofline = {"kernel": f"ple_gather_dequant ({gather_name})", "bound": "hbm",
-                    "achieved": round(gather_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(gather_gbs / HBM_PEAK_GBS, 4),
-                    "traffic": recorded_traffic(gather_name, name),
-                    "per_launch": {"bytes": gather_bytes, "avg_us": round(float(stage_us[1]), 2)}}
-    else:
-        k = ["ple_hash (hash_kernel)", "", "", "ple_gate_conv_fuse (fuse_stream_kernel / fuse_token_kernel)"][dominant]
-        nb = fuse_bytes if dominant == 3 else tokens_per_call * 12
-        gbs = nb / (stage_us[dominant] * 1e-6) / 1e9
-        roofline = {"kernel": k, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                    "traffic": recorded_traffic("fuse_stream_kernel", name) if dominant == 3 else None,
-                    "per_launch": {"bytes": nb, "avg_us": round(float(stage_us[dominant]), 2)}}
 
+def figures(res, layout):
+    """Rooflines and rates from a measure() result."""
+    tpc = res["tokens_per_call"]
+    st = res["stage_us"]
+    if layout == "heads":
+        per_row, per_tok, gname = HEADS_BYTES_PER_ROW, HEADS_BYTES_PER_TOKEN, "gather_heads_kernel"
+    elif layout == "nvfp4":
+        per_row, per_tok, gname = NVFP4_BYTES_PER_ROW, GATHER_BYTES_PER_TOKEN, "gather_nvfp4_kernel"
+    else:
+        per_row, per_tok, gname = GATHER_BYTES_PER_ROW, GATHER_BYTES_PER_TOKEN, "gather_kernel"
+    g_bytes = res["distinct_rows_per_call"] * per_row + tpc * per_tok
+    g_bytes_all = res["lookups_per_call"] * per_row + tpc * per_tok
+    gather = {"kernel": gname, "bound": "hbm", "achieved": round(g_bytes / st[1] * 1e-3, 1), "peak": HBM_PEAK_GBS,
+              "unit": "GB/s", "frac": round(g_bytes / st[1] * 1e-3 / HBM_PEAK_GBS, 4),
+              "bytes_per_launch": int(g_bytes), "avg_us": round(float(st[1]), 2),
+              "median_us": round(float(res["stage_med_us"][1]), 2),
+              "distinct_rows_per_launch": res["distinct_rows_per_call"],
+              "lookups_per_launch": res["lookups_per_call"],
+              "achieved_counting_every_lookup": round(g_bytes_all / st[1] * 1e-3, 1),
+              "note": "bytes count each distinct row once; achieved_counting_every_lookup counts repeated "
+                      "rows again (those can be served from L2 or the Infinity Cache)"}
+    if "cold_stage_us" in res:
+        c = res["cold_stage_us"][1]
+        gather["cold"] = {"avg_us": round(float(c), 2), "achieved": round(g_bytes / c * 1e-3, 1),
+                          "frac": round(g_bytes / c * 1e-3 / HBM_PEAK_GBS, 4)}
+    flop = tpc * PROJ_FLOP_PER_TOKEN
+    if res["proj_kernel"] == "proj_small_kernel":
+        # a few tokens: the kernel streams W once; its bound is HBM
+        pb = W_BYTES + tpc * 4 * D
+        proj = {"kernel": res["proj_kernel"], "bound": "hbm", "achieved": round(pb / st[2] * 1e-3, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(pb / st[2] * 1e-3 / HBM_PEAK_GBS, 4),
+                "bytes_per_launch": int(pb), "avg_us": round(float(st[2]), 2),
+                "median_us": round(float(res["stage_med_us"][2]), 2)}
+    else:
+        tf = flop / st[2] * 1e-6
+        tf_med = flop / res["stage_med_us"][2] * 1e-6
+        proj = {"kernel": res["proj_kernel"], "bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4), "flop_per_launch": int(flop),
+                "avg_us": round(float(st[2]), 2), "median_us": round(float(res["stage_med_us"][2]), 2),
+                "frac_of_median": round(tf_med / BF16_PEAK_TFLOPS, 4),
+                "min_us": round(float(res["stage_min_us"][2]), 2),
+                "max_us": round(float(res["stage_max_us"][2]), 2)}
+    fb = tpc * FUSE_BYTES_PER_TOKEN
+    fuse = {"bound": "hbm", "achieved": round(fb / st[3] * 1e-3, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(fb / st[3] * 1e-3 / HBM_PEAK_GBS, 4), "bytes_per_launch": int(fb),
+            "avg_us": round(float(st[3]), 2), "median_us": round(float(res["stage_med_us"][3]), 2)}
+    dominant = int(np.argmax(st[1:])) + 1
+    roofline = dict([gather, proj, fuse][dominant - 1])
+    roofline["stage"] = ["gather", "proj", "fuse"][dominant - 1]
+    return gather, proj, fuse, roofline
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill", choices=["tiny", "decode", "prefill", "ragged", "long"])
+    ap.add_argument("--overlap", action="store_true",
+                    help="long workload: IDs and rows of the next chunk on a second stream (ple_forward_x)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture each step's calls into a HIP graph once and time graph replays")
+    ap.add_argument("--layout", default="two", choices=["two", "heads", "nvfp4"],
+                    help="two: 2 lookups of 2560-byte FP8 rows per token; heads: 16 lookups of 160-byte "
+                         "rows; nvfp4: 2 lookups of NVFP4 rows (E2M1 codes, E4M3 scale per 16 elements)")
+    ap.add_argument("--no-per-config", action="store_true", help="time only the selected workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--copy-ceiling", action="store_true",
+                    help="also time a plain device copy of the gather's output size (x bytes read, "
+                         "x bytes written) after a 1 GiB cache flush: the rate an HBM-bound kernel "
+                         "moving the gather's bytes could reach")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        sys.exit("bench.py measures one GPU: the path runs on a single MI355X (how it would shard "
+                 "across GPUs is described, not implemented), so --gpus must be 1")
+
+    import torch
+
+    import sparse_memory_gather_amd as ple
+    from gen import inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ple.load_library()
+    ctx = Context(dev)
+    name = args.workload
+    head = measure(ctx, name, args.layout, args.steps, args.warmup, overlap=args.overlap, graph=args.graph)
     result = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "metric": METRIC, "value": round(head["value"], 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["ms_per_step"], 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": describe(name, wl, args.layout) + (
+        "config": {"workload": head["workload"] + (
                        "; IDs and rows of the next chunk gathered on a second stream during the current one"
-                       if args.overlap and name == "long" else ""), "name": name, "layout": args.layout,
-                   "tokens_per_step": tokens_per_step,
-                   "sequences": wl.S, "table_rows": wl.R,
-                   "table_bytes": wl.R * (NVFP4_BYTES_PER_LOOKUP if nvfp4 else D + (64 if heads else 4))},
-        "roofline": roofline,
-        "stages_us": {"hash": round(float(stage_us[0]), 2), "gather": round(float(stage_us[1]), 2),
-                      "proj": round(float(stage_us[2]), 2), "fuse": round(float(stage_us[3]), 2)},
-        "stages_median_us": {k: round(float(v), 2) for k, v in zip(("hash", "gather", "proj", "fuse"),
-                                                                    stage_med_us)},
-        "gather": {"bound": "hbm", "achieved": round(gather_gbs, 1), "peak": HBM_PEAK_GBS,
-                   "unit": "GB/s", "frac": round(gather_gbs / HBM_PEAK_GBS, 4),
-                   "bytes_per_launch": gather_bytes, "lookups_per_launch": lookups,
-                   "unique_rows_per_launch": unique_rows,
-                   "traffic": recorded_traffic(gather_name, name)},
-        "gather_cold": None if cold_us is None else {
-            "avg_us": round(float(cold_us[1]), 2), "achieved": round(gather_bytes / (cold_us[1] * 1e-6) / 1e9, 1),
-            "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(gather_bytes / (cold_us[1] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-            "stages_us": {k: round(float(v), 2) for k, v in zip(("hash", "gather", "proj", "fuse"), cold_us)}},
-        "proj": {"kernel": proj_name, "bound": "mfma", "achieved": round(proj_tflops, 2),
-                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(proj_tflops / BF16_PEAK_TFLOPS, 4)},
-        "fuse": {"bound": "hbm", "achieved": round(fuse_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                 "frac": round(fuse_gbs / HBM_PEAK_GBS, 4)},
-        "cpu_baseline": None,
+                       if args.overlap and name == "long" else "") + (
+                       "; each step replayed from a captured HIP graph" if args.graph else ""),
+                   "name": name, "layout": args.layout, "tokens_per_step": head["tokens_per_step"],
+                   "sequences": head["S"], "table_rows": head["R"],
+                   "table_bytes": head["R"] * (NVFP4_BYTES_PER_ROW if args.layout == "nvfp4"
+                                               else D + (64 if args.layout == "heads" else 4))},
+        "gpu_ms_per_step": round(head["gpu_ms_per_step"], 4),
     }
-    if not args.no_cpu_baseline and h0 is not None:
+    if "stage_us" in head:
+        gather, proj, fuse, roofline = figures(head, args.layout)
+        roofline["traffic"] = recorded_traffic(roofline["kernel"], name)
+        gather["traffic"] = recorded_traffic(gather["kernel"], name)
+        result["roofline"] = roofline
+        result["stages_us"] = {k: round(float(v), 2) for k, v in zip(("hash", "gather", "proj", "fuse"),
+                                                                      head["stage_us"])}
+        result["stages_median_us"] = {k: round(float(v), 2) for k, v in zip(("hash", "gather", "proj", "fuse"),
+                                                                            head["stage_med_us"])}
+        result["gather"], result["proj"], result["fuse"] = gather, proj, fuse
+    result["cpu_baseline"] = None
+
+    if not args.no_per_config and name == "prefill" and not args.graph and not args.overlap:
+        # the other workloads in the same run, each with its own timed loop
+        per = {}
+        for wname, st, wu in PER_CONFIG:
+            r = measure(ctx, wname, args.layout, st, wu)
+            g, p, f, rf = figures(r, args.layout)
+            per[wname] = {"value": round(r["value"], 1), "unit": "tokens/s", "ms_per_step": round(r["ms_per_step"], 4),
+                          "gpu_ms_per_step": round(r["gpu_ms_per_step"], 4), "steps": st, "warmup": wu,
+                          "tokens_per_step": r["tokens_per_step"], "workload": r["workload"],
+                          "dominant": {k: rf[k] for k in ("stage", "kernel", "bound", "achieved", "peak", "unit",
+                                                          "frac") if k in rf},
+                          "stages_us": {k: round(float(v), 2) for k, v in
+                                        zip(("hash", "gather", "proj", "fuse"), r["stage_us"])},
+                          "gather": {k: g[k] for k in ("achieved", "frac", "cold", "distinct_rows_per_launch",
+                                                       "lookups_per_launch", "achieved_counting_every_lookup")
+                                     if k in g}}
+            if wname == "decode":
+                rg = measure(ctx, "decode", args.layout, st, wu, graph=True)
+                per[wname]["graph_replay"] = {"ms_per_step": round(rg["ms_per_step"], 4),
+                                              "gpu_ms_per_step": round(rg["gpu_ms_per_step"], 4),
+                                              "value": round(rg["value"], 1)}
+            ctx.drop_tables(inputs.R_FULL)
+        result["per_config"] = per
+
+    if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(wl, name, W, cw, h0, args.cpu_budget, args.layout)
-    elif not args.no_cpu_baseline:
-        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
-        h0 = wl.hidden(0)
-        result["cpu_baseline"] = cpu_baseline(wl, name, W, cw, h0, args.cpu_budget, args.layout)
+        wl = inputs.make_workload(name, decode_steps=1)
+        dev_table = ctx.table(wl.R, "two")[:2] if args.layout == "two" else None
+        result["cpu_baseline"] = cpu_baseline(wl, name, ctx.W, ctx.cw, wl.hidden(0), args.cpu_budget, args.layout,
+                                              dev_table)
     if args.copy_calibration:
         # a plain copy of known size: FETCH_SIZE / WRITE_SIZE of this dispatch
         # calibrate the per-kernel counters to bytes
@@ -490,7 +638,7 @@ def main():
         torch.cuda.synchronize()
         result["copy_calibration_bytes"] = 1 << 30
     if args.copy_ceiling:
-        nbytes = int(tokens_per_call) * 2560 * 2
+        nbytes = int(head["tokens_per_step"]) * 2560 * 2
         src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
