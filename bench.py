@@ -54,6 +54,7 @@ NVFP4_BYTES_PER_ROW = D // 2 + D // 16 + 4
 PROJ_FLOP_PER_TOKEN = 2 * D * D
 W_BYTES = D * D * 2
 FUSE_BYTES_PER_TOKEN = 3 * 2 * D
+STATE_BYTES_PER_SEQ = 3 * D * 4   # the carried conv state of one sequence (fp32)
 
 # the other workloads of the same run: (name, timed steps, warm-up steps)
 PER_CONFIG = (("tiny", 50, 10), ("decode", 64, 8), ("ragged", 20, 5), ("long", 4, 1))
@@ -475,6 +476,9 @@ def measure(ctx, name, layout, steps, warmup, overlap=False, graph=False, cold=T
     res["distinct_rows_per_call"] = float(np.mean(uniq))
     res["tokens_per_call"] = tokens_per_step / n_calls
     res["proj_kernel"] = ple.proj_tiling(int(res["tokens_per_call"]))
+    if layout == "two" and ple.one_launch(int(res["tokens_per_call"]), wl.S):
+        # the whole path is one kernel, timed in the projection stage
+        res["proj_kernel"] = "decode_step_kernel"
     del calls, batches, outs, ws, state
     torch.cuda.empty_cache()
     return res
@@ -506,7 +510,15 @@ def figures(res, layout):
         gather["cold"] = {"avg_us": round(float(c), 2), "achieved": round(g_bytes / c * 1e-3, 1),
                           "frac": round(g_bytes / c * 1e-3 / HBM_PEAK_GBS, 4)}
     flop = tpc * PROJ_FLOP_PER_TOKEN
-    if res["proj_kernel"] == "proj_small_kernel":
+    if res["proj_kernel"] == "decode_step_kernel":
+        # one launch for the whole path: W once, the distinct rows, and per
+        # token h in, out, and the carried conv state read and rewritten
+        pb = W_BYTES + res["distinct_rows_per_call"] * per_row + tpc * (4 * D + 2 * STATE_BYTES_PER_SEQ)
+        proj = {"kernel": res["proj_kernel"], "bound": "hbm", "achieved": round(pb / st[2] * 1e-3, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(pb / st[2] * 1e-3 / HBM_PEAK_GBS, 4),
+                "bytes_per_launch": int(pb), "avg_us": round(float(st[2]), 2),
+                "median_us": round(float(res["stage_med_us"][2]), 2)}
+    elif res["proj_kernel"] == "proj_small_kernel":
         # a few tokens: the kernel streams W once; its bound is HBM
         pb = W_BYTES + tpc * 4 * D
         proj = {"kernel": res["proj_kernel"], "bound": "hbm", "achieved": round(pb / st[2] * 1e-3, 1),

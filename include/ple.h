@@ -81,6 +81,8 @@ typedef enum ple_status {
 #define PLE_DEVERR_CU_SEQLENS 2   /* cu_seqlens[0] != 0, decreasing, or cu_seqlens[S] != T */
 #define PLE_DEVERR_HIST_LEN 4     /* hist_len[s] outside {0, 1, 2} (treated as 0) */
 #define PLE_DEVERR_ROW_RANGE 8    /* ple_lookup: a row id outside [-1, R) (treated as -1) */
+#define PLE_DEVERR_SYNC 16        /* one-launch path: its counters in the workspace were not zero at
+                                     the call, or a wait passed its limit (outputs unspecified) */
 
 /* a1 — n-gram row IDs (mengman page, "n-gram embedding" section: IDs from
  * token IDs, positions and sequence boundaries; reactapp page, "n-gram表格":
@@ -137,7 +139,8 @@ typedef struct ple_forward_args {
     int32_t* hist_ids;          /* int32 [S][2] in/out */
     int32_t* hist_len;          /* int32 [S] in/out */
     float* conv_state;          /* float [S][3][2560] in/out, last three v, oldest first; 16-byte aligned */
-    void* workspace;            /* device scratch, >= ple_forward_workspace_size(T, S) bytes, 256-byte aligned */
+    void* workspace;            /* device scratch, >= ple_forward_workspace_size(T, S) bytes, 256-byte aligned;
+                                   its first 256 bytes must be zero before the first call on it (see below) */
     size_t workspace_bytes;
     int32_t* dev_err;           /* optional */
     float eps;                  /* RMSNorm epsilon (>= 0), 1e-6 by convention */
@@ -151,15 +154,33 @@ typedef struct ple_forward_args {
 
 /* After the call: hist_ids/hist_len hold the last min(2, hist_len + L) IDs of
  * each sequence, conv_state the last three v (an empty sequence keeps its
- * state). Everything runs on `stream`; nothing is synchronized. */
+ * state). Everything runs on `stream`; nothing is synchronized.
+ *
+ * Short calls (ple_forward_one_launch(T, S): up to 16 tokens and 256
+ * sequences, out != h) run as ONE kernel launch: projection blocks and one
+ * finisher block per token, ordered through three counters in the first 256
+ * bytes of the workspace (decode steps split into separate launches cannot
+ * hide the table reads: mengman.github.io "Qwen3.8-Flash-Next 端侧部署 01",
+ * inference-flow section; kipfel.ltd Thor article, section "五、启动参数").
+ * Those bytes must be zero before the first call on a workspace; every call
+ * leaves them zero and no other kernel writes them, so clearing the buffer
+ * once when it is allocated suffices. Non-zero counters are flagged
+ * PLE_DEVERR_SYNC. Calls that share a workspace must be ordered (one stream),
+ * as for every other use of the workspace. Results equal the longer path's
+ * bit for bit. */
 int ple_forward(const ple_forward_args* args, void* stream);
+
+/* 1 if ple_forward runs a T-token call of S sequences (FP8 table, out != h)
+ * as one launch, else 0. Host-only, enqueues nothing. */
+int ple_forward_one_launch(int64_t T, int32_t S);
 
 /* ple_forward with per-stage timing: the same launches on the same stream,
  * with events[0..4] (hipEvent_t, created by the caller) recorded before the
  * n-gram ID kernel and after the ID, gather/dequant, projection and
  * gate/conv/fuse kernels. Calls of up to 1024 tokens compute the IDs inside
- * the gather, so events[0] and events[1] then bracket no kernel. events may
- * not be NULL. */
+ * the gather, so events[0] and events[1] then bracket no kernel; a
+ * one-launch call records events[0..2] before its kernel and events[3..4]
+ * after it. events may not be NULL. */
 int ple_forward_profiled(const ple_forward_args* args, void* stream, void* const* events);
 
 /* Workspace bytes ple_forward (and ple_forward_x) needs for up to max_T
@@ -268,7 +289,7 @@ int ple_proj_tiling(int64_t T);
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation. ple_forward_noalloc is ple_forward (same arguments, kernels and
  * results, bit for bit) with args->workspace NULL and args->workspace_bytes 0:
- * its workspace is a device array inside the library, 28,852,224 bytes on
+ * its workspace is a device array inside the library, 28,852,480 bytes on
  * each GPU it runs on, held until the process ends, enough for a call of up
  * to ple_forward_noalloc_max_tokens() = 2048 tokens and
  * ple_forward_noalloc_max_sequences() = 256 sequences. Larger calls return
@@ -277,8 +298,9 @@ int ple_proj_tiling(int64_t T);
  * address is looked up once per device, on the first call with that device
  * current). Every call on one GPU shares that GPU's array: calls that overlap
  * on one GPU (two streams, or two threads without ordering) race and give
- * unspecified results; calls ordered on one stream are safe. Nothing in the
- * array needs to start at zero. */
+ * unspecified results; calls ordered on one stream are safe. The array starts
+ * zeroed when the library is loaded, and the one-launch path's counters in
+ * it are left zero by every call. */
 int ple_forward_noalloc(const ple_forward_args* args, void* stream);
 size_t ple_forward_noalloc_max_tokens(void);
 size_t ple_forward_noalloc_max_sequences(void);

@@ -35,6 +35,7 @@ DEVERR_TOKEN_RANGE = 1
 DEVERR_CU_SEQLENS = 2
 DEVERR_HIST_LEN = 4
 DEVERR_ROW_RANGE = 8
+DEVERR_SYNC = 16
 
 
 class PLEError(RuntimeError):
@@ -65,7 +66,7 @@ EXPORTS = ("ple_hash", "ple_lookup", "ple_proj", "ple_forward", "ple_forward_pro
            "ple_forward_heads_profiled", "ple_forward_heads_workspace_size", "ple_forward_x",
            "ple_lookup_nvfp4", "ple_forward_nvfp4", "ple_forward_nvfp4_profiled",
            "ple_status_string", "ple_last_error", "ple_proj_tiling", "ple_forward_noalloc",
-           "ple_forward_noalloc_max_tokens", "ple_forward_noalloc_max_sequences")
+           "ple_forward_noalloc_max_tokens", "ple_forward_noalloc_max_sequences", "ple_forward_one_launch")
 HEADS = 16            # 16-lookup layout: head tables of 160-byte rows
 SLICE = D // HEADS
 
@@ -111,6 +112,8 @@ def load_library(path: str = LIB_PATH):
     lib.ple_last_error.restype = ctypes.c_char_p
     lib.ple_proj_tiling.argtypes = [I64]
     lib.ple_proj_tiling.restype = ctypes.c_int
+    lib.ple_forward_one_launch.argtypes = [I64, I32]
+    lib.ple_forward_one_launch.restype = ctypes.c_int
     lib.ple_forward_noalloc.argtypes = [ctypes.POINTER(ForwardArgs), _P]
     lib.ple_forward_noalloc.restype = ctypes.c_int
     for name in ("ple_forward_noalloc_max_tokens", "ple_forward_noalloc_max_sequences"):
@@ -126,6 +129,12 @@ PROJ_TILINGS = {0: None, 1: "proj_small_kernel", 2: "proj_mid_kernel", 3: "proj_
 def proj_tiling(T: int):
     """Name of the projection kernel a T-token forward runs (None for T <= 0)."""
     return PROJ_TILINGS[int(load_library().ple_proj_tiling(int(T)))]
+
+
+def one_launch(T: int, S: int) -> bool:
+    """Whether ple_forward runs a T-token call of S sequences (FP8 table,
+    out not h) as one kernel launch."""
+    return bool(load_library().ple_forward_one_launch(int(T), int(S)))
 
 
 def _check(status: int):
@@ -267,7 +276,9 @@ class State:
 
 class Workspace:
     """Caller-owned scratch for ple_forward, grown on demand (allocation
-    happens here, in torch, never inside libple)."""
+    happens here, in torch, never inside libple). Allocated zeroed: its first
+    256 bytes are the one-launch path's counters, which must be zero before
+    the first call (libple leaves them zero)."""
 
     def __init__(self, device="cuda"):
         self.device = device
@@ -276,7 +287,7 @@ class Workspace:
     def get(self, T: int, S: int, heads: bool = False) -> torch.Tensor:
         need = workspace_size(T, S, heads)
         if self.buf is None or self.buf.numel() < need:
-            self.buf = torch.empty((max(need, 256),), dtype=torch.uint8, device=self.device)
+            self.buf = torch.zeros((max(need, 256),), dtype=torch.uint8, device=self.device)
         return self.buf
 
 

@@ -17,7 +17,7 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libple.so")
 HIPCC = "/opt/rocm/bin/hipcc"
 
-SOURCES = ["ple_api.hip", "ple_hash.hip", "ple_gather.hip", "ple_proj.hip", "ple_fuse.hip"]
+SOURCES = ["ple_api.hip", "ple_hash.hip", "ple_gather.hip", "ple_proj.hip", "ple_fuse.hip", "ple_decode.hip"]
 
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           "-I", os.path.join(ROOT, "include"),

@@ -73,7 +73,7 @@ int check_alias(const Range* r, int n) {
 }
 
 struct WsLayout {
-    size_t row_ids, x, e16, snap, total;
+    size_t sync, row_ids, x, e16, snap, total;
 };
 
 constexpr size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -84,6 +84,9 @@ constexpr int ids_per_token(bool heads) { return heads ? 16 : 2; }
 constexpr WsLayout layout(int64_t T, int32_t S, bool heads) {
     WsLayout w{};
     size_t off = 0;
+    // counters of the one-launch path: zero before the first call on a
+    // workspace, left zero by every call; nothing else writes them
+    w.sync = off;    off = 256;
     w.row_ids = off; off = up256(off + (size_t)T * ids_per_token(heads) * sizeof(int32_t));
     w.x = off;       off = up256(off + (size_t)T * kD * 2);
     w.e16 = off;     off = up256(off + (size_t)T * kD * 2);
@@ -123,6 +126,8 @@ const char* ple_status_string(int status) {
 const char* ple_last_error(void) { return g_last_error.c_str(); }
 
 int ple_proj_tiling(int64_t T) { return ple::proj_tiling(T); }
+
+int ple_forward_one_launch(int64_t T, int32_t S) { return ple::decode_one_launch(T, S) ? 1 : 0; }
 
 size_t ple_forward_workspace_size(int64_t max_T, int32_t max_S) {
     if (max_T < 0 || max_S < 0) return 0;
@@ -325,6 +330,42 @@ static int forward_impl(const ple_forward_args* a, void* stream, void* const* ev
     auto mark = [&](int i) -> hipError_t {
         return events ? hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), s) : hipSuccess;
     };
+    if (!from_x && !heads && !nv_blocks && a->out != a->h && decode_one_launch(T, S)) {
+        // a short call: IDs, gather, projection and fuse in one launch (the
+        // profiling events then put the whole kernel in the projection stage)
+        DecodeArgs d{};
+        d.tokens = a->tokens;
+        d.T = T;
+        d.cu = a->cu_seqlens;
+        d.S = S;
+        d.vocab = a->vocab_size;
+        d.hist_ids = a->hist_ids;
+        d.hist_len = a->hist_len;
+        d.table = a->table;
+        d.scales = a->scales;
+        d.R = a->R;
+        d.W = a->W;
+        d.conv_w = a->conv_w;
+        d.h = a->h;
+        d.out = a->out;
+        d.conv_state = a->conv_state;
+        d.snap = snap;
+        d.e16 = e16;
+        d.sync = reinterpret_cast<uint32_t*>(ws + L.sync);
+        d.eps = a->eps;
+        d.dev_err = a->dev_err;
+        d.row_ids_out = a->row_ids_out;
+        d.x_out = a->x_out;
+        d.e_out = a->e_out;
+        d.gate_out = a->gate_out;
+        d.y_out = a->y_out;
+        for (int i = 0; i < 3; ++i)
+            if (int st = hip_status(mark(i), "ple_forward: event record")) return st;
+        if (int st = hip_status(launch_decode_step(d, s), "ple_forward: one-launch kernel")) return st;
+        for (int i = 3; i < 5; ++i)
+            if (int st = hip_status(mark(i), "ple_forward: event record")) return st;
+        return ok();
+    }
     hipError_t e = mark(0);
     if (int st = hip_status(e, "ple_forward: event record")) return st;
     // short calls: the gather computes the IDs (one launch instead of two;

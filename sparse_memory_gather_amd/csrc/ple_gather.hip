@@ -19,6 +19,7 @@
 //     slower). A gather run back to back with itself, as in an isolated
 //     timing loop, is the opposite case: each run then pays for the
 //     previous run's write-back, and non-temporal stores are faster.
+#include "ple_dequant.h"
 #include "ple_ngram.h"
 
 namespace ple {
@@ -26,20 +27,6 @@ namespace {
 
 constexpr int kTokPerBlock = 4;  // one wave per token
 constexpr int kSpans = kD / 512;  // 5
-
-// 8 FP8 codes of one row times its scale
-__device__ __forceinline__ void decode8(const u32x2& q, float s, float out[8]) {
-#pragma clang fp contract(off)
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-        f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[w], false);
-        f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[w], true);
-        out[4 * w + 0] = lo[0] * s;
-        out[4 * w + 1] = lo[1] * s;
-        out[4 * w + 2] = hi[0] * s;
-        out[4 * w + 3] = hi[1] * s;
-    }
-}
 
 // kIds (all three gathers): each wave computes its token's row IDs itself
 // (short calls: one launch instead of the ID kernel and the gather). The
@@ -108,18 +95,7 @@ gather_kernel(const int32_t* __restrict__ row_ids, int64_t T, const uint8_t* __r
     const float s1 = v1 ? scales[r1] : 0.0f;
     u32x4* xrow = reinterpret_cast<u32x4*>(x + t * kD) + lane;
 #pragma unroll
-    for (int s = 0; s < kSpans; ++s) {
-        float pa[8], pb[8], acc[8];
-        decode8(a[s], s0, pa);
-        decode8(b[s], s1, pb);
-        // a missing row contributes nothing (not even a signed zero)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = v0 ? (v1 ? pa[i] + pb[i] : pa[i]) : (v1 ? pb[i] : 0.0f);
-        u32x4 o;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
-        *(xrow + s * 64) = o;
-    }
+    for (int s = 0; s < kSpans; ++s) *(xrow + s * 64) = dequant_pair8(a[s], s0, v0, b[s], s1, v1);
     if (raw) {
         u32x2* d0 = reinterpret_cast<u32x2*>(raw + (t * 2 + 0) * kD) + lane;
         u32x2* d1 = reinterpret_cast<u32x2*>(raw + (t * 2 + 1) * kD) + lane;

@@ -103,4 +103,41 @@ hipError_t launch_fuse(const uint16_t* h, const uint16_t* e16, int64_t T, const 
                        int32_t* hist_len, uint16_t* out, float eps, float* gate_out, float* y_out,
                        uint16_t* h_copy, hipStream_t stream);  // h_copy: T x 2560 bf16 scratch, used when out == h
 
+// ---- the whole path of a short call in one launch (ple_decode.hip) ----------
+constexpr int kDecodeMaxT = 16;    // tokens: their x tile is staged in LDS (82 KB at 16)
+constexpr int kDecodeMaxS = 256;   // sequences: their metadata is staged in LDS
+
+struct DecodeArgs {
+    const int32_t* tokens;
+    int64_t T;
+    const int32_t* cu;
+    int32_t S;
+    int32_t vocab;
+    int32_t* hist_ids;           // in/out
+    int32_t* hist_len;           // in/out
+    const uint8_t* table;
+    const float* scales;
+    int64_t R;
+    uint64_t mod_R, mod_m;       // set by launch_decode_step
+    const uint16_t* W;
+    const uint16_t* conv_w;
+    const uint16_t* h;           // read only: out may not be h
+    uint16_t* out;
+    float* conv_state;
+    float* snap;                 // workspace: carried state of sequences spanning finishers
+    uint16_t* e16;               // workspace: bf16 e [T][kD]
+    uint32_t* sync;              // workspace: three counters, zero at the call, left zero
+    float eps;
+    int32_t* dev_err;
+    int32_t* row_ids_out;
+    uint16_t* x_out;
+    float* e_out;
+    float* gate_out;
+    float* y_out;
+};
+
+// whether a T-token call of S sequences (FP8 table, out != h) runs as one launch
+bool decode_one_launch(int64_t T, int32_t S);
+hipError_t launch_decode_step(DecodeArgs a, hipStream_t stream);
+
 }  // namespace ple

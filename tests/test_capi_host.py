@@ -61,11 +61,12 @@ def test_status_strings_and_workspace_size():
     lib = ple.load_library()
     assert lib.ple_status_string(0) == b"ok"
     assert lib.ple_status_string(-6) == b"workspace too small"
-    # workspace: row ids + x + e (bf16) + partial sums per token, conv-state copy per sequence
+    # workspace: the one-launch path's counters (256 bytes), row ids + x + e
+    # (bf16) per token, conv-state copy per sequence
     T, S = 1000, 3
     need = ple.workspace_size(T, S)
-    assert need >= T * (8 + 2560 * 2 * 2) + S * 3 * 2560 * 4
-    assert need % 256 == 0 and ple.workspace_size(0, 0) == 0
+    assert need >= 256 + T * (8 + 2560 * 2 * 2) + S * 3 * 2560 * 4
+    assert need % 256 == 0 and ple.workspace_size(0, 0) == 256
 
 
 # Every call below fails validation, so no kernel is launched; fake device

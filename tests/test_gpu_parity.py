@@ -870,3 +870,113 @@ def test_streaming_fuse_many_short_sequences(dev, small_table, dev_weights):
         assert np.array_equal(host_bits(one["out"]), whole_out[a:b]), (i, lengths[i])
         assert torch.equal(si.conv_state[0], st.conv_state[i]), (i, lengths[i])
         assert torch.equal(si.hist_ids[0], st.hist_ids[i]) and torch.equal(si.hist_len[0], st.hist_len[i])
+
+
+# ---------------------------------------------------------------------------
+# One launch for short calls (up to 16 tokens and 256 sequences, out != h):
+# projection blocks and one finisher per token, ordered by counters in the
+# workspace. An in-place call (out == h) takes the three-launch path.
+# ---------------------------------------------------------------------------
+
+ONE_LAUNCH_CASES = [
+    ([1] * 8, [2] * 8),                                     # a decode step
+    ([16], [0]),                                            # a fresh 16-token chunk
+    ([0, 1, 5, 2, 0, 4, 3, 1], [2, 1, 0, 2, 1, 2, 0, 1]),   # empty, short and longer sequences
+    ([1] * 14 + [0] * 186 + [2], [2] * 100 + [1] * 101),    # 201 sequences, most empty
+]
+
+
+@pytest.mark.parametrize("case", range(len(ONE_LAUNCH_CASES)))
+def test_one_launch_equals_three_launches(dev, small_table, dev_weights, case):
+    lengths, hls = ONE_LAUNCH_CASES[case]
+    tab, sc = small_table
+    toks, cu, hist, hlen, h = _case(700 + case, lengths, hls)
+    S, T = len(lengths), int(cu[-1])
+    assert ple.one_launch(T, S) and not ple.one_launch(17, S)
+    rng = np.random.default_rng(701 + case)
+    state0 = (0.4 * rng.standard_normal((S, 3, D))).astype(np.float32)
+    state0[np.array(hls) == 0] = 0.0
+
+    def fresh():
+        st = ple.State(S, dev)
+        st.hist_ids.copy_(dev_i32(hist, dev))
+        st.hist_len.copy_(dev_i32(hlen, dev))
+        st.conv_state.copy_(torch.from_numpy(state0).to(dev))
+        return st
+
+    ws = ple.Workspace(dev)
+    st1, st2, st3 = fresh(), fresh(), fresh()
+    one = _forward(dev, tab, sc, dev_weights, toks, cu, h, st1, workspace=ws)        # one launch, debug
+    h2 = dev_bf16(h, dev)
+    three = ple.ple_forward(dev_i32(toks, dev), dev_i32(cu, dev), tab, sc, dev_weights[0], dev_weights[1], h2,
+                            st2, out=h2, debug=True)                                    # in place: three launches
+    fast = _forward(dev, tab, sc, dev_weights, toks, cu, h, st3, debug=False, workspace=ws)
+    for k in ("row_ids", "x", "e", "gate", "y"):
+        assert torch.equal(one[k], three[k]), k
+    assert np.array_equal(host_bits(one["out"]), host_bits(h2))
+    assert np.array_equal(host_bits(fast), host_bits(h2))
+    for st in (st1, st3):
+        assert torch.equal(st.conv_state, st2.conv_state)
+        assert torch.equal(st.hist_ids, st2.hist_ids) and torch.equal(st.hist_len, st2.hist_len)
+    # every call leaves the counters at zero
+    torch.cuda.synchronize()
+    assert int(ws.buf[:256].to(torch.int32).abs().sum().item()) == 0
+
+
+def test_one_launch_against_oracle(dev, small_table, dev_weights, weights):
+    W, cw = weights
+    tab, sc = small_table
+    lengths, hls = ONE_LAUNCH_CASES[2]
+    toks, cu, hist, hlen, h = _case(710, lengths, hls)
+    S = len(lengths)
+    rng = np.random.default_rng(711)
+    state0 = (0.4 * rng.standard_normal((S, 3, D))).astype(np.float32)
+    st = ple.State(S, dev)
+    st.hist_ids.copy_(dev_i32(hist, dev))
+    st.hist_len.copy_(dev_i32(hlen, dev))
+    st.conv_state.copy_(torch.from_numpy(state0).to(dev))
+    res = _forward(dev, tab, sc, dev_weights, toks, cu, h, st)
+    ref = oracle.forward(toks, cu, h, W, cw, R_SMALL, rows, hist, hlen, state0.astype(np.float64))
+    got = gather_debug(res, np.arange(len(toks)))
+    assert np.array_equal(got["row_ids"], ref["row_ids"])
+    assert np.array_equal(got["x"], ref["x"])
+    assert np.all(np.abs(got["e"].astype(np.float64) - ref["e"]) <= E_REL * e_bound(ref["x"], W) + 1e-7)
+    assert np.all(np.abs(got["g"] - ref["g"]) <= gate_bound(ref, h, W))
+    s64 = state0.astype(np.float64)
+    assert np.all(np.abs(got["y"] - ref["y"]) <= y_bound(ref, cu, cw, s64, W, h))
+    out = inputs.bf16_bits_to_f32(got["out"]).astype(np.float64)
+    assert np.all(np.abs(out - ref["out"]) <= OUT_ATOL + OUT_RTOL * np.abs(ref["out"]))
+    assert np.array_equal(st.hist_len.cpu().numpy(), ref["hist_len"])
+    hid = st.hist_ids.cpu().numpy()
+    for s in range(S):
+        k = ref["hist_len"][s]
+        assert np.array_equal(hid[s][2 - k:], ref["hist_ids"][s][2 - k:]), s
+    assert np.all(np.abs(st.conv_state.cpu().numpy() - ref["conv_state"]) <= state_bound(ref, cu, cw, W, h))
+    assert np.array_equal(st.conv_state[0].cpu().numpy(), state0[0])        # empty sequence untouched
+
+
+def test_one_launch_flags_a_workspace_whose_counters_are_not_zero(dev, small_table, dev_weights):
+    # a ticket counter far past the grid: every block takes a ticket beyond
+    # its roles and exits at once, flagging PLE_DEVERR_SYNC (nothing waits)
+    tab, sc = small_table
+    toks, cu, hist, hlen, h = _case(720, [1] * 8, [2] * 8)
+    ws = ple.Workspace(dev)
+    ws.get(8, 8)
+    ws.buf[:4].view(torch.int32).fill_(1000)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    ple.ple_forward(dev_i32(toks, dev), dev_i32(cu, dev), tab, sc, dev_weights[0], dev_weights[1],
+                    dev_bf16(h, dev), ple.State(8, dev), workspace=ws, dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & ple.DEVERR_SYNC
+    # cleared again, the same workspace serves a normal call
+    ws.buf[:256].zero_()
+    err.zero_()
+    st_a, st_b = ple.State(8, dev), ple.State(8, dev)
+    a = ple.ple_forward(dev_i32(toks, dev), dev_i32(cu, dev), tab, sc, dev_weights[0], dev_weights[1],
+                        dev_bf16(h, dev), st_a, workspace=ws, dev_err=err)
+    h2 = dev_bf16(h, dev)
+    ple.ple_forward(dev_i32(toks, dev), dev_i32(cu, dev), tab, sc, dev_weights[0], dev_weights[1], h2, st_b,
+                    out=h2)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert np.array_equal(host_bits(a), host_bits(h2))
