@@ -279,7 +279,7 @@ class Context:
         torch.cuda.empty_cache()
 
 
-def measure(ctx, name, layout, steps, warmup, overlap=False, graph=False, cold=True):
+def measure(ctx, name, layout, steps, warmup, overlap=False, graph=False, cold=True, warmup_ms=100.0):
     """Time `steps` steps of workload `name` after `warmup` steps. Returns the
     workload's figures: tokens/s from wall time and from events around the
     timed loop, per-stage averages and medians from a second pass with
@@ -292,6 +292,7 @@ def measure(ctx, name, layout, steps, warmup, overlap=False, graph=False, cold=T
 
     dev, hev = ctx.dev, ctx.hev
     wl = inputs.make_workload(name, decode_steps=max(1, steps + warmup))
+    n_batches = len(wl.chunks)
     heads, nvfp4 = layout == "heads", layout == "nvfp4"
     tab, sc, blocks = ctx.table(wl.R, layout)
     Wd, cwd, bf16 = ctx.Wd, ctx.cwd, ctx.bf16
@@ -393,10 +394,17 @@ def measure(ctx, name, layout, steps, warmup, overlap=False, graph=False, cold=T
         def step(k):
             eager_step(k)
 
-    print(f"[bench] {name}: warmup {warmup}, timing {steps} steps", file=sys.stderr, flush=True)
-    for k in range(warmup):
-        step(k)
-    torch.cuda.synchronize()
+    # warm-up: at least `warmup` steps, and at least warmup_ms of GPU work
+    # since the last idle period: from idle the clocks take some 10-20 ms to
+    # ramp up, and a timed loop started earlier measures the ramp
+    n_warm, t_warm = 0, time.perf_counter()
+    while n_warm < warmup or (time.perf_counter() - t_warm) * 1e3 < warmup_ms:
+        for _ in range(max(warmup, 1)):
+            step(n_warm)
+            n_warm += 1
+        torch.cuda.synchronize()
+    warmup = n_warm
+    print(f"[bench] {name}: {warmup} warm-up steps, timing {steps} steps", file=sys.stderr, flush=True)
     loop_ev = hev.create(2)
     t0 = time.perf_counter()
     hev.record(loop_ev[0], stream)
@@ -406,7 +414,7 @@ def measure(ctx, name, layout, steps, warmup, overlap=False, graph=False, cold=T
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = hev.elapsed_ms(loop_ev[0], loop_ev[1])
-    res = {"name": name, "layout": layout, "steps": steps, "warmup": warmup,
+    res = {"name": name, "layout": layout, "steps": steps, "warmup": warmup, "n_batches": n_batches,
            "tokens_per_step": tokens_per_step, "ms_per_step": 1e3 * wall / steps,
            "value": tokens_per_step * steps / wall, "gpu_ms_per_step": gpu_ms / steps,
            "workload": describe(name, wl, layout), "S": wl.S, "R": wl.R, "graph": graph}
@@ -509,6 +517,13 @@ def figures(res, layout):
         c = res["cold_stage_us"][1]
         gather["cold"] = {"avg_us": round(float(c), 2), "achieved": round(g_bytes / c * 1e-3, 1),
                           "frac": round(g_bytes / c * 1e-3 / HBM_PEAK_GBS, 4)}
+    if res["proj_kernel"] == "decode_step_kernel":
+        # no gather kernel: the rows are read inside the one launch, whose
+        # time the projection stage carries (the gather stage's events
+        # bracket nothing but their own records)
+        gather = {"kernel": None, "note": "rows read inside decode_step_kernel (one launch)",
+                  "distinct_rows_per_launch": res["distinct_rows_per_call"],
+                  "lookups_per_launch": res["lookups_per_call"]}
     flop = tpc * PROJ_FLOP_PER_TOKEN
     if res["proj_kernel"] == "decode_step_kernel":
         # one launch for the whole path: W once, the distinct rows, and per
@@ -547,8 +562,11 @@ def figures(res, layout):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps before the timed loop (at least; see --warmup-ms)")
+    ap.add_argument("--warmup-ms", type=float, default=100.0,
+                    help="keep warming up until this much GPU work has run, so that the clocks have ramped up")
     ap.add_argument("--workload", default="prefill", choices=["tiny", "decode", "prefill", "ragged", "long"])
     ap.add_argument("--overlap", action="store_true",
                     help="long workload: IDs and rows of the next chunk on a second stream (ple_forward_x)")
@@ -582,10 +600,11 @@ def main():
     ple.load_library()
     ctx = Context(dev)
     name = args.workload
-    head = measure(ctx, name, args.layout, args.steps, args.warmup, overlap=args.overlap, graph=args.graph)
+    head = measure(ctx, name, args.layout, args.steps, args.warmup, overlap=args.overlap, graph=args.graph,
+                   warmup_ms=args.warmup_ms)
     result = {
         "metric": METRIC, "value": round(head["value"], 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["ms_per_step"], 4),
+        "steps": args.steps, "warmup": head["warmup"], "ms_per_step": round(head["ms_per_step"], 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": head["workload"] + (
@@ -614,20 +633,20 @@ def main():
         # the other workloads in the same run, each with its own timed loop
         per = {}
         for wname, st, wu in PER_CONFIG:
-            r = measure(ctx, wname, args.layout, st, wu)
+            r = measure(ctx, wname, args.layout, st, wu, warmup_ms=args.warmup_ms)
             g, p, f, rf = figures(r, args.layout)
             per[wname] = {"value": round(r["value"], 1), "unit": "tokens/s", "ms_per_step": round(r["ms_per_step"], 4),
-                          "gpu_ms_per_step": round(r["gpu_ms_per_step"], 4), "steps": st, "warmup": wu,
+                          "gpu_ms_per_step": round(r["gpu_ms_per_step"], 4), "steps": st, "warmup": r["warmup"],
                           "tokens_per_step": r["tokens_per_step"], "workload": r["workload"],
                           "dominant": {k: rf[k] for k in ("stage", "kernel", "bound", "achieved", "peak", "unit",
                                                           "frac") if k in rf},
                           "stages_us": {k: round(float(v), 2) for k, v in
                                         zip(("hash", "gather", "proj", "fuse"), r["stage_us"])},
                           "gather": {k: g[k] for k in ("achieved", "frac", "cold", "distinct_rows_per_launch",
-                                                       "lookups_per_launch", "achieved_counting_every_lookup")
-                                     if k in g}}
+                                                       "lookups_per_launch", "achieved_counting_every_lookup",
+                                                       "note") if k in g}}
             if wname == "decode":
-                rg = measure(ctx, "decode", args.layout, st, wu, graph=True)
+                rg = measure(ctx, "decode", args.layout, st, wu, graph=True, warmup_ms=args.warmup_ms)
                 per[wname]["graph_replay"] = {"ms_per_step": round(rg["ms_per_step"], 4),
                                               "gpu_ms_per_step": round(rg["gpu_ms_per_step"], 4),
                                               "value": round(rg["value"], 1)}
