@@ -25,7 +25,9 @@
  *  - x = bf16_rne(fl32(fl32(dec(code_r2)*scale[r2]) + fl32(dec(code_r3)*scale[r3])))
  *    with dec = OCP FP8 E4M3FN decode and one fp32 scale per row.
  *  - e = bf16_rne(x W^T), W bf16 [2560 out][2560 in], fp32 accumulation: the
- *    projection is a bf16 layer, and the gate and the conv read its bf16 output.
+ *    projection is a bf16 layer (outside the routed experts the model's
+ *    weights are BF16, the table FP8: bittide model card copy, "模型简介"),
+ *    and the gate and the conv read its bf16 output.
  *  - g = sigmoid(<h/rms(h), e/rms(e)> / sqrt(2560)), rms(z) = sqrt(mean(z^2) + eps).
  *  - v = g e; y[t][c] = sum_{k=0..3} conv_w[c][k] v[t-3+k][c] (causal,
  *    depthwise, conv_w[c][3] on the current token, v before a sequence's

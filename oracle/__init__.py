@@ -40,7 +40,9 @@ import numpy as np
 
 D = 2560
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB = os.path.join(_HERE, "libple_oracle.so")
+# PLE_ORACLE_LIB: another build of the same source (the sanitizer run loads
+# the UBSan build through it)
+LIB = os.environ.get("PLE_ORACLE_LIB") or os.path.join(_HERE, "libple_oracle.so")
 _lib = None
 
 _P = ctypes.c_void_p
@@ -258,7 +260,9 @@ def forward(tokens, cu_seqlens, h_bf16, W_bf16, conv_w_bf16, R: int, row_source,
             hist_ids=None, hist_len=None, conv_state=None, eps: float = 1e-6):
     """One chunk through the whole path. Returns a dict with row_ids, x, e
     (the exact projection, fp64), e_b (its bf16 rounding: the projection's
-    output tensor, which the gate and the conv consume), g, y, out (fp64,
+    output tensor, which the gate and the conv consume; outside the routed
+    experts the model's weights are BF16, bittide model card copy,
+    "模型简介"), g, y, out (fp64,
     unrounded), and the new hist_ids / hist_len / conv_state (conv_state kept
     in fp64 so chained chunks equal one long chunk)."""
     tokens = _c(tokens, np.int32)

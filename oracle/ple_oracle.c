@@ -22,9 +22,11 @@
  *    history at a sequence start) has row -1 and contributes zero.
  *  - x = bf16_rne( fl32( fl32(dec(code_bi)*s_bi) + fl32(dec(code_tri)*s_tri) ) ),
  *    E4M3FN decode, one fp32 scale per row.
- *  - e = x W^T (W[out][in]), fp64 here; the projection is a bf16 layer, so
- *    its output is the bf16 tensor e_b = bf16_rne(e) (one rounding from the
- *    exact value), and the gate and the conv below act on e_b.
+ *  - e = x W^T (W[out][in]), fp64 here. Outside the routed experts the
+ *    model's weights are BF16 and only the table is FP8 (bittide model card
+ *    copy, "模型简介"), so the projection is a bf16 layer whose output is the
+ *    bf16 tensor e_b = bf16_rne(e) (one rounding from the exact value); the
+ *    gate and the conv below act on e_b.
  *  - g = sigmoid( <h/rms(h), e_b/rms(e_b)> / sqrt(2560) ), rms(z) = sqrt(mean(z^2)+eps).
  *  - v = g e_b; y[t][c] = sum_{k=0..3} w[c][k] v[t-3+k][c] (causal depthwise,
  *    w[c][3] on the current token; v before a sequence start comes from the
