@@ -213,10 +213,12 @@ proj_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __restric
                                j * 32 + fr);
     }
     if (kFwd) {
-        // the wave's own LDS writes are complete before its reads (in-order LDS
-        // queue per wave); each store instruction writes four 256-byte token
-        // rows. Plain stores leave e in the memory-side cache for the fuse
-        // kernel, which reads it next.
+        // the lanes read staging rows other lanes of the wave wrote: a
+        // wave-scope fence orders those LDS writes before the reads. Each
+        // store instruction writes four 256-byte token rows; plain stores
+        // leave e in the memory-side cache for the fuse kernel, which reads
+        // it next.
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         const int c = lane & 15;
 #pragma unroll 4
         for (int q = 0; q < 16; ++q) {
