@@ -59,17 +59,18 @@ STATE_BYTES_PER_SEQ = 3 * D * 4   # the carried conv state of one sequence (fp32
 # the other workloads of the same run: (name, timed steps, warm-up steps)
 PER_CONFIG = (("tiny", 50, 10), ("decode", 64, 8), ("ragged", 20, 5), ("long", 4, 1))
 
+_CSRC = "sparse_memory_gather_amd/csrc/"
+_PROJ_SRC = [_CSRC + f for f in ("ple_proj.hip", "ple_kernels.h")]
+_GATHER_SRC = [_CSRC + f for f in ("ple_gather.hip", "ple_dequant.h", "ple_ngram.h", "ple_kernels.h")]
+_FUSE_SRC = [_CSRC + f for f in ("ple_fuse.hip", "ple_fuse_common.h", "ple_ngram.h", "ple_kernels.h")]
+_DECODE_SRC = [_CSRC + f for f in ("ple_decode.hip", "ple_dequant.h", "ple_fuse_common.h", "ple_ngram.h",
+                                   "ple_kernels.h")]
+# every file a kernel is compiled from: a recorded traffic figure holds only
+# while their contents are unchanged
 KERNEL_SOURCES = {
-    "proj_kernel": ["sparse_memory_gather_amd/csrc/ple_proj.hip", "sparse_memory_gather_amd/csrc/ple_kernels.h"],
-    "proj_w320_kernel": ["sparse_memory_gather_amd/csrc/ple_proj.hip",
-                         "sparse_memory_gather_amd/csrc/ple_kernels.h"],
-    "gather_kernel": ["sparse_memory_gather_amd/csrc/ple_gather.hip", "sparse_memory_gather_amd/csrc/ple_kernels.h"],
-    "gather_heads_kernel": ["sparse_memory_gather_amd/csrc/ple_gather.hip",
-                            "sparse_memory_gather_amd/csrc/ple_kernels.h"],
-    "gather_nvfp4_kernel": ["sparse_memory_gather_amd/csrc/ple_gather.hip",
-                            "sparse_memory_gather_amd/csrc/ple_kernels.h"],
-    "fuse_stream_kernel": ["sparse_memory_gather_amd/csrc/ple_fuse.hip",
-                           "sparse_memory_gather_amd/csrc/ple_kernels.h"],
+    "proj_kernel": _PROJ_SRC, "proj_w320_kernel": _PROJ_SRC,
+    "gather_kernel": _GATHER_SRC, "gather_heads_kernel": _GATHER_SRC, "gather_nvfp4_kernel": _GATHER_SRC,
+    "fuse_stream_kernel": _FUSE_SRC, "decode_step_kernel": _DECODE_SRC,
 }
 
 
@@ -492,6 +493,66 @@ def measure(ctx, name, layout, steps, warmup, overlap=False, graph=False, cold=T
     return res
 
 
+def copy_ceiling(dev, total_bytes, reps=12):
+    """A plain device copy moving `total_bytes` (half read, half written),
+    timed like the gather: a 1 GiB read before each copy evicts the caches,
+    and events bracket the one launch. The like-for-like ceiling for an
+    HBM-bound kernel of that size measured that way."""
+    import torch
+    n = max(1, int(total_bytes) // 2)
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.empty(reps, dtype=torch.uint8, device=dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for k in range(reps):
+        torch.amax(flush, dim=0, out=sink[k])
+        ev[k][0].record()
+        dst.copy_(src)
+        ev[k][1].record()
+    torch.cuda.synchronize()
+    us = [a.elapsed_time(b) * 1e3 for a, b in ev[2:]]
+    avg = sum(us) / len(us)
+    del src, dst, flush, sink
+    return {"bytes": 2 * n, "avg_us": round(avg, 2), "achieved": round(2 * n / avg * 1e-3, 1), "unit": "GB/s",
+            "frac": round(2 * n / avg * 1e-3 / HBM_PEAK_GBS, 4), "kernel": "torch copy_ (uint8, contiguous)"}
+
+
+def vendor_gemm(dev, T, reps=20):
+    """The projection's product through torch (hipBLASLt on ROCm): bf16
+    x [T][2560] times W^T as a contiguous [2560][2560] operand, bf16 out,
+    events around each call, after a warm-up. A reference point for the MFMA
+    kernel on the same shape, not part of the path."""
+    import torch
+    g = torch.Generator(device=dev).manual_seed(7)
+    x = torch.randn((T, D), device=dev, generator=g).to(torch.bfloat16)
+    wt = (torch.randn((D, D), device=dev, generator=g) * D ** -0.5).to(torch.bfloat16).contiguous()
+    out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    for _ in range(5):
+        torch.mm(x, wt, out=out)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        torch.mm(x, wt, out=out)
+        b.record()
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    avg = sum(us) / len(us)
+    tf = T * PROJ_FLOP_PER_TOKEN / avg * 1e-6
+    del x, wt, out
+    return {"op": "torch.mm bf16 (hipBLASLt)", "tokens": T, "avg_us": round(avg, 2),
+            "median_us": round(us[len(us) // 2], 2), "achieved": round(tf, 2), "unit": "TFLOP/s",
+            "frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+
+
+def stage_table(res, key="stage_us"):
+    """Per-stage durations (us) of a measure() result; a one-launch step has
+    one stage, timed by the events around its timed loop."""
+    if res["proj_kernel"] == "decode_step_kernel":
+        return {"decode_step_kernel": round(1e3 * res["gpu_ms_per_step"], 2)}
+    return {k: round(float(v), 2) for k, v in zip(("hash", "gather", "proj", "fuse"), res[key])}
+
+
 def figures(res, layout):
     """Rooflines and rates from a measure() result."""
     tpc = res["tokens_per_call"]
@@ -527,12 +588,17 @@ def figures(res, layout):
     flop = tpc * PROJ_FLOP_PER_TOKEN
     if res["proj_kernel"] == "decode_step_kernel":
         # one launch for the whole path: W once, the distinct rows, and per
-        # token h in, out, and the carried conv state read and rewritten
+        # token h in, out, and the carried conv state read and rewritten. A
+        # step is that one launch, so the events around the timed loop give
+        # its duration (launch gaps included); events around a single launch
+        # would add their own records' cost to a ~20 us kernel
         pb = W_BYTES + res["distinct_rows_per_call"] * per_row + tpc * (4 * D + 2 * STATE_BYTES_PER_SEQ)
-        proj = {"kernel": res["proj_kernel"], "bound": "hbm", "achieved": round(pb / st[2] * 1e-3, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(pb / st[2] * 1e-3 / HBM_PEAK_GBS, 4),
-                "bytes_per_launch": int(pb), "avg_us": round(float(st[2]), 2),
-                "median_us": round(float(res["stage_med_us"][2]), 2)}
+        us = 1e3 * res["gpu_ms_per_step"]
+        proj = {"kernel": res["proj_kernel"], "bound": "hbm", "achieved": round(pb / us * 1e-3, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(pb / us * 1e-3 / HBM_PEAK_GBS, 4),
+                "bytes_per_launch": int(pb), "avg_us": round(us, 2),
+                "timing": "events around the timed loop of one-launch steps",
+                "events_around_one_launch_us": round(float(st[2]), 2)}
     elif res["proj_kernel"] == "proj_small_kernel":
         # a few tokens: the kernel streams W once; its bound is HBM
         pb = W_BYTES + tpc * 4 * D
@@ -553,6 +619,11 @@ def figures(res, layout):
     fuse = {"bound": "hbm", "achieved": round(fb / st[3] * 1e-3, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(fb / st[3] * 1e-3 / HBM_PEAK_GBS, 4), "bytes_per_launch": int(fb),
             "avg_us": round(float(st[3]), 2), "median_us": round(float(res["stage_med_us"][3]), 2)}
+    if res["proj_kernel"] == "decode_step_kernel":
+        fuse = {"kernel": None, "note": "gate, conv and residual add inside decode_step_kernel (one launch)"}
+        roofline = dict(proj)
+        roofline["stage"] = "whole step"
+        return gather, proj, fuse, roofline
     dominant = int(np.argmax(st[1:])) + 1
     roofline = dict([gather, proj, fuse][dominant - 1])
     roofline["stage"] = ["gather", "proj", "fuse"][dominant - 1]
@@ -580,10 +651,6 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
-    ap.add_argument("--copy-ceiling", action="store_true",
-                    help="also time a plain device copy of the gather's output size (x bytes read, "
-                         "x bytes written) after a 1 GiB cache flush: the rate an HBM-bound kernel "
-                         "moving the gather's bytes could reach")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -622,10 +689,12 @@ def main():
         roofline["traffic"] = recorded_traffic(roofline["kernel"], name)
         gather["traffic"] = recorded_traffic(gather["kernel"], name)
         result["roofline"] = roofline
-        result["stages_us"] = {k: round(float(v), 2) for k, v in zip(("hash", "gather", "proj", "fuse"),
-                                                                      head["stage_us"])}
-        result["stages_median_us"] = {k: round(float(v), 2) for k, v in zip(("hash", "gather", "proj", "fuse"),
-                                                                            head["stage_med_us"])}
+        result["stages_us"] = stage_table(head)
+        result["stages_median_us"] = stage_table(head, "stage_med_us")
+        if gather.get("kernel"):
+            gather["copy_same_bytes"] = copy_ceiling(dev, gather["bytes_per_launch"])
+        if proj.get("bound") == "mfma":
+            proj["vendor_gemm_same_shape"] = vendor_gemm(dev, int(head["tokens_per_call"]))
         result["gather"], result["proj"], result["fuse"] = gather, proj, fuse
     result["cpu_baseline"] = None
 
@@ -638,13 +707,15 @@ def main():
             per[wname] = {"value": round(r["value"], 1), "unit": "tokens/s", "ms_per_step": round(r["ms_per_step"], 4),
                           "gpu_ms_per_step": round(r["gpu_ms_per_step"], 4), "steps": st, "warmup": r["warmup"],
                           "tokens_per_step": r["tokens_per_step"], "workload": r["workload"],
-                          "dominant": {k: rf[k] for k in ("stage", "kernel", "bound", "achieved", "peak", "unit",
-                                                          "frac") if k in rf},
-                          "stages_us": {k: round(float(v), 2) for k, v in
-                                        zip(("hash", "gather", "proj", "fuse"), r["stage_us"])},
+                          "dominant": dict({k: rf[k] for k in ("stage", "kernel", "bound", "achieved", "peak",
+                                                               "unit", "frac") if k in rf},
+                                           traffic=recorded_traffic(rf["kernel"], wname)),
+                          "stages_us": stage_table(r),
                           "gather": {k: g[k] for k in ("achieved", "frac", "cold", "distinct_rows_per_launch",
                                                        "lookups_per_launch", "achieved_counting_every_lookup",
                                                        "note") if k in g}}
+            if g.get("kernel"):
+                per[wname]["gather"]["copy_same_bytes"] = copy_ceiling(dev, g["bytes_per_launch"])
             if wname == "decode":
                 rg = measure(ctx, "decode", args.layout, st, wu, graph=True, warmup_ms=args.warmup_ms)
                 per[wname]["graph_replay"] = {"ms_per_step": round(rg["ms_per_step"], 4),
@@ -668,25 +739,6 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         result["copy_calibration_bytes"] = 1 << 30
-    if args.copy_ceiling:
-        nbytes = int(head["tokens_per_step"]) * 2560 * 2
-        src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
-        sink = torch.empty(12, dtype=torch.uint8, device=dev)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(12)]
-        for k in range(12):
-            torch.amax(flush, dim=0, out=sink[k])
-            ev[k][0].record()
-            dst.copy_(src)
-            ev[k][1].record()
-        torch.cuda.synchronize()
-        us = [a.elapsed_time(b) * 1e3 for a, b in ev[2:]]
-        avg = sum(us) / len(us)
-        result["copy_ceiling"] = {"bytes": 2 * nbytes, "avg_us": round(avg, 2),
-                                  "achieved": round(2 * nbytes / avg * 1e-3, 1), "unit": "GB/s",
-                                  "kernel": "torch copy_ (uint8, contiguous)"}
-        del src, dst, flush, sink
     print(json.dumps(result), flush=True)
 
 
