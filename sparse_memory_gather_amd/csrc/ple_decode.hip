@@ -105,42 +105,53 @@ decode_step_kernel(const DecodeArgs a) {
             const ModR mr{a.mod_R, a.mod_m};
             s_rows[tid] = make_int2(bigram_row(k, mr), trigram_row(k, mr));
         }
-        __syncthreads();
-        // x of every token into LDS, 8 elements per piece (the gather's
-        // device code): consecutive threads read consecutive 8-byte pieces of
-        // a row, all loads in flight before the first conversion
-        constexpr int kPieces = kDecodeMaxT * (kD / 8) / fuse::kThreads;  // per thread, at most
-        u32x2 ca[kPieces], cb[kPieces];
-        float sa[kPieces], sb[kPieces];
-#pragma unroll
-        for (int j = 0; j < kPieces; ++j) {
-            const int c = tid + j * fuse::kThreads;
-            const int t = c / (kD / 8), k8 = (c % (kD / 8)) * 8;
-            const int2 r = c < T * (kD / 8) ? s_rows[t] : make_int2(-1, -1);
-            const u32x2 z = {0u, 0u};
-            ca[j] = r.x >= 0 ? *reinterpret_cast<const u32x2*>(a.table + (int64_t)r.x * kD + k8) : z;
-            cb[j] = r.y >= 0 ? *reinterpret_cast<const u32x2*>(a.table + (int64_t)r.y * kD + k8) : z;
-            sa[j] = r.x >= 0 ? a.scales[r.x] : 0.0f;
-            sb[j] = r.y >= 0 ? a.scales[r.y] : 0.0f;
-        }
-        // then the W fragments, needed only when this wave's turn in the k
-        // chain comes. Each of these loads touches 32 rows of W, so a block's
-        // 160 KB keep the CU's address unit busy for microseconds: issued
-        // before the rows, they would hold the rows (and the x tile waiting
-        // for them) behind
+        // the W fragments: wave 0 computes the IDs first, the other waves
+        // issue these at once. Each load touches 32 rows of W, so a block's
+        // 160 KB keep the CU's address unit busy for microseconds; the barrier
+        // below (which waits for LDS operations, not for loads in flight)
+        // takes most of that time, and the row loads after it do not queue
+        // behind W
         const bool wrow = fr < kRowsPerBlock;   // MFMA rows past the block's features are zero
         const uint16_t* wp = a.W + (int64_t)(f0 + (wrow ? fr : 0)) * kD + k0;
         bf16x8 fa[kSteps];
 #pragma unroll
         for (int q = 0; q < kSteps; ++q) fa[q] = wrow ? *reinterpret_cast<const bf16x8*>(wp + q * 16) : zero;
+        __syncthreads();
+        // x of every token into LDS, 8 elements per piece (the gather's
+        // device code): consecutive threads read consecutive 8-byte pieces of
+        // a row, all loads in flight before the first conversion
+        constexpr int kPieces = kDecodeMaxT * (kD / 8) / fuse::kThreads;  // per thread, at most
+        const int n_pieces = T * (kD / 8);
+        u32x2 ca[kPieces], cb[kPieces];
+        float sa[kPieces], sb[kPieces];
+        bool va[kPieces], vb[kPieces];
+#pragma unroll
+        for (int j = 0; j < kPieces; ++j) {
+            if (j * fuse::kThreads < n_pieces) {   // the same for every thread of the block
+                const int c = tid + j * fuse::kThreads;
+                const bool in = c < n_pieces;
+                const int t = in ? c / (kD / 8) : 0, k8 = (c % (kD / 8)) * 8;
+                const int2 r = s_rows[t];
+                va[j] = in && r.x >= 0;
+                vb[j] = in && r.y >= 0;
+                // loads under a per-lane condition would need their values at
+                // once (to merge with the zeros of the other lanes), and the
+                // loads issued before them would be waited for too; row 0
+                // stands in for a missing row instead, and the dequant drops
+                // its bytes
+                const int64_t rx = r.x >= 0 ? r.x : 0, ry = r.y >= 0 ? r.y : 0;
+                ca[j] = *reinterpret_cast<const u32x2*>(a.table + rx * kD + k8);
+                cb[j] = *reinterpret_cast<const u32x2*>(a.table + ry * kD + k8);
+                sa[j] = a.scales[rx];
+                sb[j] = a.scales[ry];
+            }
+        }
 #pragma unroll
         for (int j = 0; j < kPieces; ++j) {
             const int c = tid + j * fuse::kThreads;
-            if (c < T * (kD / 8)) {
+            if (j * fuse::kThreads < n_pieces && c < n_pieces) {
                 const int t = c / (kD / 8), k8 = (c % (kD / 8)) * 8;
-                const int2 r = s_rows[t];
-                *reinterpret_cast<u32x4*>(x_s + t * kXRow + k8) =
-                    dequant_pair8(ca[j], sa[j], r.x >= 0, cb[j], sb[j], r.y >= 0);
+                *reinterpret_cast<u32x4*>(x_s + t * kXRow + k8) = dequant_pair8(ca[j], sa[j], va[j], cb[j], sb[j], vb[j]);
             }
         }
         __syncthreads();
