@@ -11,10 +11,10 @@
 // takes when it starts (an atomic counter in the caller's workspace):
 //   - tickets 0 .. kProj-1: projection block p computes e for features
 //     32p .. 32p+31 of every token (all 32 A rows of the MFMA). It computes
-//     the tokens' row IDs once (the ID kernel's device code), loads the
-//     rows with coalesced reads and then its W fragments, dequantizes all
-//     of x into an LDS tile (the gather's device code) while W is in
-//     flight, and runs proj_small_kernel's k chain (ten waves of 16 k-steps
+//     the tokens' row IDs once (the ID kernel's device code) while its other
+//     waves issue their W fragment loads, loads the rows with coalesced
+//     reads, dequantizes all of x into an LDS tile (the gather's device
+//     code), and runs proj_small_kernel's k chain (ten waves of 16 k-steps
 //     handing the accumulator on through LDS), so x and e are bit-identical
 //     to the three-launch path. It writes e as bf16 into the workspace,
 //     copies the carried state of sequences that need it, then releases and
