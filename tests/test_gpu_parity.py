@@ -11,7 +11,8 @@ import sparse_memory_gather_amd as ple
 from gen import inputs, table
 
 from parity_util import (D, check_samples, dev_bf16, dev_i32, e_bound, gate_bound, gather_debug, head_rows,
-                         host_bits, oracle_samples, rows, state_bound, y_bound, E_REL, OUT_ATOL, OUT_RTOL)
+                         host_bits, oracle_samples, oracle_windows, rows, state_bound, y_bound, E_REL, OUT_ATOL,
+                         OUT_RTOL)
 
 pytestmark = pytest.mark.gpu
 
@@ -300,6 +301,44 @@ def test_projection_tilings_agree_bit_exactly(dev, small_table, dev_weights):
         got = run(cuts)
         for a, b in zip(got, full):
             assert np.array_equal(a, b), cuts
+
+
+@pytest.mark.parametrize("lengths", [[3000], [1500, 1, 2595]])
+def test_mid_size_tilings_against_oracle(dev, small_table, dev_weights, weights, lengths):
+    # a call of 257-3200 tokens runs the 128-token tiles of the projection
+    # and one of 3201-6400 tokens (4096 here) the 256 x 256 tiles: e, g, y and
+    # out against the oracle at every sequence's first and last tokens,
+    # random interior tokens and every 16th block-range start of the
+    # streaming fuse, and the carried conv state of every sequence
+    W, cw = weights
+    tab, sc = small_table
+    toks, cu, hist, hlen, h = _case(301 + len(lengths), lengths, [0] * len(lengths))
+    T, S = int(cu[-1]), len(lengths)
+    assert ple.proj_tiling(T) == ("proj_mid_kernel" if T <= 3200 else "proj_kernel")
+    st = ple.State(S, dev)
+    res = _forward(dev, tab, sc, dev_weights, toks, cu, h, st)
+    _same_without_debug(dev, tab, sc, dev_weights, toks, cu, h, ple.State(S, dev), res, st)
+    seqs = [(toks[cu[s]:cu[s + 1]], h[cu[s]:cu[s + 1]]) for s in range(S)]
+    rng = np.random.default_rng(303)
+    wins = []
+    for s in range(S):
+        n = int(cu[s + 1] - cu[s])
+        wins += [(s, 0, min(4, n)), (s, max(0, n - 4), n)]
+        wins += [(s, int(p), int(p) + 1) for p in sorted(set(rng.integers(0, n, 6).tolist()))]
+    pb = -(-T // 256)
+    for b in range(pb, T, 16 * pb):
+        s = int(np.searchsorted(cu, b, side="right") - 1)
+        off = b - int(cu[s])
+        wins.append((s, max(0, off - 3), min(int(cu[s + 1] - cu[s]), off + 4)))
+    ref = oracle_windows(seqs, wins, W, cw, R_SMALL)
+    idx = [int(cu[s]) + p for s, lo, hi in wins for p in range(lo, hi)]
+    check_samples(gather_debug(res, idx), ref, W, f"T={T}")
+    # the carried state: the last three v of each sequence of 3 or more tokens
+    full = [s for s in range(S) if cu[s + 1] - cu[s] >= 3]
+    sref = oracle_windows(seqs, [(s, int(cu[s + 1] - cu[s]) - 3, int(cu[s + 1] - cu[s])) for s in full],
+                          W, cw, R_SMALL)
+    got = st.conv_state.cpu().numpy().astype(np.float64)[full].reshape(-1, D)
+    assert np.all(np.abs(sref["v"] - got) <= sref["dv"] + 1e-7)
 
 
 def test_streaming_fuse_equals_per_sequence_calls(dev, small_table, dev_weights):
