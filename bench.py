@@ -495,6 +495,79 @@ def measure(ctx, name, layout, steps, warmup, overlap=False, graph=False, cold=T
     return res
 
 
+def gather_stream(ctx, name, layout, batches=20):
+    """The gather kernel over `batches` different batches of the workload's
+    own shape and generator (the long workload: its 16 chunks), launched
+    back to back after one untimed pass, with events around the loop only.
+    A batch's rows are not those of the batch before, so for uniform tokens
+    no row is served from a cache filled by an earlier launch; Zipf batches
+    still share their most frequent rows. Bytes count each batch's distinct
+    rows once. None for the short workloads (no gather of their own to
+    time this way: a tiny table, or the rows read inside the one-launch
+    decode kernel)."""
+    import torch
+
+    import sparse_memory_gather_amd as ple
+    from gen import inputs
+
+    if name not in ("prefill", "ragged", "long"):
+        return None
+    dev = ctx.dev
+    heads, nvfp4 = layout == "heads", layout == "nvfp4"
+    wl = inputs.make_workload(name)
+    tab, sc, blocks = ctx.table(wl.R, layout)
+    if name == "long":
+        toks = [t for t, _ in wl.chunks]
+        cu = wl.chunks[0][1]
+    else:
+        cu = wl.chunks[0][1]
+        T = int(cu[-1])
+        rng = np.random.Generator(np.random.PCG64([wl.seed, 0x5354]))
+        gen = inputs.zipf_tokens if name == "prefill" else inputs.uniform_tokens
+        toks = [gen(rng, T) for _ in range(batches)]
+    S = len(cu) - 1
+    per_row = HEADS_BYTES_PER_ROW if heads else NVFP4_BYTES_PER_ROW if nvfp4 else GATHER_BYTES_PER_ROW
+    per_tok = HEADS_BYTES_PER_TOKEN if heads else GATHER_BYTES_PER_TOKEN
+    cu_d = torch.from_numpy(cu).to(dev)
+    rids, total = [], 0
+    for i, t in enumerate(toks):
+        if name == "long" and i > 0:
+            hid = torch.from_numpy(toks[i - 1][-2:].reshape(1, 2).astype(np.int32)).to(dev)
+            hl = torch.full((1,), 2, dtype=torch.int32, device=dev)
+        else:
+            hid = torch.zeros((S, 2), dtype=torch.int32, device=dev)
+            hl = torch.zeros((S,), dtype=torch.int32, device=dev)
+        rid = ple.ple_hash(torch.from_numpy(t).to(dev), cu_d, hid, hl, wl.R, heads=heads)
+        valid = rid >= 0
+        key = rid.to(torch.int64)
+        if heads:
+            key = key + torch.arange(16, device=dev, dtype=torch.int64)[None, :] * wl.R
+        total += int(torch.unique(key[valid]).numel()) * per_row + len(t) * per_tok
+        rids.append(rid)
+    x = torch.empty((len(toks[0]), D), dtype=torch.bfloat16, device=dev)
+
+    def run():
+        for rid in rids:
+            if nvfp4:
+                ple.ple_lookup_nvfp4(rid, tab, blocks, sc, x=x)
+            else:
+                ple.ple_lookup(rid, tab, sc, x=x, heads=heads)
+
+    run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    run()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / len(rids)
+    bytes_per = total / len(rids)
+    return {"batches": len(rids), "avg_us": round(us, 2), "bytes_per_launch": int(bytes_per),
+            "achieved": round(bytes_per / us * 1e-3, 1), "unit": "GB/s",
+            "frac": round(bytes_per / us * 1e-3 / HBM_PEAK_GBS, 4),
+            "timing": "events around back-to-back launches over different batches"}
+
+
 def copy_ceiling(dev, total_bytes, reps=12):
     """A plain device copy moving `total_bytes` (half read, half written),
     timed like the gather: a 1 GiB read before each copy evicts the caches,
@@ -695,6 +768,7 @@ def main():
         result["stages_median_us"] = stage_table(head, "stage_med_us")
         if gather.get("kernel"):
             gather["copy_same_bytes"] = copy_ceiling(dev, gather["bytes_per_launch"])
+            gather["stream"] = gather_stream(ctx, name, args.layout)
         if proj.get("bound") == "mfma":
             proj["vendor_gemm_same_shape"] = vendor_gemm(dev, int(head["tokens_per_call"]))
         result["gather"], result["proj"], result["fuse"] = gather, proj, fuse
@@ -718,6 +792,7 @@ def main():
                                                        "note") if k in g}}
             if g.get("kernel"):
                 per[wname]["gather"]["copy_same_bytes"] = copy_ceiling(dev, g["bytes_per_launch"])
+                per[wname]["gather"]["stream"] = gather_stream(ctx, wname, args.layout)
             if wname == "decode":
                 rg = measure(ctx, "decode", args.layout, st, wu, graph=True, warmup_ms=args.warmup_ms)
                 per[wname]["graph_replay"] = {"ms_per_step": round(rg["ms_per_step"], 4),
