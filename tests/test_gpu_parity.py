@@ -922,6 +922,7 @@ ONE_LAUNCH_CASES = [
     ([16], [0]),                                            # a fresh 16-token chunk
     ([0, 1, 5, 2, 0, 4, 3, 1], [2, 1, 0, 2, 1, 2, 0, 1]),   # empty, short and longer sequences
     ([1] * 14 + [0] * 186 + [2], [2] * 100 + [1] * 101),    # 201 sequences, most empty
+    ([0] * 120 + [1] * 16 + [0] * 120, [2, 1, 0, 2] * 64),   # the limits: 256 sequences, 16 tokens
 ]
 
 
