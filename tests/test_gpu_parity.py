@@ -398,10 +398,11 @@ def test_in_place_equals_out_of_place_both_fuse_kernels(dev, small_table, dev_we
     assert np.array_equal(host_bits(hd), host_bits(ref))
 
 
-@pytest.mark.parametrize("T", [300, 2000])
+@pytest.mark.parametrize("T", [8, 300, 2000])
 def test_forward_flags_bad_inputs_on_the_device(dev, small_table, dev_weights, T):
-    # 300 tokens: IDs computed inside the gather, one-token fuse; 2000: the
-    # ID kernel and the streaming fuse. Bad values the host cannot see are
+    # 8 tokens: the one-launch kernel; 300 tokens: IDs computed inside the
+    # gather, one-token fuse; 2000: the ID kernel and the streaming fuse.
+    # Bad values the host cannot see are
     # flagged in dev_err (1: token ID outside the vocabulary, 4: hist_len
     # outside 0..2, 2: malformed cu_seqlens) and every kernel stays in bounds.
     tab, sc = small_table
