@@ -37,12 +37,12 @@
 #include <atomic>
 
 #include "ple_dequant.h"
+#include "ple_fragments.h"
 #include "ple_fuse_common.h"
 
 namespace ple {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kRowsPerBlock = 32;            // features per projection block (the MFMA's A rows)
@@ -53,67 +53,6 @@ constexpr uint32_t kSpinLimit = 1u << 21;    // polls of `done` before giving up
 constexpr int kDevErrSync = 16;              // PLE_DEVERR_SYNC
 
 constexpr int kXRow = kD + 8;   // LDS row of the x tile in bf16: 16 bytes of padding spread the tokens over the banks
-
-// W fragments of one wave, loaded in 64-byte runs and moved into the MFMA
-// layout in registers.
-//
-// The A operand of v_mfma_f32_32x32x16_bf16 puts row (lane & 31) in every
-// lane, so a load in that layout reads 32 rows of 16 or 32 bytes each; the
-// address unit takes such a load as 64 pieces, and the 160 loads of a
-// block's W slice held it for about 4.4 us. Here register q, lane l loads
-// row (q & 3) + (l & 28) at 16-byte chunk (l >> 5) + 2 (l & 3) + 8 (q >> 2)
-// of the wave's 512-byte k range: four lanes in a row read one 64-byte run of
-// one cache line, and the same 160 KB load in about 1.2 us. In lane and
-// register bits the two layouts differ by two exchanges: lane bit 0 with
-// register bit 0 and lane bit 1 with register bit 1. After them register q,
-// lane l holds row (l & 31), chunk 2q + (l >> 5): the MFMA fragment q.
-//
-// Each exchange is a v_cndmask_b32 with a DPP source (quad_perm swaps lanes
-// l and l ^ 1, or l and l ^ 2) under a lane mask in VCC: y keeps its own
-// value on the lanes with the bit set and takes x from the partner lane
-// elsewhere; x mirrors it. Written as inline assembly because the compiler
-// selects with a 64-bit SGPR mask (the VOP3 form, which takes no DPP) and
-// then needs a separate DPP move per value. The s_nop gives the two wait
-// states a DPP read needs after a VALU write of the same register.
-#define PLE_LANE_SWAP_ASM(QP)                                                                        \
-    asm volatile("s_nop 1\n\t"                                                                      \
-                 "s_mov_b64 vcc, %16\n\t"                                                           \
-                 "v_cndmask_b32_dpp %4, %8, %12, vcc " QP " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
-                 "v_cndmask_b32_dpp %5, %9, %13, vcc " QP " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
-                 "v_cndmask_b32_dpp %6, %10, %14, vcc " QP " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
-                 "v_cndmask_b32_dpp %7, %11, %15, vcc " QP " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
-                 "s_mov_b64 vcc, %17\n\t"                                                           \
-                 "v_cndmask_b32_dpp %0, %12, %8, vcc " QP " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
-                 "v_cndmask_b32_dpp %1, %13, %9, vcc " QP " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
-                 "v_cndmask_b32_dpp %2, %14, %10, vcc " QP " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
-                 "v_cndmask_b32_dpp %3, %15, %11, vcc " QP " row_mask:0xf bank_mask:0xf bound_ctrl:1"      \
-                 : "=&v"(nx[0]), "=&v"(nx[1]), "=&v"(nx[2]), "=&v"(nx[3]),                                \
-                   "=&v"(ny[0]), "=&v"(ny[1]), "=&v"(ny[2]), "=&v"(ny[3])                                 \
-                 : "v"(xv[0]), "v"(xv[1]), "v"(xv[2]), "v"(xv[3]),                                        \
-                   "v"(yv[0]), "v"(yv[1]), "v"(yv[2]), "v"(yv[3]), "s"(m), "s"(~m)                        \
-                 : "vcc")
-
-// exchange lane bit BIT (1 or 2) with the register bit that tells x from y;
-// m has bit l set for the lanes l with that lane bit set
-template <int BIT>
-__device__ inline void lane_swap(bf16x8& x, bf16x8& y, uint64_t m) {
-    const u32x4 xv = __builtin_bit_cast(u32x4, x), yv = __builtin_bit_cast(u32x4, y);
-    u32x4 nx, ny;
-    if (BIT == 1) PLE_LANE_SWAP_ASM("quad_perm:[1,0,3,2]");
-    else PLE_LANE_SWAP_ASM("quad_perm:[2,3,0,1]");
-    x = __builtin_bit_cast(bf16x8, nx);
-    y = __builtin_bit_cast(bf16x8, ny);
-}
-#undef PLE_LANE_SWAP_ASM
-
-__device__ inline void w_runs_to_fragments(bf16x8 (&fa)[kSteps]) {
-    static_assert(kSteps == 16, "four register bits: rows 0-1, chunks 3-4");
-#pragma unroll
-    for (int q = 0; q < kSteps; q += 2) lane_swap<1>(fa[q], fa[q + 1], 0xAAAAAAAAAAAAAAAAull);
-#pragma unroll
-    for (int q = 0; q < kSteps; ++q)
-        if (!(q & 2)) lane_swap<2>(fa[q], fa[q + 2], 0xCCCCCCCCCCCCCCCCull);
-}
 
 __global__ void __launch_bounds__(fuse::kThreads)
 decode_step_kernel(const DecodeArgs a) {
@@ -167,17 +106,16 @@ decode_step_kernel(const DecodeArgs a) {
             const ModR mr{a.mod_R, a.mod_m};
             s_rows[tid] = make_int2(bigram_row(k, mr), trigram_row(k, mr));
         }
-        // W in 64-byte runs (w_runs_to_fragments), issued while wave 0
-        // computes the IDs; the barrier below waits for LDS operations, not
-        // for loads in flight. Row (q & 3) + (lane & 28) of the block's 32,
-        // chunk (lane >> 5) + 2 (lane & 3) + 8 (q >> 2) of the wave's k range
+        // W in 64-byte runs (ple_fragments.h), issued while wave 0 computes
+        // the IDs: about a quarter of the address-unit time of loads in the
+        // MFMA layout. The barrier below waits for LDS operations, not for
+        // loads in flight
         static_assert(kRowsPerBlock == 32, "the runs cover the MFMA's 32 rows");
-        const uint16_t* wp = a.W + (int64_t)(f0 + (lane & 28)) * kD + wave * kSteps * 16 +
-                             ((lane >> 5) + 2 * (lane & 3)) * 8;
+        const uint16_t* wp = a.W + (int64_t)f0 * kD + wave * kSteps * 16;
         bf16x8 fa[kSteps];
 #pragma unroll
         for (int q = 0; q < kSteps; ++q)
-            fa[q] = *reinterpret_cast<const bf16x8*>(wp + (q & 3) * kD + (q >> 2) * 64);
+            fa[q] = *reinterpret_cast<const bf16x8*>(wp + run_row(q, lane) * kD + run_chunk(q, lane) * 8);
         __syncthreads();
         // x of every token into LDS, 8 elements per piece (the gather's
         // device code): consecutive threads read consecutive 8-byte pieces of
@@ -242,7 +180,7 @@ decode_step_kernel(const DecodeArgs a) {
         for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
         const int wv = __builtin_amdgcn_readfirstlane(wave);
         for (int i = 0; i + 1 < wv; ++i) __syncthreads();
-        w_runs_to_fragments(fa);
+        runs_to_fragments(fa);
         if (wv > 0) {
             __syncthreads();
             acc = acc_s[lane];

@@ -35,12 +35,12 @@
 // whichever needs fewer rounds of blocks on the 256 CUs.
 #include <atomic>
 
+#include "ple_fragments.h"
 #include "ple_kernels.h"
 
 namespace ple {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void gbl_void;
@@ -236,15 +236,21 @@ proj_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __restric
 // the fragments of k-steps 20w .. 20w+19, all loaded up front. A tile's
 // accumulator passes from wave to wave through LDS, so it sees the same MFMA
 // sequence over k as in proj_kernel and every output element is
-// bit-identical to what proj_kernel produces. kRows < 32 leaves the MFMA's
-// other A rows zero (an output element depends only on its own row and
-// column), so that an 8-token step spreads its W loads over 160 CUs. With
+// bit-identical to what proj_kernel produces. With kRows = 16 the MFMA's
+// other 16 A rows repeat the block's rows and their outputs are dropped (an
+// output element depends only on its own row and column), so that an
+// 8-token step spreads its W loads over 160 CUs; likewise tokens past the
+// last feed token 0's x into columns that are never stored. With
 // kTiles > 1 the tiles' chains are pipelined through the waves with the same
 // W fragments: in step s wave w runs its segment of tile s - w, so the block
 // takes kW + kTiles - 1 steps instead of kW x kTiles, each wave loading its x
 // fragments of the next tile right after its segment of the current one;
 // calls of up to 256 tokens take one round of blocks (one block per CU fits
-// at this register use).
+// at this register use). A block loads W and its first token tile in
+// 64-byte runs (ple_fragments.h), a quarter of the address-unit time of loads
+// in the MFMA layout, and wave w moves them into that layout during the step
+// before its first segment (passing w barriers first, so only wave 0's
+// exchange precedes the first segment).
 template <bool kFwd, int kRows, int kTiles>
 __global__ void __launch_bounds__(512)
 proj_small_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __restrict__ W,
@@ -257,36 +263,36 @@ proj_small_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __r
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int fr = lane & 31, kh = lane >> 5;
     const int f0 = blockIdx.x * kRows;
-    const bool row = fr < kRows;
-    const uint16_t* wrow = W + (int64_t)(f0 + (row ? fr : 0)) * kD + wave * SPW * 16 + kh * 8;
     bf16x8 fa[SPW], fb[SPW];
-    const bf16x8 zero = {};
+    // token tile t >= 1 in the MFMA layout. Tokens past the last read token 0
+    // (in bounds): their columns of the product are never stored, and loads
+    // under a per-lane condition would make the compiler wait for the first
+    // of them before issuing the rest
     auto load_x = [&](int t) {
         const int64_t tok = ((int64_t)blockIdx.y * kTiles + t) * 32 + fr;
-        const bool live = tok < M;
-        const uint16_t* xrow = x + (live ? tok : 0) * kD + wave * SPW * 16 + kh * 8;
+        const uint16_t* xrow = x + (tok < M ? tok : 0) * kD + wave * SPW * 16 + kh * 8;
 #pragma unroll
-        for (int q = 0; q < SPW; ++q) fb[q] = live ? *reinterpret_cast<const bf16x8*>(xrow + q * 16) : zero;
+        for (int q = 0; q < SPW; ++q) fb[q] = *reinterpret_cast<const bf16x8*>(xrow + q * 16);
     };
-#pragma unroll
-    for (int q = 0; q < SPW; ++q) fa[q] = row ? *reinterpret_cast<const bf16x8*>(wrow + q * 16) : zero;
-    load_x(0);
-    if constexpr (kTiles == 1) {
-        // one tile: the chain passes from wave to wave
+    // a tile's segment on this wave: k-steps 20 wave .. 20 wave + 19 of tile
+    // t, the accumulator from the wave before (or zero), to the wave after
+    // (or e for the last wave)
+    auto segment = [&](int t) {
         f32x16 acc;
+        if (wave == 0) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-        for (int w = 0; w < kW; ++w) {
-            if (wave == w) {
-                if (w > 0) acc = acc_s[0][lane];
-#pragma unroll
-                for (int q = 0; q < SPW; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[q], fb[q], acc, 0, 0, 0);
-                if (w + 1 < kW) acc_s[0][lane] = acc;
-            }
-            __syncthreads();
+            for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+        } else {
+            acc = acc_s[t][lane];
         }
-        const int64_t tok = (int64_t)blockIdx.y * 32 + fr;
-        if (wave == kW - 1 && tok < M) {
+#pragma unroll
+        for (int q = 0; q < SPW; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[q], fb[q], acc, 0, 0, 0);
+        if (wave + 1 < kW) {
+            acc_s[t][lane] = acc;
+            return;
+        }
+        const int64_t tok = ((int64_t)blockIdx.y * kTiles + t) * 32 + fr;
+        if (tok < M) {
             // lane holds token `tok` and features f0 + 8 g + 4 kh + 0..3
 #pragma unroll
             for (int g = 0; g < kRows / 8; ++g) {
@@ -296,42 +302,32 @@ proj_small_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __r
                 if (kFwd) *reinterpret_cast<u32x2*>(e16 + off) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
             }
         }
-        return;
+    };
+    // W rows f0 .. f0 + kRows - 1 and token tile 0 in runs. With 16 rows the
+    // MFMA's other 16 A rows repeat them; those outputs are never stored
+    const int kb = wave * SPW * 16;
+    const int64_t t0 = (int64_t)blockIdx.y * kTiles * 32;
+#pragma unroll
+    for (int q = 0; q < SPW; ++q) {
+        const int r = run_row(q, lane);
+        fa[q] = *reinterpret_cast<const bf16x8*>(W + (int64_t)(f0 + (r < kRows ? r : r - kRows)) * kD + kb +
+                                                 run_chunk(q, lane) * 8);
+        const int64_t tok = t0 + r;
+        fb[q] = *reinterpret_cast<const bf16x8*>(x + (tok < M ? tok : 0) * kD + kb + run_chunk(q, lane) * 8);
     }
-    // step s: wave w runs k-steps 20w .. 20w+19 of tile s - w; tile t's
-    // accumulator goes from wave w to wave w+1 through acc_s[t] between steps
-    for (int s = 0; s < kW + kTiles - 1; ++s) {
-        const int t = s - wave;
-        if (t >= 0 && t < kTiles) {
-            f32x16 acc;
-            if (wave == 0) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-            } else {
-                acc = acc_s[t][lane];
-            }
-#pragma unroll
-            for (int q = 0; q < SPW; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[q], fb[q], acc, 0, 0, 0);
-            if (wave + 1 < kW) {
-                acc_s[t][lane] = acc;
-            } else {
-                const int64_t tok = ((int64_t)blockIdx.y * kTiles + t) * 32 + fr;
-                if (tok < M) {
-                    // lane holds token `tok` and features f0 + 8 g + 4 kh + 0..3
-#pragma unroll
-                    for (int g = 0; g < kRows / 8; ++g) {
-                        const float v0 = acc[4 * g], v1 = acc[4 * g + 1], v2 = acc[4 * g + 2], v3 = acc[4 * g + 3];
-                        const int64_t off = tok * kD + f0 + g * 8 + kh * 4;
-                        if (!kFwd || e32) *reinterpret_cast<f32x4*>(e32 + off) = f32x4{v0, v1, v2, v3};
-                        if (kFwd)
-                            *reinterpret_cast<u32x2*>(e16 + off) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-                    }
-                }
-            }
-            if (t + 1 < kTiles) load_x(t + 1);
-        }
+    // wave w runs tile t in step w + t; every wave passes kW + kTiles - 1
+    // barriers, one at the end of each step
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    for (int i = 0; i + 1 < wv; ++i) __syncthreads();
+    runs_to_fragments(fa);
+    runs_to_fragments(fb);
+    if (wv > 0) __syncthreads();
+    for (int t = 0; t < kTiles; ++t) {
+        segment(t);
+        if (t + 1 < kTiles) load_x(t + 1);
         __syncthreads();
     }
+    for (int i = wv; i + 1 < kW; ++i) __syncthreads();
 }
 
 // Mid-size calls (257-3200 tokens): tiles of 128 tokens x 256 features so
