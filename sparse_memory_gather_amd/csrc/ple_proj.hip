@@ -244,7 +244,7 @@ proj_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __restric
 // kTiles > 1 the tiles' chains are pipelined through the waves with the same
 // W fragments: in step s wave w runs its segment of tile s - w, so the block
 // takes kW + kTiles - 1 steps instead of kW x kTiles, each wave loading its x
-// fragments of the next tile right after its segment of the current one;
+// fragments of the next tile during its segment of the current one;
 // calls of up to 256 tokens take one round of blocks (one block per CU fits
 // at this register use). A block loads W and its first token tile in
 // 64-byte runs (ple_fragments.h), a quarter of the address-unit time of loads
@@ -264,16 +264,6 @@ proj_small_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __r
     const int fr = lane & 31, kh = lane >> 5;
     const int f0 = blockIdx.x * kRows;
     bf16x8 fa[SPW], fb[SPW];
-    // token tile t >= 1 in the MFMA layout. Tokens past the last read token 0
-    // (in bounds): their columns of the product are never stored, and loads
-    // under a per-lane condition would make the compiler wait for the first
-    // of them before issuing the rest
-    auto load_x = [&](int t) {
-        const int64_t tok = ((int64_t)blockIdx.y * kTiles + t) * 32 + fr;
-        const uint16_t* xrow = x + (tok < M ? tok : 0) * kD + wave * SPW * 16 + kh * 8;
-#pragma unroll
-        for (int q = 0; q < SPW; ++q) fb[q] = *reinterpret_cast<const bf16x8*>(xrow + q * 16);
-    };
     // a tile's segment on this wave: k-steps 20 wave .. 20 wave + 19 of tile
     // t, the accumulator from the wave before (or zero), to the wave after
     // (or e for the last wave)
@@ -285,8 +275,28 @@ proj_small_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __r
         } else {
             acc = acc_s[t][lane];
         }
+        if (t + 1 < kTiles) {
+            // the next tile's fragment q replaces this one's as soon as its
+            // MFMA has issued, so those loads are in flight during the
+            // segment. Tokens past the last read token 0 (in bounds): their
+            // columns of the product are never stored, and loads under a
+            // per-lane condition would make the compiler wait for the first
+            // of them before issuing the rest
+            const int64_t tok = ((int64_t)blockIdx.y * kTiles + t + 1) * 32 + fr;
+            const uint16_t* xrow = x + (tok < M ? tok : 0) * kD + wave * SPW * 16 + kh * 8;
 #pragma unroll
-        for (int q = 0; q < SPW; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[q], fb[q], acc, 0, 0, 0);
+            for (int q = 0; q < SPW; ++q) {
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[q], fb[q], acc, 0, 0, 0);
+                fb[q] = *reinterpret_cast<const bf16x8*>(xrow + q * 16);
+                // one MFMA, then one load (without this the compiler issues
+                // 15 of the MFMAs before the first load)
+                __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x20, 1, 0);  // VMEM read
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < SPW; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[q], fb[q], acc, 0, 0, 0);
+        }
         if (wave + 1 < kW) {
             acc_s[t][lane] = acc;
             return;
@@ -324,7 +334,6 @@ proj_small_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __r
     if (wv > 0) __syncthreads();
     for (int t = 0; t < kTiles; ++t) {
         segment(t);
-        if (t + 1 < kTiles) load_x(t + 1);
         __syncthreads();
     }
     for (int i = wv; i + 1 < kW; ++i) __syncthreads();
