@@ -60,11 +60,11 @@ STATE_BYTES_PER_SEQ = 3 * D * 4   # the carried conv state of one sequence (fp32
 PER_CONFIG = (("tiny", 50, 10), ("decode", 64, 8), ("ragged", 20, 5), ("long", 4, 1))
 
 _CSRC = "sparse_memory_gather_amd/csrc/"
-_PROJ_SRC = [_CSRC + f for f in ("ple_proj.hip", "ple_kernels.h")]
+_PROJ_SRC = [_CSRC + f for f in ("ple_proj.hip", "ple_fragments.h", "ple_kernels.h")]
 _GATHER_SRC = [_CSRC + f for f in ("ple_gather.hip", "ple_dequant.h", "ple_ngram.h", "ple_kernels.h")]
 _FUSE_SRC = [_CSRC + f for f in ("ple_fuse.hip", "ple_fuse_common.h", "ple_ngram.h", "ple_kernels.h")]
-_DECODE_SRC = [_CSRC + f for f in ("ple_decode.hip", "ple_dequant.h", "ple_fuse_common.h", "ple_ngram.h",
-                                   "ple_kernels.h")]
+_DECODE_SRC = [_CSRC + f for f in ("ple_decode.hip", "ple_dequant.h", "ple_fragments.h", "ple_fuse_common.h",
+                                   "ple_ngram.h", "ple_kernels.h")]
 # every file a kernel is compiled from: a recorded traffic figure holds only
 # while their contents are unchanged
 KERNEL_SOURCES = {

@@ -236,21 +236,19 @@ proj_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __restric
 // the fragments of k-steps 20w .. 20w+19, all loaded up front. A tile's
 // accumulator passes from wave to wave through LDS, so it sees the same MFMA
 // sequence over k as in proj_kernel and every output element is
-// bit-identical to what proj_kernel produces. With kRows = 16 the MFMA's
-// other 16 A rows repeat the block's rows and their outputs are dropped (an
-// output element depends only on its own row and column), so that an
-// 8-token step spreads its W loads over 160 CUs; likewise tokens past the
-// last feed token 0's x into columns that are never stored. With
+// bit-identical to what proj_kernel produces. kRows < 32 leaves the MFMA's
+// other A rows zero (an output element depends only on its own row and
+// column), so that an 8-token step spreads its W loads over 160 CUs. With
 // kTiles > 1 the tiles' chains are pipelined through the waves with the same
 // W fragments: in step s wave w runs its segment of tile s - w, so the block
 // takes kW + kTiles - 1 steps instead of kW x kTiles, each wave loading its x
 // fragments of the next tile during its segment of the current one;
 // calls of up to 256 tokens take one round of blocks (one block per CU fits
-// at this register use). A block loads W and its first token tile in
-// 64-byte runs (ple_fragments.h), a quarter of the address-unit time of loads
-// in the MFMA layout, and wave w moves them into that layout during the step
-// before its first segment (passing w barriers first, so only wave 0's
-// exchange precedes the first segment).
+// at this register use). With 32 rows a block loads W and its first token
+// tile in 64-byte runs (ple_fragments.h), a quarter of the address-unit time
+// of loads in the MFMA layout, and wave w moves them into that layout during
+// the step before its first segment (passing w barriers first, so only
+// wave 0's exchange precedes the first segment).
 template <bool kFwd, int kRows, int kTiles>
 __global__ void __launch_bounds__(512)
 proj_small_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __restrict__ W,
@@ -313,30 +311,69 @@ proj_small_kernel(const uint16_t* __restrict__ x, int64_t M, const uint16_t* __r
             }
         }
     };
-    // W rows f0 .. f0 + kRows - 1 and token tile 0 in runs. With 16 rows the
-    // MFMA's other 16 A rows repeat them; those outputs are never stored
-    const int kb = wave * SPW * 16;
-    const int64_t t0 = (int64_t)blockIdx.y * kTiles * 32;
+    if constexpr (kRows == 32) {
+        // W rows f0 .. f0+31 and token tile 0 in runs; tokens past the last
+        // read token 0 (in bounds), whose columns are never stored
+        const int kb = wave * SPW * 16;
+        const int64_t t0 = (int64_t)blockIdx.y * kTiles * 32;
 #pragma unroll
-    for (int q = 0; q < SPW; ++q) {
-        const int r = run_row(q, lane);
-        fa[q] = *reinterpret_cast<const bf16x8*>(W + (int64_t)(f0 + (r < kRows ? r : r - kRows)) * kD + kb +
-                                                 run_chunk(q, lane) * 8);
-        const int64_t tok = t0 + r;
-        fb[q] = *reinterpret_cast<const bf16x8*>(x + (tok < M ? tok : 0) * kD + kb + run_chunk(q, lane) * 8);
+        for (int q = 0; q < SPW; ++q) {
+            const int r = run_row(q, lane);
+            fa[q] = *reinterpret_cast<const bf16x8*>(W + (int64_t)(f0 + r) * kD + kb + run_chunk(q, lane) * 8);
+            const int64_t tok = t0 + r;
+            fb[q] = *reinterpret_cast<const bf16x8*>(x + (tok < M ? tok : 0) * kD + kb + run_chunk(q, lane) * 8);
+        }
+        // wave w runs tile t in step w + t; every wave passes kW + kTiles - 1
+        // barriers, one at the end of each step
+        const int wv = __builtin_amdgcn_readfirstlane(wave);
+        for (int i = 0; i + 1 < wv; ++i) __syncthreads();
+        runs_to_fragments(fa);
+        runs_to_fragments(fb);
+        if (wv > 0) __syncthreads();
+        for (int t = 0; t < kTiles; ++t) {
+            segment(t);
+            __syncthreads();
+        }
+        for (int i = wv; i + 1 < kW; ++i) __syncthreads();
+    } else {
+        // 16 rows and one token tile (a decode step's few tokens): W and x in
+        // the MFMA layout, the lanes of the MFMA's other 16 A rows and of the
+        // tokens past the last loading nothing (zeros). Here that is fewer
+        // pieces for the address unit than runs over all 32 rows and tokens
+        static_assert(kTiles == 1, "16-row blocks take one token tile");
+        const bf16x8 zero = {};
+        const bool row = fr < kRows;
+        const uint16_t* wrow = W + (int64_t)(f0 + (row ? fr : 0)) * kD + wave * SPW * 16 + kh * 8;
+        const int64_t tok = (int64_t)blockIdx.y * 32 + fr;
+        const bool live = tok < M;
+        const uint16_t* xrow = x + (live ? tok : 0) * kD + wave * SPW * 16 + kh * 8;
+#pragma unroll
+        for (int q = 0; q < SPW; ++q) fa[q] = row ? *reinterpret_cast<const bf16x8*>(wrow + q * 16) : zero;
+#pragma unroll
+        for (int q = 0; q < SPW; ++q) fb[q] = live ? *reinterpret_cast<const bf16x8*>(xrow + q * 16) : zero;
+        f32x16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+        for (int w = 0; w < kW; ++w) {
+            if (wave == w) {
+                if (w > 0) acc = acc_s[0][lane];
+#pragma unroll
+                for (int q = 0; q < SPW; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[q], fb[q], acc, 0, 0, 0);
+                if (w + 1 < kW) acc_s[0][lane] = acc;
+            }
+            __syncthreads();
+        }
+        if (wave == kW - 1 && live) {
+            // lane holds token `tok` and features f0 + 8 g + 4 kh + 0..3
+#pragma unroll
+            for (int g = 0; g < kRows / 8; ++g) {
+                const float v0 = acc[4 * g], v1 = acc[4 * g + 1], v2 = acc[4 * g + 2], v3 = acc[4 * g + 3];
+                const int64_t off = tok * kD + f0 + g * 8 + kh * 4;
+                if (!kFwd || e32) *reinterpret_cast<f32x4*>(e32 + off) = f32x4{v0, v1, v2, v3};
+                if (kFwd) *reinterpret_cast<u32x2*>(e16 + off) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+            }
+        }
     }
-    // wave w runs tile t in step w + t; every wave passes kW + kTiles - 1
-    // barriers, one at the end of each step
-    const int wv = __builtin_amdgcn_readfirstlane(wave);
-    for (int i = 0; i + 1 < wv; ++i) __syncthreads();
-    runs_to_fragments(fa);
-    runs_to_fragments(fb);
-    if (wv > 0) __syncthreads();
-    for (int t = 0; t < kTiles; ++t) {
-        segment(t);
-        __syncthreads();
-    }
-    for (int i = wv; i + 1 < kW; ++i) __syncthreads();
 }
 
 // Mid-size calls (257-3200 tokens): tiles of 128 tokens x 256 features so

@@ -200,3 +200,29 @@ def test_noalloc_refuses_oversize_calls_and_a_workspace_before_any_launch():
     a = _fwd_args()
     assert lib.ple_forward_noalloc(ctypes.byref(a), None) == -6
     assert lib.ple_forward_noalloc(None, None) == -1
+
+
+def test_traffic_hashes_cover_every_file_a_kernel_is_built_from():
+    """bench.py reports a recorded HBM-traffic figure only while the hash of
+    the kernel's source files matches: the list must hold the .hip file and
+    every header it includes, directly or not."""
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    sys.path.insert(0, root)
+    import bench
+    csrc = os.path.join(root, "sparse_memory_gather_amd", "csrc")
+
+    def closure(name, seen):
+        if name in seen:
+            return seen
+        seen.add(name)
+        for inc in re.findall(r'^#include "([^"]+)"', open(os.path.join(csrc, name)).read(), re.M):
+            if os.path.exists(os.path.join(csrc, inc)):
+                closure(inc, seen)
+        return seen
+
+    for kernel, files in bench.KERNEL_SOURCES.items():
+        names = {os.path.basename(f) for f in files}
+        hip = [n for n in names if n.endswith(".hip")]
+        assert len(hip) == 1, kernel
+        assert closure(hip[0], set()) == names, kernel
