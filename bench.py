@@ -281,7 +281,7 @@ class Context:
 
 
 def measure(ctx, name, layout, steps, warmup, overlap=False, graph=False, cold=True, warmup_ms=100.0,
-            inplace=False):
+            inplace=False, staged=False):
     """Time `steps` steps of workload `name` after `warmup` steps. Returns the
     workload's figures: tokens/s from wall time and from events around the
     timed loop, per-stage averages and medians from a second pass with
@@ -327,9 +327,10 @@ def measure(ctx, name, layout, steps, warmup, overlap=False, graph=False, cold=T
     # one prepared call per fixed set of buffers (each long chunk, each decode
     # step's batch, the single prefill/ragged/tiny batch): the argument
     # checks and marshalling happen once, outside the timing
-    # (in place, out == h: a short call then runs as three launches instead of one)
+    # (inplace: out == h; staged: every stage its own launch, also for the
+    # short calls ple_forward runs as one)
     calls = [ple.Forward(t, c, tab, sc, Wd, cwd, h, state, out=h if inplace else o, workspace=ws, heads=heads,
-                         nvfp4_blocks=blocks) for (t, c, h), o in zip(batches, outs)]
+                         nvfp4_blocks=blocks, staged=staged) for (t, c, h), o in zip(batches, outs)]
 
     def eager_step(k, events=None):
         if name == "long":
@@ -421,7 +422,7 @@ def measure(ctx, name, layout, steps, warmup, overlap=False, graph=False, cold=T
            "tokens_per_step": tokens_per_step, "ms_per_step": 1e3 * wall / steps,
            "value": tokens_per_step * steps / wall, "gpu_ms_per_step": gpu_ms / steps,
            "workload": describe(name, wl, layout), "S": wl.S, "R": wl.R, "graph": graph}
-    if graph or overlap or inplace:
+    if graph or overlap or inplace or staged:
         return res
 
     # per-kernel durations inside the real forward: events around each kernel
@@ -798,12 +799,14 @@ def main():
                 per[wname]["graph_replay"] = {"ms_per_step": round(rg["ms_per_step"], 4),
                                               "gpu_ms_per_step": round(rg["gpu_ms_per_step"], 4),
                                               "value": round(rg["value"], 1)}
-                # the same steps in place (out == h), which ple_forward runs as
-                # three launches: IDs in the gather, small-T projection, one-token fuse
-                r3 = measure(ctx, "decode", args.layout, st, wu, warmup_ms=args.warmup_ms, inplace=True)
-                per[wname]["three_launches_in_place"] = {"ms_per_step": round(r3["ms_per_step"], 4),
-                                                         "gpu_ms_per_step": round(r3["gpu_ms_per_step"], 4),
-                                                         "value": round(r3["value"], 1)}
+                # the same steps in place (out == h), one launch as well; and
+                # as three launches (ple_forward_staged: IDs in the gather,
+                # small-T projection, one-token fuse)
+                for key, kw in (("in_place", {"inplace": True}), ("three_launches", {"staged": True})):
+                    r3 = measure(ctx, "decode", args.layout, st, wu, warmup_ms=args.warmup_ms, **kw)
+                    per[wname][key] = {"ms_per_step": round(r3["ms_per_step"], 4),
+                                       "gpu_ms_per_step": round(r3["gpu_ms_per_step"], 4),
+                                       "value": round(r3["value"], 1)}
             ctx.drop_tables(inputs.R_FULL)
         result["per_config"] = per
 

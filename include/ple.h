@@ -159,9 +159,10 @@ typedef struct ple_forward_args {
  * state). Everything runs on `stream`; nothing is synchronized.
  *
  * Short calls (ple_forward_one_launch(T, S): up to 16 tokens and 256
- * sequences, out != h) run as ONE kernel launch: projection blocks and one
- * finisher block per token, ordered through three counters in the first 256
- * bytes of the workspace (decode steps split into separate launches cannot
+ * sequences) run as ONE kernel launch: projection blocks and one finisher
+ * block per token, ordered through three counters in the first 256 bytes of
+ * the workspace (in place, the projection blocks also copy h into the
+ * workspace, where the finishers read the earlier tokens' rows) (decode steps split into separate launches cannot
  * hide the table reads: mengman.github.io "Qwen3.8-Flash-Next 端侧部署 01",
  * inference-flow section; kipfel.ltd Thor article, section "五、启动参数").
  * Those bytes must be zero before the first call on a workspace; every call
@@ -172,9 +173,17 @@ typedef struct ple_forward_args {
  * bit for bit. */
 int ple_forward(const ple_forward_args* args, void* stream);
 
-/* 1 if ple_forward runs a T-token call of S sequences (FP8 table, out != h)
- * as one launch, else 0. Host-only, enqueues nothing. */
+/* 1 if ple_forward runs a T-token call of S sequences (FP8 table) as one
+ * launch, else 0. Host-only, enqueues nothing. */
 int ple_forward_one_launch(int64_t T, int32_t S);
+
+/* ple_forward (the same operation, arguments, workspace, errors and results,
+ * bit for bit) with every stage its own kernel launch at every call size:
+ * the ID kernel (or IDs inside the gather for short calls), the gather, the
+ * projection and the fuse, as ple_forward runs calls beyond
+ * ple_forward_one_launch. For callers that want the stages as separate
+ * launches, for instance to compare the two paths. */
+int ple_forward_staged(const ple_forward_args* args, void* stream);
 
 /* ple_forward with per-stage timing: the same launches on the same stream,
  * with events[0..4] (hipEvent_t, created by the caller) recorded before the

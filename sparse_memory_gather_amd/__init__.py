@@ -66,7 +66,8 @@ EXPORTS = ("ple_hash", "ple_lookup", "ple_proj", "ple_forward", "ple_forward_pro
            "ple_forward_heads_profiled", "ple_forward_heads_workspace_size", "ple_forward_x",
            "ple_lookup_nvfp4", "ple_forward_nvfp4", "ple_forward_nvfp4_profiled",
            "ple_status_string", "ple_last_error", "ple_proj_tiling", "ple_forward_noalloc",
-           "ple_forward_noalloc_max_tokens", "ple_forward_noalloc_max_sequences", "ple_forward_one_launch")
+           "ple_forward_noalloc_max_tokens", "ple_forward_noalloc_max_sequences", "ple_forward_one_launch",
+           "ple_forward_staged")
 HEADS = 16            # 16-lookup layout: head tables of 160-byte rows
 SLICE = D // HEADS
 
@@ -89,7 +90,7 @@ def load_library(path: str = LIB_PATH):
         getattr(lib, name).restype = ctypes.c_int
     lib.ple_proj.argtypes = [_P, I64, _P, _P, _P]
     lib.ple_proj.restype = ctypes.c_int
-    for name in ("ple_forward", "ple_forward_heads"):
+    for name in ("ple_forward", "ple_forward_heads", "ple_forward_staged"):
         getattr(lib, name).argtypes = [ctypes.POINTER(ForwardArgs), _P]
         getattr(lib, name).restype = ctypes.c_int
     for name in ("ple_forward_profiled", "ple_forward_heads_profiled"):
@@ -132,8 +133,8 @@ def proj_tiling(T: int):
 
 
 def one_launch(T: int, S: int) -> bool:
-    """Whether ple_forward runs a T-token call of S sequences (FP8 table,
-    out not h) as one kernel launch."""
+    """Whether ple_forward runs a T-token call of S sequences (FP8 table) as
+    one kernel launch."""
     return bool(load_library().ple_forward_one_launch(int(T), int(S)))
 
 
@@ -302,12 +303,14 @@ class Forward:
     def __init__(self, tokens, cu_seqlens, table, scales, W, conv_w, h, state: State, out=None,
                  workspace=None, vocab_size: int = DEFAULT_VOCAB, eps: float = DEFAULT_EPS,
                  dev_err=None, debug: bool = False, heads: bool = False, nvfp4_blocks=None,
-                 noalloc: bool = False):
+                 noalloc: bool = False, staged: bool = False):
         T = tokens.numel()
         S = cu_seqlens.numel() - 1
         nv = nvfp4_blocks is not None
         if nv and heads:
             raise ValueError("the NVFP4 table is read with two lookups per token")
+        if staged and (noalloc or heads or nv):
+            raise ValueError("staged runs the two-lookup FP8 table through ple_forward_staged")
         R = scales.shape[0] if nv else _rows_of(table, scales, heads)
         n = HEADS if heads else 2
         dev = tokens.device
@@ -363,6 +366,9 @@ class Forward:
         if noalloc:
             self._run = lambda st: lib.ple_forward_noalloc(byref, st)
             self._run_ev = None
+        elif staged:
+            self._run = lambda st: lib.ple_forward_staged(byref, st)
+            self._run_ev = None
         elif nv:
             blk = _dev(nvfp4_blocks, "nvfp4_blocks", torch.uint8, (R, D // 16))
             self._run = lambda st: lib.ple_forward_nvfp4(byref, blk, st)
@@ -380,7 +386,7 @@ class Forward:
         if events is None:
             _check(self._run(_stream(stream)))
         elif self._run_ev is None:
-            raise ValueError("per-stage events are not recorded by ple_forward_noalloc")
+            raise ValueError("per-stage events are recorded by ple_forward_profiled only (not by noalloc or staged)")
         else:
             _check(self._run_ev(_stream(stream), (_P * 5)(*[ctypes.c_void_p(int(e)) for e in events])))
         if self.debug is not None:
@@ -392,7 +398,7 @@ class Forward:
 def ple_forward(tokens, cu_seqlens, table, scales, W, conv_w, h, state: State, out=None,
                 workspace=None, vocab_size: int = DEFAULT_VOCAB, eps: float = DEFAULT_EPS,
                 dev_err=None, debug: bool = False, stream=None, events=None, heads: bool = False,
-                nvfp4_blocks=None, noalloc: bool = False):
+                nvfp4_blocks=None, noalloc: bool = False, staged: bool = False):
     """a1..a4 for one chunk. Updates `state` in place; returns out (bf16
     [T][2560]) or, with debug=True, a dict with out, row_ids, x, e, gate, y.
     `events`: optional sequence of five hipEvent_t handles (ints) recorded
@@ -400,10 +406,11 @@ def ple_forward(tokens, cu_seqlens, table, scales, W, conv_w, h, state: State, o
     layout (scales [16][R], row_ids [T][16]). nvfp4_blocks (uint8 [R][160]):
     the NVFP4 table, `table` then being the packed codes uint8 [R][1280].
     noalloc=True: ple_forward_noalloc (no workspace; up to
-    noalloc_limits() tokens and sequences)."""
+    noalloc_limits() tokens and sequences). staged=True: ple_forward_staged
+    (every stage its own launch, also for the calls ple_forward runs as one)."""
     return Forward(tokens, cu_seqlens, table, scales, W, conv_w, h, state, out=out, workspace=workspace,
                    vocab_size=vocab_size, eps=eps, dev_err=dev_err, debug=debug, heads=heads,
-                   nvfp4_blocks=nvfp4_blocks, noalloc=noalloc)(stream=stream, events=events)
+                   nvfp4_blocks=nvfp4_blocks, noalloc=noalloc, staged=staged)(stream=stream, events=events)
 
 
 def noalloc_limits():

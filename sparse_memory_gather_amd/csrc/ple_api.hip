@@ -263,7 +263,7 @@ int ple_proj(const uint16_t* x_bf16, int64_t T, const uint16_t* W_bf16, float* e
 // scales, R and vocab_size unused)
 // nv_blocks != NULL: NVFP4 table (table = codes [R][1280], nv_blocks [R][160])
 static int forward_impl(const ple_forward_args* a, void* stream, void* const* events, bool heads,
-                        const uint16_t* x_in = nullptr, const uint8_t* nv_blocks = nullptr) {
+                        const uint16_t* x_in = nullptr, const uint8_t* nv_blocks = nullptr, bool staged = false) {
     if (!a) return fail(PLE_ERR_NULL, "ple_forward: args is NULL");
     const bool from_x = x_in != nullptr;
     const int64_t T = a->T;
@@ -330,9 +330,11 @@ static int forward_impl(const ple_forward_args* a, void* stream, void* const* ev
     auto mark = [&](int i) -> hipError_t {
         return events ? hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), s) : hipSuccess;
     };
-    if (!from_x && !heads && !nv_blocks && a->out != a->h && decode_one_launch(T, S)) {
+    if (!from_x && !heads && !nv_blocks && !staged && decode_one_launch(T, S)) {
         // a short call: IDs, gather, projection and fuse in one launch (the
-        // profiling events then put the whole kernel in the projection stage)
+        // profiling events then put the whole kernel in the projection stage).
+        // In place, the projection blocks copy h into the x region, which
+        // this path does not otherwise use
         DecodeArgs d{};
         d.tokens = a->tokens;
         d.T = T;
@@ -348,6 +350,7 @@ static int forward_impl(const ple_forward_args* a, void* stream, void* const* ev
         d.conv_w = a->conv_w;
         d.h = a->h;
         d.out = a->out;
+        d.hw = a->out == a->h ? reinterpret_cast<uint16_t*>(ws + L.x) : nullptr;
         d.conv_state = a->conv_state;
         d.snap = snap;
         d.e16 = e16;
@@ -418,6 +421,10 @@ static int check_events(void* const* events) {
 extern "C" {
 
 int ple_forward(const ple_forward_args* a, void* stream) { return forward_impl(a, stream, nullptr, false); }
+
+int ple_forward_staged(const ple_forward_args* a, void* stream) {
+    return forward_impl(a, stream, nullptr, false, nullptr, nullptr, true);
+}
 
 int ple_forward_profiled(const ple_forward_args* a, void* stream, void* const* events) {
     if (int st = check_events(events)) return st;

@@ -188,6 +188,14 @@ decode_step_kernel(const DecodeArgs a) {
 #pragma unroll
         for (int q = 0; q < kSteps; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[q], fb[q], acc, 0, 0, 0);
         if (wv + 1 < kChainWaves) acc_s[lane] = acc;
+        if (wv == 0 && a.hw && lane < T * 4) {
+            // in place (out == h): wave 0, done with its turn, copies this
+            // block's 32 features of every token's h for the finishers that
+            // read earlier tokens' rows; out overwrites h only after every
+            // projection block has released
+            const int64_t off = (int64_t)(lane >> 2) * kD + f0 + (lane & 3) * 8;
+            *reinterpret_cast<u32x4*>(a.hw + off) = *reinterpret_cast<const u32x4*>(a.h + off);
+        }
         for (int i = wv; i < kChainWaves; ++i) __syncthreads();
         if (wave == kChainWaves - 1 && live) {
             // lane holds token fr and features f0 + 8 g + 4 kh + 0..3
@@ -213,7 +221,9 @@ decode_step_kernel(const DecodeArgs a) {
     // finisher: token t
     const int64_t t = ticket - kProj;
     fuse::TokenFuse f;
-    fuse::token_begin(f, t, a.T, s_cu, S, a.h, nullptr, a.conv_w, a.snap, a.conv_state, tid);
+    // in place, the earlier tokens' h rows are other finishers' out rows:
+    // they are read from the projection blocks' copy after the wait
+    fuse::token_begin(f, t, a.T, s_cu, S, a.h, nullptr, a.conv_w, a.snap, a.conv_state, tid, a.hw == nullptr);
     // a one-token sequence's state is read and rewritten by this block alone
     const bool own_state = f.sbase == a.conv_state;
     if (own_state) fuse::token_state(f, tid);
@@ -233,6 +243,7 @@ decode_step_kernel(const DecodeArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     __syncthreads();
+    if (a.hw) fuse::token_window(f, t, a.hw, tid);
     if (!own_state) fuse::token_state(f, tid);
     fuse::token_end(f, t, a.e16, a.tokens, a.conv_state, a.hist_ids, a.hist_len, a.out, a.eps, a.gate_out,
                     a.y_out, red_s, g_s, tid);

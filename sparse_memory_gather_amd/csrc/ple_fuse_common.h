@@ -155,11 +155,12 @@ struct TokenFuse {
 // the token's sequence and window, its h rows and conv weights: everything
 // that does not need e or the carried state. hw: where the h rows of the
 // three earlier tokens are read (a copy when out is h), or NULL for h.
+// window = false leaves those three rows out (token_window reads them later).
 // cu, tokens may be copies in LDS.
 __device__ __forceinline__ void token_begin(TokenFuse& f, int64_t t, int64_t T, const int32_t* cu, int32_t S,
                                             const uint16_t* __restrict__ h, const uint16_t* __restrict__ hw,
                                             const uint16_t* __restrict__ conv_w, const float* snap,
-                                            const float* conv_state, int tid) {
+                                            const float* conv_state, int tid, bool window = true) {
     const uint32_t cb = (uint32_t)tid * FPT * 2;
     f.s = seq_of(cu, S, t);
     f.st = cu[f.s];
@@ -173,7 +174,7 @@ __device__ __forceinline__ void token_begin(TokenFuse& f, int64_t t, int64_t T, 
     const uint16_t* hwin = hw ? hw : h;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        if (k >= f.first) {
+        if (k >= f.first && (window || k == 3)) {
             const int64_t p = t - 3 + k;
             f.hp[k] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>((k < 3 ? hwin : h) + p * kD) + cb);
         } else {
@@ -181,6 +182,16 @@ __device__ __forceinline__ void token_begin(TokenFuse& f, int64_t t, int64_t T, 
         }
     }
     load_conv_w(conv_w, tid, f.w);
+}
+
+// the h rows of the window's earlier tokens, from hw, after a token_begin
+// with window = false
+__device__ __forceinline__ void token_window(TokenFuse& f, int64_t t, const uint16_t* __restrict__ hw, int tid) {
+    const uint32_t cb = (uint32_t)tid * FPT * 2;
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+        if (k >= f.first)
+            f.hp[k] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(hw + (t - 3 + k) * kD) + cb);
 }
 
 // the carried-state taps of the window

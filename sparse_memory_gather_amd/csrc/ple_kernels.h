@@ -121,8 +121,9 @@ struct DecodeArgs {
     uint64_t mod_R, mod_m;       // set by launch_decode_step
     const uint16_t* W;
     const uint16_t* conv_w;
-    const uint16_t* h;           // read only: out may not be h
+    const uint16_t* h;           // read only (out may be h: see hw)
     uint16_t* out;
+    uint16_t* hw;                // workspace: copy of h [T][kD] when out == h, else NULL
     float* conv_state;
     float* snap;                 // workspace: carried state of sequences spanning finishers
     uint16_t* e16;               // workspace: bf16 e [T][kD]
@@ -136,7 +137,7 @@ struct DecodeArgs {
     float* y_out;
 };
 
-// whether a T-token call of S sequences (FP8 table, out != h) runs as one launch
+// whether a T-token call of S sequences (FP8 table) runs as one launch
 bool decode_one_launch(int64_t T, int32_t S);
 hipError_t launch_decode_step(DecodeArgs a, hipStream_t stream);
 

@@ -913,9 +913,11 @@ def test_streaming_fuse_many_short_sequences(dev, small_table, dev_weights):
 
 
 # ---------------------------------------------------------------------------
-# One launch for short calls (up to 16 tokens and 256 sequences, out != h):
-# projection blocks and one finisher per token, ordered by counters in the
-# workspace. An in-place call (out == h) takes the three-launch path.
+# One launch for short calls (up to 16 tokens and 256 sequences): projection
+# blocks and one finisher per token, ordered by counters in the workspace.
+# ple_forward_staged runs the same calls as three launches. In place
+# (out == h), the finishers read the earlier tokens' h rows from a copy the
+# projection blocks take.
 # ---------------------------------------------------------------------------
 
 ONE_LAUNCH_CASES = [
@@ -946,17 +948,23 @@ def test_one_launch_equals_three_launches(dev, small_table, dev_weights, case):
         return st
 
     ws = ple.Workspace(dev)
-    st1, st2, st3 = fresh(), fresh(), fresh()
+    st1, st2, st3, st4, st5 = fresh(), fresh(), fresh(), fresh(), fresh()
     one = _forward(dev, tab, sc, dev_weights, toks, cu, h, st1, workspace=ws)        # one launch, debug
-    h2 = dev_bf16(h, dev)
-    three = ple.ple_forward(dev_i32(toks, dev), dev_i32(cu, dev), tab, sc, dev_weights[0], dev_weights[1], h2,
-                            st2, out=h2, debug=True)                                    # in place: three launches
+    three = ple.ple_forward(dev_i32(toks, dev), dev_i32(cu, dev), tab, sc, dev_weights[0], dev_weights[1],
+                            dev_bf16(h, dev), st2, debug=True, staged=True)         # three launches
     fast = _forward(dev, tab, sc, dev_weights, toks, cu, h, st3, debug=False, workspace=ws)
+    h4 = dev_bf16(h, dev)
+    ple.ple_forward(dev_i32(toks, dev), dev_i32(cu, dev), tab, sc, dev_weights[0], dev_weights[1], h4, st4,
+                    out=h4, workspace=ws)                                            # one launch, in place
+    h5 = dev_bf16(h, dev)
+    ple.ple_forward(dev_i32(toks, dev), dev_i32(cu, dev), tab, sc, dev_weights[0], dev_weights[1], h5, st5,
+                    out=h5, staged=True)                                             # three launches, in place
     for k in ("row_ids", "x", "e", "gate", "y"):
         assert torch.equal(one[k], three[k]), k
-    assert np.array_equal(host_bits(one["out"]), host_bits(h2))
-    assert np.array_equal(host_bits(fast), host_bits(h2))
-    for st in (st1, st3):
+    want = host_bits(three["out"])
+    for got in (one["out"], fast, h4, h5):
+        assert np.array_equal(host_bits(got), want)
+    for st in (st1, st3, st4, st5):
         assert torch.equal(st.conv_state, st2.conv_state)
         assert torch.equal(st.hist_ids, st2.hist_ids) and torch.equal(st.hist_len, st2.hist_len)
     # every call leaves the counters at zero
@@ -1015,9 +1023,8 @@ def test_one_launch_flags_a_workspace_whose_counters_are_not_zero(dev, small_tab
     st_a, st_b = ple.State(8, dev), ple.State(8, dev)
     a = ple.ple_forward(dev_i32(toks, dev), dev_i32(cu, dev), tab, sc, dev_weights[0], dev_weights[1],
                         dev_bf16(h, dev), st_a, workspace=ws, dev_err=err)
-    h2 = dev_bf16(h, dev)
-    ple.ple_forward(dev_i32(toks, dev), dev_i32(cu, dev), tab, sc, dev_weights[0], dev_weights[1], h2, st_b,
-                    out=h2)
+    b = ple.ple_forward(dev_i32(toks, dev), dev_i32(cu, dev), tab, sc, dev_weights[0], dev_weights[1],
+                        dev_bf16(h, dev), st_b, staged=True)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
-    assert np.array_equal(host_bits(a), host_bits(h2))
+    assert np.array_equal(host_bits(a), host_bits(b))
