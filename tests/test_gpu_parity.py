@@ -491,6 +491,45 @@ def test_graph_captured_forward_replays_like_eager(dev, small_table, dev_weights
         _ = torch.randn(1000, device=dev).sum().item()   # unrelated eager work between replays
 
 
+
+def test_graph_captured_in_place_one_launch_replays_like_eager(dev, small_table, dev_weights):
+    # a short call in place (out == h): one launch, whose finishers read the
+    # earlier tokens' h rows from the copy the projection blocks take;
+    # captured once and replayed three times against three eager calls
+    tab, sc = small_table
+    T, S = 16, 4
+    assert ple.one_launch(T, S)
+    rng = np.random.default_rng(31)
+    toks = dev_i32(inputs.uniform_tokens(rng, T), dev)
+    cu = dev_i32(np.array([0, 1, 6, 10, 16], np.int32), dev)
+    h0 = dev_bf16(inputs.normal_bf16(rng, (T, D)), dev)
+    h_g, h_e = h0.clone(), h0.clone()
+    st_g, st_e = ple.State(S, dev), ple.State(S, dev)
+    call = ple.Forward(toks, cu, tab, sc, dev_weights[0], dev_weights[1], h_g, st_g, out=h_g)
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        call()                                   # warm-up outside the graph
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    h_g.copy_(h0)
+    st_g.hist_ids.zero_()
+    st_g.hist_len.zero_()
+    st_g.conv_state.zero_()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        call()
+    torch.cuda.synchronize()
+    assert torch.equal(h_g, h0)                  # capture does not run the work
+    for rep in range(3):
+        g.replay()
+        ple.ple_forward(toks, cu, tab, sc, dev_weights[0], dev_weights[1], h_e, st_e, out=h_e)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(h_g), host_bits(h_e)), rep
+        assert torch.equal(st_g.conv_state, st_e.conv_state) and torch.equal(st_g.hist_ids, st_e.hist_ids), rep
+        _ = torch.randn(1000, device=dev).sum().item()   # unrelated eager work between replays
+
 def test_in_place_out_equals_h(dev, small_table, dev_weights):
     tab, sc = small_table
     rng = np.random.default_rng(7)
