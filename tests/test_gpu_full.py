@@ -238,6 +238,7 @@ def test_decode_64_steps_after_history(dev, full_table, dev_weights, weights):
                     dev_bf16(h_hist, dev), st, workspace=ws)
     assert np.array_equal(st.hist_ids.cpu().numpy(), hist[:, -2:])
     st_dbg = st.clone()
+    st_ip = st.clone()      # the same steps in place (out == h), also one launch
     # the sequences as the oracle sees them: history, then one token per step
     steps_toks = np.stack([c[0] for c in wl.chunks], axis=1)      # [8][64]
     full = np.concatenate([hist, steps_toks], axis=1).astype(np.int32)
@@ -249,6 +250,10 @@ def test_decode_64_steps_after_history(dev, full_table, dev_weights, weights):
         hs.append(h)
         res = _run_pair(dev, tab, sc, dev_weights, dev_i32(toks, dev), dev_i32(cu, dev), dev_bf16(h, dev),
                         st, st_dbg, ws)
+        h_ip = dev_bf16(h, dev)
+        ple.ple_forward(dev_i32(toks, dev), dev_i32(cu, dev), tab, sc, dev_weights[0], dev_weights[1], h_ip, st_ip,
+                        out=h_ip, workspace=ws)
+        assert np.array_equal(host_bits(h_ip), host_bits(res["out"])), f"decode step {k}: in place"
         check_every_token_gather(dev, tab, sc, res, ref_ids[:, hlen + k], f"decode step {k}")
         if k in check_k:
             got.append(gather_debug(res, np.arange(S)))
@@ -261,6 +266,7 @@ def test_decode_64_steps_after_history(dev, full_table, dev_weights, weights):
     got = {key: np.concatenate([g[key] for g in got]) for key in got[0]}
     print("[decode] steps", check_k, check_samples(got, ref, W, "decode"), flush=True)
     print("[decode] state after 64 steps", check_state(st, seqs, W, cw, wl.R, "decode"), flush=True)
+    assert torch.equal(st_ip.conv_state, st.conv_state) and torch.equal(st_ip.hist_ids, st.hist_ids)
 
 
 def test_prefill_heads_layout(dev, full_table, dev_weights, weights):
